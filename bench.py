@@ -1,0 +1,272 @@
+"""Benchmark of the EQ-Linear hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c5]
+
+One step = one pass of the whole path over one batch of resident synthetic input:
+pack the weight spectrum (forward and input-gradient packings), forward, input
+gradient, weight gradient.  The default workload is the p4 (T=4) fp16 large square
+layer, N=65536 rows, C=D=4096 (C'=D'=1024), forward + backward.
+
+Prints ONE JSON line.  `value` is the dense-equivalent throughput of the step,
+3 passes x 2*N*D*C FLOPs per step time.  `roofline` covers the step's dominant
+kernel, timed with HIP events on the stream the library launches on (torch's
+current stream).  `cpu_baseline` times the fp64 CPU oracle on a bounded row
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+MFMA_PEAK = {"f16": 2516.6, "f32": 157.3}   # dense TFLOP/s: 256 CU x 2.4 GHz x (4096 | 256) FLOP/clk
+HBM_PEAK = 8000.0                            # GB/s
+METRIC = "EQ-Linear dense-equivalent TFLOP/s + % MFMA peak, p4 fp16 fwd/bwd, 1 MI355X"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c5", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true", help="skip timing the unrolled dense GEMM comparator")
+    ap.add_argument("--cpu-rows", type=int, default=8192)
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "group_circulant_linear_p4_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        table = json.load(f)
+    ent = table.get("%s/%s" % (kernel, workload))
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the EQ-Linear path has no multi-GPU mode in this "
+              "library (rows shard independently; see the design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import group_circulant_linear_p4_amd as eql
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(1)
+    eql.lib()  # fail loudly if the HIP library is missing
+    wl = W.WORKLOADS[args.workload]
+    T, N, Cp, Dp = wl.T, wl.N, wl.Cp, wl.Dp
+    code = eql.EQL_F16 if wl.dtype == "f16" else eql.EQL_F32
+    tdt = torch.float16 if wl.dtype == "f16" else torch.float32
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("bench: generating %s" % wl.name, file=sys.stderr, flush=True)
+
+    x_h, w_h, dy_h = W.make_x(wl), W.make_w(wl), W.make_dy(wl)
+    x = torch.from_numpy(x_h).to(dev)
+    w = torch.from_numpy(w_h).to(dev)
+    dy = torch.from_numpy(dy_h).to(dev)
+    y = torch.empty((N, Dp * T), dtype=tdt, device=dev)
+    dx = torch.empty((N, Cp * T), dtype=tdt, device=dev)
+    dw = torch.empty((Dp, Cp, T), dtype=tdt, device=dev)
+    wp = torch.empty(eql.eqlinear_packed_weight_bytes(Dp, Cp, T, code), dtype=torch.uint8, device=dev)
+    wpb = torch.empty(eql.eqlinear_packed_weight_bytes(Cp, Dp, T, code), dtype=torch.uint8, device=dev)
+    ws_bytes = eql.eqlinear_bwd_w_workspace_bytes(N, Cp, Dp, T, code)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+
+    calls = {
+        "pack": lambda: (eql.eqlinear_pack_weight(w, wp, Dp, Cp, T, code, eql.EQL_PACK_FWD, sptr),
+                         eql.eqlinear_pack_weight(w, wpb, Dp, Cp, T, code, eql.EQL_PACK_BWDX, sptr)),
+        "fwd": lambda: eql.eqlinear_fwd(x, wp, y, N, Cp, Dp, T, code, sptr),
+        "bwd_x": lambda: eql.eqlinear_bwd_x(dy, wpb, dx, N, Cp, Dp, T, code, sptr),
+        "bwd_w": lambda: eql.eqlinear_bwd_w(x, dy, dw, ws, ws_bytes, N, Cp, Dp, T, code, sptr),
+    }
+    order = ["pack", "fwd", "bwd_x", "bwd_w"]
+
+    def step(events=None):
+        for i, k in enumerate(order):
+            if events is not None:
+                events[k][0].record(stream)
+            calls[k]()
+            if events is not None:
+                events[k][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [{k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for k in order}
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    per = {k: float(np.mean([e[k][0].elapsed_time(e[k][1]) for e in evs])) for k in order}
+
+    dense_eq = 2.0 * N * (Dp * T) * (Cp * T)
+    actual = 2.0 * (2 * T - 2 if T % 2 == 0 else 2 * T - 1) * N * Dp * Cp if T > 1 else 2.0 * N * Dp * Cp
+    n_passes = 3
+    value = n_passes * dense_eq / (ms_per_step * 1e-3) / 1e12
+    elt = 2 if wl.dtype == "f16" else 4
+    bytes_pass = {
+        "fwd": elt * (N * Cp * T + N * Dp * T + Dp * Cp * T),
+        "bwd_x": elt * (N * Dp * T + N * Cp * T + Dp * Cp * T),
+        "bwd_w": elt * (N * Cp * T + N * Dp * T + Dp * Cp * T),
+    }
+    passes = {}
+    for k in ("fwd", "bwd_x", "bwd_w"):
+        t = per[k] * 1e-3
+        passes[k] = {
+            "ms": round(per[k], 4),
+            "dense_eq_tflops": round(dense_eq / t / 1e12, 1),
+            "actual_tflops": round(actual / t / 1e12, 1),
+            "mfma_frac": round(actual / t / 1e12 / MFMA_PEAK[wl.dtype], 4),
+            "hbm_gbs": round(bytes_pass[k] / t / 1e9, 1),
+        }
+    # Dominant kernel: the pass with the largest share of the step.
+    dom = max(("fwd", "bwd_x", "bwd_w"), key=lambda k: per[k])
+    t_dom = per[dom] * 1e-3
+    flop_bound = actual / MFMA_PEAK[wl.dtype] / 1e12 >= bytes_pass[dom] / HBM_PEAK / 1e9
+    if flop_bound:
+        roofline = {"bound": "mfma", "achieved": round(actual / t_dom / 1e12, 1), "peak": MFMA_PEAK[wl.dtype],
+                    "unit": "TFLOP/s"}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(bytes_pass[dom] / t_dom / 1e9, 1), "peak": HBM_PEAK,
+                    "unit": "GB/s"}
+    roofline["frac"] = round(roofline["achieved"] / roofline["peak"], 4)
+    roofline["traffic"] = traffic_for(dom, wl.key)
+    roofline["kernel"] = {"fwd": "eqlinear_fwd", "bwd_x": "eqlinear_bwd_x", "bwd_w": "eqlinear_bwd_w"}[dom]
+    roofline["ms_per_launch"] = round(per[dom], 4)
+
+    dense = None
+    if not args.no_dense:
+        dense = dense_comparator(torch, x, w, dy, T, reps=max(5, min(args.steps, 20)))
+        dense["speedup_fwd"] = round(dense["fwd_ms"] / per["fwd"], 3)
+        dense["speedup_bwd_x"] = round(dense["bwd_x_ms"] / per["bwd_x"], 3)
+        dense["speedup_bwd_w"] = round(dense["bwd_w_ms"] / per["bwd_w"], 3)
+        total = dense["fwd_ms"] + dense["bwd_x_ms"] + dense["bwd_w_ms"]
+        dense["speedup_fwd_bwd"] = round(total / (per["fwd"] + per["bwd_x"] + per["bwd_w"]), 3)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        del x, dy, y, dx
+        torch.cuda.empty_cache()
+        cpu = cpu_baseline(wl, x_h, w_h, dy_h, min(args.cpu_rows, N), n_passes)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded; x,dy ~ N(0,1), w ~ N(0,1/C)%s)" % (
+            ", 1%% rows x16" if wl.hot_rows_frac else ""),
+        "config": {"workload": wl.name, "T": T, "N": N, "C": Cp * T, "D": Dp * T,
+                   "step": "pack(fwd)+pack(bwd_x)+fwd+bwd_x+bwd_w"},
+        "passes": passes,
+        "pack_ms": round(per["pack"], 4),
+        "mfma_frac_step": round(n_passes * actual / (ms_per_step * 1e-3) / 1e12 / MFMA_PEAK[wl.dtype], 4),
+        "roofline": roofline,
+        "dense_baseline": dense,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+def dense_comparator(torch, x, w, dy, T, reps):
+    """The unrolled ("replicate and multiply dense") layer on the same GPU: torch
+    F.linear and matmuls on the dense (D'T) x (C'T) weight (built outside the timed
+    region)."""
+    Dp, Cp, _ = w.shape
+    g = torch.arange(T, device=w.device)
+    idx = (g.view(T, 1) - g.view(1, T)) % T
+    Wd = w[:, :, idx].permute(0, 2, 1, 3).reshape(Dp * T, Cp * T).contiguous()
+    F = torch.nn.functional
+
+    def timeit(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    dyT = dy.t().contiguous()
+    res = {
+        "fwd_ms": timeit(lambda: F.linear(x, Wd)),
+        "bwd_x_ms": timeit(lambda: torch.matmul(dy, Wd)),
+        "bwd_w_ms": timeit(lambda: torch.matmul(dyT, x)),
+    }
+    res = {k: round(v, 4) for k, v in res.items()}
+    res["kind"] = "torch F.linear / matmul on the unrolled dense weight (hipBLASLt)"
+    del Wd, dyT
+    return res
+
+
+def cpu_baseline(wl, x_h, w_h, dy_h, rows, n_passes):
+    """The fp64 oracle on the first `rows` rows of the workload, all three passes."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    xs, dys = x_h[:rows], dy_h[:rows]
+    t0 = time.perf_counter()
+    oracle.fwd(xs, w_h)
+    oracle.bwd_x(dys, w_h)
+    oracle.bwd_w(xs, dys, wl.T)
+    dt = time.perf_counter() - t0
+    flops = n_passes * 2.0 * rows * wl.D * wl.C
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": "rows 0..%d of the same workload, forward + input gradient + weight gradient, "
+                      "fp64 dense unroll (%.1f s)" % (rows - 1, dt)}
+
+
+if __name__ == "__main__":
+    main()

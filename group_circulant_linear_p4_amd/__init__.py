@@ -1,0 +1,149 @@
+"""EQ-Linear (group-circulant linear layer over the cyclic group C_T) on MI355X.
+
+The layer's weight is one set of shared parameters w[D', C', T] replicated under
+cyclic shifts, W[d*T+g, c*T+h] = w[d, c, (g-h) mod T] ("Insight Central" in
+"Resumo Tecnico: Flash EQ-Linear"); it is evaluated exactly by a group-axis DFT,
+per-frequency channel GEMMs on the half spectrum and the inverse DFT, all in
+hand-written HIP kernels for gfx950 behind the C ABI in include/eqlinear.h.
+
+This module is the thin ctypes binding of that ABI: one Python function per C
+entry point, with the same name and argument order.  Buffers may be given as
+torch tensors on a ROCm device or as raw device addresses (int); `stream` as a
+torch.cuda.Stream, a raw hipStream_t (int) or None for torch's current stream.
+A non-zero status raises EqlError.  No computation happens in Python, and there
+is no fallback: if libeqlinear.so is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "EQL_F32", "EQL_F16", "EQL_PACK_FWD", "EQL_PACK_BWDX", "EQL_MAX_T", "EqlError",
+    "lib", "library_path", "eqlinear_abi_version", "eqlinear_status_string",
+    "eqlinear_packed_weight_bytes", "eqlinear_pack_weight", "eqlinear_fwd", "eqlinear_bwd_x",
+    "eqlinear_bwd_w_workspace_bytes", "eqlinear_bwd_w",
+]
+
+EQL_F32, EQL_F16 = 0, 1
+EQL_PACK_FWD, EQL_PACK_BWDX = 0, 1
+EQL_MAX_T = 16
+EQL_OK, EQL_EINVAL, EQL_EALIGN, EQL_EUNSUPPORTED, EQL_EHIP = 0, 1, 2, 3, 4
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libeqlinear.so")
+_lib = None
+
+
+class EqlError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (where, eqlinear_status_string(status), status))
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libeqlinear.so (loaded on first use; raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError("libeqlinear.so is not built (run `python -m group_circulant_linear_p4_amd.build`); "
+                              "there is no fallback implementation")
+        L = ctypes.CDLL(_LIB_PATH)
+        i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+        L.eqlinear_abi_version.argtypes, L.eqlinear_abi_version.restype = [], i32
+        L.eqlinear_status_string.argtypes, L.eqlinear_status_string.restype = [i32], ctypes.c_char_p
+        L.eqlinear_packed_weight_bytes.argtypes = [i64, i64, i32, i32]
+        L.eqlinear_packed_weight_bytes.restype = sz
+        L.eqlinear_pack_weight.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp]
+        L.eqlinear_pack_weight.restype = i32
+        L.eqlinear_fwd.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, vp]
+        L.eqlinear_fwd.restype = i32
+        L.eqlinear_bwd_x.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, vp]
+        L.eqlinear_bwd_x.restype = i32
+        L.eqlinear_bwd_w_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
+        L.eqlinear_bwd_w_workspace_bytes.restype = sz
+        L.eqlinear_bwd_w.argtypes = [vp, vp, vp, vp, sz, i64, i64, i64, i32, i32, vp]
+        L.eqlinear_bwd_w.restype = i32
+        _lib = L
+    return _lib
+
+
+def _ptr(buf):
+    if buf is None:
+        return None
+    if isinstance(buf, int):
+        return buf or None
+    data_ptr = getattr(buf, "data_ptr", None)
+    if data_ptr is None:
+        raise TypeError("expected a device tensor or an int address, got %r" % type(buf))
+    if not buf.is_cuda:
+        raise ValueError("EQ-Linear buffers must live in GPU memory (got a %s tensor)" % buf.device)
+    if not buf.is_contiguous():
+        raise ValueError("EQ-Linear buffers must be contiguous")
+    return data_ptr() or None
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream or None
+    if isinstance(stream, int):
+        return stream or None
+    return getattr(stream, "cuda_stream", stream) or None
+
+
+def _dtype(dtype) -> int:
+    if isinstance(dtype, int):
+        return dtype
+    import torch
+    if dtype == torch.float16:
+        return EQL_F16
+    if dtype == torch.float32:
+        return EQL_F32
+    raise ValueError("unsupported dtype %r (fp16 or fp32)" % (dtype,))
+
+
+def _check(status: int, where: str) -> None:
+    if status != EQL_OK:
+        raise EqlError(status, where)
+
+
+def eqlinear_abi_version() -> int:
+    return lib().eqlinear_abi_version()
+
+
+def eqlinear_status_string(status: int) -> str:
+    return lib().eqlinear_status_string(int(status)).decode()
+
+
+def eqlinear_packed_weight_bytes(out_ch: int, in_ch: int, T: int, dtype) -> int:
+    return lib().eqlinear_packed_weight_bytes(out_ch, in_ch, T, _dtype(dtype))
+
+
+def eqlinear_pack_weight(w, w_packed, Dp: int, Cp: int, T: int, dtype, mode: int, stream=None) -> None:
+    _check(lib().eqlinear_pack_weight(_ptr(w), _ptr(w_packed), Dp, Cp, T, _dtype(dtype), mode, _stream(stream)),
+           "eqlinear_pack_weight")
+
+
+def eqlinear_fwd(x, w_packed, y, N: int, Cp: int, Dp: int, T: int, dtype, stream=None) -> None:
+    _check(lib().eqlinear_fwd(_ptr(x), _ptr(w_packed), _ptr(y), N, Cp, Dp, T, _dtype(dtype), _stream(stream)),
+           "eqlinear_fwd")
+
+
+def eqlinear_bwd_x(dy, w_packed_bwdx, dx, N: int, Cp: int, Dp: int, T: int, dtype, stream=None) -> None:
+    _check(lib().eqlinear_bwd_x(_ptr(dy), _ptr(w_packed_bwdx), _ptr(dx), N, Cp, Dp, T, _dtype(dtype),
+                                _stream(stream)), "eqlinear_bwd_x")
+
+
+def eqlinear_bwd_w_workspace_bytes(N: int, Cp: int, Dp: int, T: int, dtype) -> int:
+    return lib().eqlinear_bwd_w_workspace_bytes(N, Cp, Dp, T, _dtype(dtype))
+
+
+def eqlinear_bwd_w(x, dy, dw, workspace, ws_bytes: int, N: int, Cp: int, Dp: int, T: int, dtype,
+                   stream=None) -> None:
+    _check(lib().eqlinear_bwd_w(_ptr(x), _ptr(dy), _ptr(dw), _ptr(workspace), ws_bytes, N, Cp, Dp, T,
+                                _dtype(dtype), _stream(stream)), "eqlinear_bwd_w")

@@ -1,0 +1,80 @@
+"""Build the HIP library libeqlinear.so for gfx950, in-tree.
+
+    python -m group_circulant_linear_p4_amd.build        # or build_library()
+
+Every source under csrc/ is compiled by hipcc into _build/ (in parallel) and
+linked into group_circulant_linear_p4_amd/libeqlinear.so.
+"""
+from __future__ import annotations
+
+import concurrent.futures
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libeqlinear.so")
+ARCH = os.environ.get("EQL_OFFLOAD_ARCH", "gfx950")
+
+SOURCES = [
+    "eql_api.hip",
+    "eql_pack.hip",
+    "eql_fwd_f16.hip",
+    "eql_fwd_f32.hip",
+    "eql_bwdw_f16.hip",
+    "eql_bwdw_f32.hip",
+]
+
+CFLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
+    # No packed-fp32 instructions: every fp32 op is scalar per lane.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Rounding is decided by the source: no implicit multiply-add contraction.
+    "-ffp-contract=off",
+    "-Wall", "-Wno-unused-function",
+    "-I", INCLUDE, "-I", CSRC,
+]
+
+
+def hipcc() -> str:
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(path):
+        raise RuntimeError("hipcc not found; the EQ-Linear library needs ROCm to build")
+    return path
+
+
+def _compile(src: str, extra: list[str]) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *CFLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), res.stderr[-8000:]))
+    return obj
+
+
+def build_library(jobs: int | None = None, extra_flags: list[str] | None = None, verbose: bool = False) -> str:
+    """Compile every source and link libeqlinear.so; returns the library path."""
+    os.makedirs(BUILD, exist_ok=True)
+    extra = list(extra_flags or [])
+    jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 2)))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, *objs, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), res.stderr[-8000:]))
+    os.replace(tmp, LIB)
+    if verbose:
+        print("built", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build_library(verbose=True)
+    sys.exit(0)

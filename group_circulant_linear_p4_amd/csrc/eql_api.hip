@@ -1,0 +1,222 @@
+// C ABI of the EQ-Linear library (declared in include/eqlinear.h): argument
+// validation, tile / split policy and launches on the caller's stream.  Nothing
+// here allocates device memory or synchronises the host.
+#include <cmath>
+#include <cstdint>
+
+#include "eql_launch.h"
+#include "eqlinear.h"
+
+using namespace eql;
+
+namespace {
+
+constexpr int64_t kMaxGrid = (1LL << 24) - 1;  // workgroups per launch (x 256 threads < 2^32)
+constexpr int kTargetWorkgroups = 256;         // one per compute unit of an MI355X
+
+bool dtype_ok(int dtype) { return dtype == EQL_F32 || dtype == EQL_F16; }
+int elt_bytes(int dtype) { return dtype == EQL_F16 ? 2 : 4; }
+int group_channels(int dtype) { return 16 / elt_bytes(dtype); }
+int64_t groups_of(int64_t ch, int dtype) { return (ch + group_channels(dtype) - 1) / group_channels(dtype); }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// cos / sin(2 pi m / T), m = 0..T-1: computed in double with the C library and
+// rounded once to float.
+Twiddles make_twiddles(int T) {
+  Twiddles tw{};
+  const double two_pi = 6.28318530717958647692528676655900577;
+  for (int m = 0; m < T; ++m) {
+    tw.cs[m] = (float)std::cos(two_pi * m / T);
+    tw.sn[m] = (float)std::sin(two_pi * m / T);
+  }
+  tw.inv_t = (float)(1.0 / T);
+  return tw;
+}
+
+int check_sizes(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype) {
+  if (!dtype_ok(dtype) || T < 1) return EQL_EINVAL;
+  if (T > EQL_MAX_T) return EQL_EUNSUPPORTED;
+  if (N < 0 || Cp < 1 || Dp < 1) return EQL_EINVAL;
+  if (N >= (1LL << 31) || Cp * T >= (1LL << 24) || Dp * T >= (1LL << 24)) return EQL_EINVAL;
+  return EQL_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? EQL_OK : EQL_EHIP; }
+
+// Shared by the forward pass and the input gradient: out = in * W^T for the packed
+// weight with (out, in) channel counts (Dout, Cin).
+int run_fwd(const void* x, const void* wp, void* y, int64_t N, int64_t Cin, int64_t Dout, int T,
+            int dtype, void* stream) {
+  int st = check_sizes(N, Cin, Dout, T, dtype);
+  if (st != EQL_OK) return st;
+  if (N == 0) return EQL_OK;
+  if (!x || !wp || !y) return EQL_EINVAL;
+  if (!aligned16(x) || !aligned16(wp) || !aligned16(y)) return EQL_EALIGN;
+
+  const int nbm = fwd_nb_max(T);
+  const int64_t rowTiles = ceil_div(N, kFwdRows);
+  int nb = nbm;
+  if (nbm > 1 && rowTiles * ceil_div(Dout, 32 * nbm) < kTargetWorkgroups) nb = 1;
+  const int64_t colTiles = ceil_div(Dout, 32 * nb);
+  if (colTiles > kMaxGrid) return EQL_EINVAL;
+
+  FwdArgs a{};
+  a.wp = wp;
+  a.Cin = (int)Cin;
+  a.Dout = (int)Dout;
+  a.Jtot = (int)groups_of(Cin, dtype);
+  a.colTiles = (int)colTiles;
+  a.aligned16 = (Cin * T * elt_bytes(dtype)) % 16 == 0;
+  a.tw = make_twiddles(T);
+
+  // Rows in pieces small enough for one grid.
+  const int64_t maxRows = (kMaxGrid / colTiles) * kFwdRows;
+  const size_t inRow = (size_t)Cin * T * elt_bytes(dtype), outRow = (size_t)Dout * T * elt_bytes(dtype);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int64_t r0 = 0; r0 < N; r0 += maxRows) {
+    const int64_t rows = N - r0 < maxRows ? N - r0 : maxRows;
+    a.x = static_cast<const char*>(x) + (size_t)r0 * inRow;
+    a.y = static_cast<char*>(y) + (size_t)r0 * outRow;
+    a.N = (int)rows;
+    a.numTiles = (int)(ceil_div(rows, kFwdRows) * colTiles);
+    const hipError_t e = dtype == EQL_F16 ? launch_fwd_f16(T, nb, a, (unsigned)a.numTiles, s)
+                                          : launch_fwd_f32(T, nb, a, (unsigned)a.numTiles, s);
+    if (e != hipSuccess) return EQL_EHIP;
+  }
+  return EQL_OK;
+}
+
+struct SplitPlan {
+  int64_t S, rowsPerSplit, dTiles, cTiles;
+};
+
+// Row ranges of the weight-gradient reduction: enough ranges to give every
+// compute unit one workgroup, each range a whole number of row chunks.
+SplitPlan plan_bwdw(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype) {
+  SplitPlan p{};
+  const int64_t chunk = (int64_t)bwdw_ksc(T) * 2 * group_channels(dtype);
+  p.dTiles = ceil_div(Dp, kBwdwRowsD);
+  p.cTiles = ceil_div(Cp, 32 * bwdw_nb(T));
+  if (N == 0) return p;
+  const int64_t tiles = p.dTiles * p.cTiles;
+  int64_t S = tiles >= kTargetWorkgroups ? 1 : kTargetWorkgroups / tiles;
+  const int64_t maxS = ceil_div(N, chunk);
+  if (S > maxS) S = maxS;
+  p.rowsPerSplit = ceil_div(ceil_div(N, S), chunk) * chunk;
+  p.S = ceil_div(N, p.rowsPerSplit);
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int eqlinear_abi_version(void) { return 100; }
+
+const char* eqlinear_status_string(int status) {
+  switch (status) {
+    case EQL_OK: return "ok";
+    case EQL_EINVAL: return "invalid argument (null pointer, size out of range, unknown dtype or mode, or workspace too small)";
+    case EQL_EALIGN: return "a base pointer is not 16-byte aligned";
+    case EQL_EUNSUPPORTED: return "group order T above EQL_MAX_T";
+    case EQL_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t eqlinear_packed_weight_bytes(int64_t out_ch, int64_t in_ch, int T, int dtype) {
+  if (check_sizes(0, in_ch, out_ch, T, dtype) != EQL_OK) return 0;
+  return (size_t)out_ch * (size_t)groups_of(in_ch, dtype) * group_channels(dtype) * T * elt_bytes(dtype);
+}
+
+int eqlinear_pack_weight(const void* w, void* w_packed, int64_t Dp, int64_t Cp, int T, int dtype,
+                         int mode, void* stream) {
+  int st = check_sizes(0, Cp, Dp, T, dtype);
+  if (st != EQL_OK) return st;
+  if (mode != EQL_PACK_FWD && mode != EQL_PACK_BWDX) return EQL_EINVAL;
+  if (!w || !w_packed) return EQL_EINVAL;
+  if (!aligned16(w) || !aligned16(w_packed)) return EQL_EALIGN;
+  PackArgs a{};
+  a.w = w;
+  a.wp = w_packed;
+  a.Dp = (int)Dp;
+  a.Cp = (int)Cp;
+  a.transposed = mode == EQL_PACK_BWDX;
+  a.outCh = (int)(a.transposed ? Cp : Dp);
+  a.inCh = (int)(a.transposed ? Dp : Cp);
+  a.Jin = (int)groups_of(a.inCh, dtype);
+  a.tw = make_twiddles(T);
+  const int64_t threads = (int64_t)a.outCh * a.Jin * group_channels(dtype);
+  const int64_t grid = ceil_div(threads, 256);
+  if (grid > kMaxGrid) return EQL_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return status_of(dtype == EQL_F16 ? launch_pack_f16(T, a, (unsigned)grid, s)
+                                    : launch_pack_f32(T, a, (unsigned)grid, s));
+}
+
+int eqlinear_fwd(const void* x, const void* w_packed, void* y, int64_t N, int64_t Cp, int64_t Dp,
+                 int T, int dtype, void* stream) {
+  return run_fwd(x, w_packed, y, N, Cp, Dp, T, dtype, stream);
+}
+
+int eqlinear_bwd_x(const void* dy, const void* w_packed_bwdx, void* dx, int64_t N, int64_t Cp,
+                   int64_t Dp, int T, int dtype, void* stream) {
+  // The input gradient is the forward algorithm with the roles of the channel
+  // axes swapped: in = D', out = C'.
+  int st = check_sizes(N, Cp, Dp, T, dtype);
+  if (st != EQL_OK) return st;
+  return run_fwd(dy, w_packed_bwdx, dx, N, Dp, Cp, T, dtype, stream);
+}
+
+size_t eqlinear_bwd_w_workspace_bytes(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype) {
+  if (check_sizes(N, Cp, Dp, T, dtype) != EQL_OK) return 0;
+  const SplitPlan p = plan_bwdw(N, Cp, Dp, T, dtype);
+  return (size_t)p.S * T * (size_t)Dp * (size_t)Cp * sizeof(float);
+}
+
+int eqlinear_bwd_w(const void* x, const void* dy, void* dw, void* workspace, size_t ws_bytes,
+                   int64_t N, int64_t Cp, int64_t Dp, int T, int dtype, void* stream) {
+  int st = check_sizes(N, Cp, Dp, T, dtype);
+  if (st != EQL_OK) return st;
+  const SplitPlan p = plan_bwdw(N, Cp, Dp, T, dtype);
+  const size_t need = (size_t)p.S * T * (size_t)Dp * (size_t)Cp * sizeof(float);
+  if (!dw || (N > 0 && (!x || !dy || !workspace))) return EQL_EINVAL;
+  if (ws_bytes < need) return EQL_EINVAL;
+  if (!aligned16(dw) || (N > 0 && (!aligned16(x) || !aligned16(dy) || !aligned16(workspace))))
+    return EQL_EALIGN;
+  const int64_t tiles = p.S * p.dTiles * p.cTiles;
+  const int64_t rgrid = ceil_div(Dp * Cp, 256);
+  if (tiles > kMaxGrid || rgrid > kMaxGrid) return EQL_EINVAL;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Twiddles tw = make_twiddles(T);
+  if (p.S > 0) {
+    BwdwArgs a{};
+    a.x = x;
+    a.dy = dy;
+    a.ws = static_cast<float*>(workspace);
+    a.N = (int)N;
+    a.Cp = (int)Cp;
+    a.Dp = (int)Dp;
+    a.rowsPerSplit = (int)p.rowsPerSplit;
+    a.cTiles = (int)p.cTiles;
+    a.dTiles = (int)p.dTiles;
+    a.numTiles = (int)tiles;
+    a.tw = tw;
+    const hipError_t e = dtype == EQL_F16 ? launch_bwdw_f16(T, a, (unsigned)tiles, s)
+                                          : launch_bwdw_f32(T, a, (unsigned)tiles, s);
+    if (e != hipSuccess) return EQL_EHIP;
+  }
+  BwdwReduceArgs r{};
+  r.ws = static_cast<const float*>(workspace);
+  r.dw = dw;
+  r.S = (int)p.S;
+  r.Dp = (int)Dp;
+  r.Cp = (int)Cp;
+  r.tw = tw;
+  return status_of(dtype == EQL_F16 ? launch_bwdw_reduce_f16(T, r, (unsigned)rgrid, s)
+                                    : launch_bwdw_reduce_f32(T, r, (unsigned)rgrid, s));
+}
+
+}  // extern "C"

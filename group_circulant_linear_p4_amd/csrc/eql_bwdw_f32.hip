@@ -1,0 +1,28 @@
+// Weight-gradient kernel instantiations for the f32 element type, T = 1..16.
+#include "eql_launch.h"
+
+namespace eql {
+
+template <int T>
+static hipError_t bwdw_one(const BwdwArgs& a, unsigned grid, hipStream_t s) {
+  return launch_kernel((const void*)&eql_bwdw_kernel<T, float, bwdw_nb(T), bwdw_ksc(T)>, grid, a, s);
+}
+
+template <int T>
+static hipError_t reduce_one(const BwdwReduceArgs& a, unsigned grid, hipStream_t s) {
+  return launch_kernel((const void*)&eql_bwdw_reduce<T, float>, grid, a, s);
+}
+
+hipError_t launch_bwdw_f32(int T, const BwdwArgs& a, unsigned grid, hipStream_t s) {
+#define EQL_CASE(t) return bwdw_one<t>(a, grid, s);
+  EQL_FOR_EACH_T(T, EQL_CASE)
+#undef EQL_CASE
+}
+
+hipError_t launch_bwdw_reduce_f32(int T, const BwdwReduceArgs& a, unsigned grid, hipStream_t s) {
+#define EQL_CASE(t) return reduce_one<t>(a, grid, s);
+  EQL_FOR_EACH_T(T, EQL_CASE)
+#undef EQL_CASE
+}
+
+}  // namespace eql

@@ -1,0 +1,307 @@
+// Device-side building blocks of the EQ-Linear kernels for gfx950: vector types,
+// the MFMA step, the group-axis transforms and the vectorised loads/stores.
+//
+// Plane convention (the real half spectrum along the group axis, "Abordagem
+// Algoritmica" in "Resumo Tecnico: Flash EQ-Linear"): a length-T group vector v is
+// represented by T real planes
+//   p = 0                    k = 0       sum_h v_h
+//   p = 1 (even T > 1)       k = T/2     sum_h (-1)^h v_h
+//   p = NR + 2q, NR + 2q + 1 k = q + 1   Re / Im of sum_h v_h exp(-2 pi i h k / T)
+// where NR is the number of real planes.  Activations may carry a per-plane scale
+// sigma_p (p4 uses 1/2 on its two real planes, which keeps |X_p| <= 2 max|x| and
+// makes every transform coefficient 0, +-1 or +-1/2).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace eql {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kMaxT = 16;
+
+__host__ __device__ constexpr int n_real_planes(int T) { return (T % 2 == 0 && T > 1) ? 2 : 1; }
+__host__ __device__ constexpr int n_pairs(int T) { return (T - n_real_planes(T)) / 2; }
+
+// cos / sin of 2*pi*m/T for m = 0..T-1, computed on the host in double and rounded
+// once to float.  Passed as a kernel argument, so the values live in scalar
+// registers.  Entries whose exact value is 0 or +-1 are never read: those cases are
+// folded at compile time (see mac_cos / mac_msin).
+struct Twiddles {
+  float cs[kMaxT];
+  float sn[kMaxT];
+  float inv_t;  // 1/T rounded to float
+};
+
+// s + v * cos(2 pi m / T) with the exact coefficient when it is 0 or +-1.
+template <int T>
+__device__ __forceinline__ float mac_cos(float s, float v, int m, const Twiddles& tw) {
+  m %= T;
+  if (m == 0) return s + v;
+  if (2 * m == T) return s - v;
+  if (4 * m == T || 4 * m == 3 * T) return s;
+  return __builtin_fmaf(v, tw.cs[m], s);
+}
+
+// s - v * sin(2 pi m / T) with the exact coefficient when it is 0 or +-1.
+template <int T>
+__device__ __forceinline__ float mac_msin(float s, float v, int m, const Twiddles& tw) {
+  m %= T;
+  if (m == 0 || 2 * m == T) return s;
+  if (4 * m == T) return s - v;
+  if (4 * m == 3 * T) return s + v;
+  return __builtin_fmaf(-v, tw.sn[m], s);
+}
+
+// ---------------------------------------------------------------------------
+// Forward group transform of one length-T vector into T planes.
+// kScaled selects the activation scaling (p4: 1/2 on the real planes); weights are
+// always transformed unscaled.
+// ---------------------------------------------------------------------------
+template <int T, bool kScaled>
+struct Dft {
+  static __device__ __forceinline__ void run(const float (&v)[T], float (&out)[T],
+                                             const Twiddles& tw) {
+    constexpr int NR = n_real_planes(T);
+#pragma unroll
+    for (int p = 0; p < T; ++p) {
+      const int k = p == 0 ? 0 : (p < NR ? T / 2 : (p - NR) / 2 + 1);
+      const bool im = p >= NR && ((p - NR) & 1);
+      float s = 0.0f;
+#pragma unroll
+      for (int h = 0; h < T; ++h) s = im ? mac_msin<T>(s, v[h], h * k, tw) : mac_cos<T>(s, v[h], h * k, tw);
+      out[p] = s;
+    }
+  }
+};
+
+// p4: butterflies only.  The additions are ordered so that a cyclic shift of v
+// permutes / negates the outputs exactly in floating point:
+//   shift by one maps (X0, X2, Xr, Xi) to (X0, -X2, Xi, -Xr).
+template <bool kScaled>
+struct Dft<4, kScaled> {
+  static __device__ __forceinline__ void run(const float (&v)[4], float (&out)[4], const Twiddles&) {
+    const float s02 = v[0] + v[2], d02 = v[0] - v[2];
+    const float s13 = v[1] + v[3], d13 = v[3] - v[1];
+    if (kScaled) {
+      out[0] = 0.5f * (s02 + s13);
+      out[1] = 0.5f * (s02 - s13);
+    } else {
+      out[0] = s02 + s13;
+      out[1] = s02 - s13;
+    }
+    out[2] = d02;
+    out[3] = d13;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Inverse transform of T planes back to T group values.
+// kSigma2 = false: planes computed from sigma-scaled activations and unscaled
+// weights (forward / input gradient).  kSigma2 = true: both operands were
+// sigma-scaled activations (weight gradient).  For T != 4 sigma = 1 and the two
+// coincide: y_g = (1/T) (P0 + (-1)^g P_N + 2 sum_k (cos P_re - sin P_im)).
+// ---------------------------------------------------------------------------
+template <int T, bool kSigma2>
+struct Idft {
+  static __device__ __forceinline__ void run(const float (&P)[T], float (&y)[T], const Twiddles& tw) {
+    constexpr int NR = n_real_planes(T);
+#pragma unroll
+    for (int g = 0; g < T; ++g) {
+      float s = P[0];
+      if (NR == 2) s = (g & 1) ? s - P[1] : s + P[1];
+      float u = 0.0f;
+#pragma unroll
+      for (int q = 0; q < n_pairs(T); ++q) {
+        u = mac_cos<T>(u, P[NR + 2 * q], g * (q + 1), tw);
+        u = mac_msin<T>(u, P[NR + 2 * q + 1], g * (q + 1), tw);
+      }
+      y[g] = (s + 2.0f * u) * tw.inv_t;
+    }
+  }
+};
+
+// p4 inverse.  With activations scaled by 1/2 on the real planes every
+// coefficient is +-1/2:  y = 1/2 ((P0 +- P2) +- Pr / Pi).
+template <>
+struct Idft<4, false> {
+  static __device__ __forceinline__ void run(const float (&P)[4], float (&y)[4], const Twiddles&) {
+    const float a = P[0] + P[1], b = P[0] - P[1];
+    y[0] = 0.5f * (a + P[2]);
+    y[1] = 0.5f * (b - P[3]);
+    y[2] = 0.5f * (a - P[2]);
+    y[3] = 0.5f * (b + P[3]);
+  }
+};
+
+// p4 inverse for the weight gradient (both operands scaled by 1/2 on the real
+// planes, so those planes carry 1/4):  dw = (P0 +- P2) +- Pr / Pi / 2.
+template <>
+struct Idft<4, true> {
+  static __device__ __forceinline__ void run(const float (&P)[4], float (&y)[4], const Twiddles&) {
+    const float a = P[0] + P[1], b = P[0] - P[1];
+    const float r = 0.5f * P[2], i = 0.5f * P[3];
+    y[0] = a + r;
+    y[1] = b - i;
+    y[2] = a - r;
+    y[3] = b + i;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Element types.  A "unit" is 16 bytes: 8 fp16 or 4 fp32 values.
+// ---------------------------------------------------------------------------
+template <typename Elt>
+struct EltT;
+
+template <>
+struct EltT<_Float16> {
+  static constexpr int kPerUnit = 8;
+  static constexpr uint32_t kSignMask = 0x80008000u;
+  static __device__ __forceinline__ float get(const u32x4& u, int e) {
+    return (float)__builtin_bit_cast(f16x8, u)[e];
+  }
+  static __device__ __forceinline__ u32x4 pack(const float (&v)[8]) {
+    f16x8 h;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = (_Float16)v[e];
+    return __builtin_bit_cast(u32x4, h);
+  }
+  // One k-step: 32x32 output tile += A(32 x 16) * B(16 x 32).
+  static __device__ __forceinline__ void mfma(f32x16& acc, const u32x4& a, const u32x4& b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                 __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
+  }
+};
+
+template <>
+struct EltT<float> {
+  static constexpr int kPerUnit = 4;
+  static constexpr uint32_t kSignMask = 0x80000000u;
+  static __device__ __forceinline__ float get(const u32x4& u, int e) {
+    return __builtin_bit_cast(f32x4, u)[e];
+  }
+  static __device__ __forceinline__ u32x4 pack(const float (&v)[4]) {
+    f32x4 f = {v[0], v[1], v[2], v[3]};
+    return __builtin_bit_cast(u32x4, f);
+  }
+  // One k-step: four 32x32x2 products; element e of each lane's unit feeds product e.
+  static __device__ __forceinline__ void mfma(f32x16& acc, const u32x4& a, const u32x4& b) {
+    const f32x4 af = __builtin_bit_cast(f32x4, a), bf = __builtin_bit_cast(f32x4, b);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(af[0], bf[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(af[1], bf[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(af[2], bf[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(af[3], bf[3], acc, 0, 0, 0);
+  }
+};
+
+__device__ __forceinline__ u32x4 neg_unit(const u32x4& u, uint32_t mask) {
+  return u ^ (u32x4){mask, mask, mask, mask};
+}
+
+// Largest power of two dividing n, capped at 16 (the widest global access).
+__host__ __device__ constexpr int pow2_part(int n) {
+  return (n % 16 == 0) ? 16 : (n % 8 == 0) ? 8 : (n % 4 == 0) ? 4 : (n % 2 == 0) ? 2 : 1;
+}
+
+// Load NB bytes (a power of two <= 16) from a suitably aligned address into the
+// low bytes of a u32x4.
+template <int NBYTES>
+__device__ __forceinline__ void load_bytes(const void* p, uint32_t* dst) {
+  if constexpr (NBYTES == 16) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+    dst[0] = v[0]; dst[1] = v[1]; dst[2] = v[2]; dst[3] = v[3];
+  } else if constexpr (NBYTES == 8) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+    dst[0] = v[0]; dst[1] = v[1];
+  } else if constexpr (NBYTES == 4) {
+    dst[0] = *reinterpret_cast<const uint32_t*>(p);
+  } else {
+    static_assert(NBYTES == 2, "unsupported width");
+    dst[0] = *reinterpret_cast<const uint16_t*>(p);
+  }
+}
+
+// Read T contiguous elements starting at `p` (aligned to pow2_part(T*sizeof(Elt)))
+// into floats.
+template <int T, typename Elt>
+__device__ __forceinline__ void load_group(const Elt* p, float (&v)[T]) {
+  constexpr int BYTES = T * (int)sizeof(Elt);
+  constexpr int W = pow2_part(BYTES);
+  constexpr int WORDS = (BYTES + 3) / 4;
+  uint32_t w[WORDS > 0 ? WORDS : 1];
+#pragma unroll
+  for (int i = 0; i < WORDS; ++i) w[i] = 0;
+  if constexpr (W >= 4) {
+#pragma unroll
+    for (int b = 0; b < BYTES; b += W) load_bytes<W>(reinterpret_cast<const char*>(p) + b, &w[b / 4]);
+  } else {
+    // 2-byte granularity (fp16 with odd T): assemble half-words.
+#pragma unroll
+    for (int e = 0; e < T; ++e) {
+      const uint32_t hv = *reinterpret_cast<const uint16_t*>(p + e);
+      w[e / 2] |= (e & 1) ? (hv << 16) : hv;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < T; ++e) {
+    if constexpr (sizeof(Elt) == 2) {
+      const uint16_t bits = (uint16_t)(w[e / 2] >> ((e & 1) * 16));
+      v[e] = (float)__builtin_bit_cast(_Float16, bits);
+    } else {
+      v[e] = __builtin_bit_cast(float, w[e]);
+    }
+  }
+}
+
+// Write T floats, rounded to Elt (nearest even), as contiguous elements at `p`
+// (aligned to pow2_part(T*sizeof(Elt))).
+template <int T, typename Elt>
+__device__ __forceinline__ void store_group(Elt* p, const float (&v)[T]) {
+  constexpr int BYTES = T * (int)sizeof(Elt);
+  constexpr int W = pow2_part(BYTES);
+  if constexpr (W >= 4) {
+    constexpr int WORDS = BYTES / 4;
+    uint32_t w[WORDS];
+#pragma unroll
+    for (int i = 0; i < WORDS; ++i) {
+      if constexpr (sizeof(Elt) == 2) {
+        const _Float16 lo = (_Float16)v[2 * i], hi = (_Float16)v[2 * i + 1];
+        w[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+      } else {
+        w[i] = __builtin_bit_cast(uint32_t, v[i]);
+      }
+    }
+    char* b = reinterpret_cast<char*>(p);
+#pragma unroll
+    for (int off = 0; off < BYTES; off += W) {
+      if constexpr (W == 16) {
+        *reinterpret_cast<u32x4*>(b + off) = (u32x4){w[off / 4], w[off / 4 + 1], w[off / 4 + 2], w[off / 4 + 3]};
+      } else if constexpr (W == 8) {
+        *reinterpret_cast<u32x2*>(b + off) = (u32x2){w[off / 4], w[off / 4 + 1]};
+      } else {
+        *reinterpret_cast<uint32_t*>(b + off) = w[off / 4];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < T; ++e) p[e] = (Elt)v[e];
+  }
+}
+
+// XCD-aware tile order.  Consecutive workgroup ids are dispatched round-robin over
+// the 8 XCDs; this remaps them so that each XCD receives a contiguous range of
+// logical tiles (and so shares row blocks of the input in its own L2).
+__device__ __forceinline__ int xcd_remap(int b, int num) {
+  constexpr int kXcd = 8;
+  const int per = num / kXcd, rem = num % kXcd;
+  const int xcd = b % kXcd, local = b / kXcd;
+  return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+}
+
+}  // namespace eql

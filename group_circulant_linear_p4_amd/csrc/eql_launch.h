@@ -1,0 +1,60 @@
+// Internal launch interface between the C ABI (eql_api.hip) and the kernel
+// instantiations (one translation unit per kernel family and element type).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "eql_bwdw.h"
+#include "eql_fwd.h"
+#include "eql_pack.h"
+
+namespace eql {
+
+// Tile policy, shared by the host (grid sizes, workspace) and the instantiations.
+// NB = 32-column blocks per wave: T*NB*16 fp32 accumulators per lane stay <= 256.
+__host__ __device__ constexpr int fwd_nb_max(int T) { return T <= 4 ? 4 : (T <= 8 ? 2 : 1); }
+// Channel groups per K chunk (two per k-step).
+__host__ __device__ constexpr int fwd_jc(int T) { return T <= 4 ? 4 : 2; }
+// bwd_w: column blocks per wave and k-steps per row chunk.
+__host__ __device__ constexpr int bwdw_nb(int T) { return fwd_nb_max(T); }
+__host__ __device__ constexpr int bwdw_ksc(int T) { return T <= 4 ? 2 : 1; }
+
+// elt: 2 = fp16, 4 = fp32.  Each returns the launch status.
+hipError_t launch_fwd_f16(int T, int NB, const FwdArgs& a, unsigned grid, hipStream_t s);
+hipError_t launch_fwd_f32(int T, int NB, const FwdArgs& a, unsigned grid, hipStream_t s);
+hipError_t launch_bwdw_f16(int T, const BwdwArgs& a, unsigned grid, hipStream_t s);
+hipError_t launch_bwdw_f32(int T, const BwdwArgs& a, unsigned grid, hipStream_t s);
+hipError_t launch_bwdw_reduce_f16(int T, const BwdwReduceArgs& a, unsigned grid, hipStream_t s);
+hipError_t launch_bwdw_reduce_f32(int T, const BwdwReduceArgs& a, unsigned grid, hipStream_t s);
+hipError_t launch_pack_f16(int T, const PackArgs& a, unsigned grid, hipStream_t s);
+hipError_t launch_pack_f32(int T, const PackArgs& a, unsigned grid, hipStream_t s);
+
+template <typename A>
+inline hipError_t launch_kernel(const void* fn, unsigned grid, const A& args, hipStream_t s) {
+  void* kargs[] = {const_cast<A*>(&args)};
+  return hipLaunchKernel(fn, dim3(grid), dim3(256), kargs, 0, s);
+}
+
+// Expands F(T) for T = 1..16 inside a switch on `t`.
+#define EQL_FOR_EACH_T(t, F) \
+  switch (t) {               \
+    case 1: F(1)             \
+    case 2: F(2)             \
+    case 3: F(3)             \
+    case 4: F(4)             \
+    case 5: F(5)             \
+    case 6: F(6)             \
+    case 7: F(7)             \
+    case 8: F(8)             \
+    case 9: F(9)             \
+    case 10: F(10)           \
+    case 11: F(11)           \
+    case 12: F(12)           \
+    case 13: F(13)           \
+    case 14: F(14)           \
+    case 15: F(15)           \
+    case 16: F(16)           \
+    default: return hipErrorInvalidValue; \
+  }
+
+}  // namespace eql

@@ -1,0 +1,86 @@
+"""Drop-in torch layer over the C ABI: the shared parameters w[D', C', T] are the
+only state, exactly as in an unrolled ("naive") EQ-Linear layer, so an existing
+weight can be used as is ("Implementacao" in "Resumo Tecnico: Flash EQ-Linear":
+training-free, plug-and-play replacement).
+
+Forward packs the half spectrum of w and runs eqlinear_fwd; backward runs
+eqlinear_bwd_x on the conjugate-transposed packing and eqlinear_bwd_w.  Torch only
+allocates the buffers; every arithmetic step runs in the HIP library.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import (EQL_PACK_BWDX, EQL_PACK_FWD, eqlinear_bwd_w, eqlinear_bwd_w_workspace_bytes, eqlinear_bwd_x,
+               eqlinear_fwd, eqlinear_pack_weight, eqlinear_packed_weight_bytes)
+
+
+def _packed(w: torch.Tensor, mode: int) -> torch.Tensor:
+    Dp, Cp, T = w.shape
+    out_ch, in_ch = (Dp, Cp) if mode == EQL_PACK_FWD else (Cp, Dp)
+    buf = torch.empty(eqlinear_packed_weight_bytes(out_ch, in_ch, T, w.dtype), dtype=torch.uint8, device=w.device)
+    eqlinear_pack_weight(w, buf, Dp, Cp, T, w.dtype, mode)
+    return buf
+
+
+class EQLinearFunction(torch.autograd.Function):
+    """y[..., D'*T] = x[..., C'*T] W^T with W[d*T+g, c*T+h] = w[d, c, (g-h) mod T]."""
+
+    @staticmethod
+    def forward(ctx, x: torch.Tensor, w: torch.Tensor):
+        Dp, Cp, T = w.shape
+        if x.shape[-1] != Cp * T:
+            raise ValueError("x has %d features, the weight expects C'*T = %d" % (x.shape[-1], Cp * T))
+        if x.dtype != w.dtype:
+            raise ValueError("x and w must share a dtype (fp16 or fp32)")
+        w = w.contiguous()
+        x2 = x.reshape(-1, Cp * T).contiguous()
+        N = x2.shape[0]
+        y = torch.empty((N, Dp * T), dtype=x.dtype, device=x.device)
+        eqlinear_fwd(x2, _packed(w, EQL_PACK_FWD), y, N, Cp, Dp, T, x.dtype)
+        ctx.save_for_backward(x2, w)
+        ctx.lead_shape = x.shape[:-1]
+        return y.reshape(*x.shape[:-1], Dp * T)
+
+    @staticmethod
+    def backward(ctx, dy: torch.Tensor):
+        x2, w = ctx.saved_tensors
+        Dp, Cp, T = w.shape
+        N = x2.shape[0]
+        dy2 = dy.reshape(-1, Dp * T).to(x2.dtype).contiguous()
+        dx = dw = None
+        if ctx.needs_input_grad[0]:
+            dx = torch.empty((N, Cp * T), dtype=x2.dtype, device=x2.device)
+            eqlinear_bwd_x(dy2, _packed(w, EQL_PACK_BWDX), dx, N, Cp, Dp, T, x2.dtype)
+            dx = dx.reshape(*ctx.lead_shape, Cp * T)
+        if ctx.needs_input_grad[1]:
+            ws_bytes = eqlinear_bwd_w_workspace_bytes(N, Cp, Dp, T, x2.dtype)
+            ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=x2.device)
+            dw = torch.empty_like(w)
+            eqlinear_bwd_w(x2, dy2, dw, ws, ws_bytes, N, Cp, Dp, T, x2.dtype)
+        return dx, dw
+
+
+def eqlinear(x: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
+    return EQLinearFunction.apply(x, w)
+
+
+class EQLinear(torch.nn.Module):
+    """Equivariant linear layer over C_T: in_channels*T -> out_channels*T features."""
+
+    def __init__(self, in_channels: int, out_channels: int, group_order: int = 4, device=None, dtype=None):
+        super().__init__()
+        self.in_channels, self.out_channels, self.group_order = in_channels, out_channels, group_order
+        self.weight = torch.nn.Parameter(torch.empty(out_channels, in_channels, group_order, device=device,
+                                                     dtype=dtype))
+        with torch.no_grad():
+            self.weight.normal_(0.0, 1.0 / math.sqrt(in_channels * group_order))
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        return EQLinearFunction.apply(x, self.weight)
+
+    def extra_repr(self) -> str:
+        return "in_channels=%d, out_channels=%d, group_order=%d" % (self.in_channels, self.out_channels,
+                                                                    self.group_order)

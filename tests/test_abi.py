@@ -1,0 +1,124 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments with the documented status codes
+before launching anything (every call below fails validation or is a no-op)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import group_circulant_linear_p4_amd as eql
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "eqlinear.h")
+
+A16 = 0x10000          # fake, 16-byte aligned device addresses (never dereferenced:
+A16B = 0x20000         # every call that receives them fails validation first)
+MIS = 0x10008          # 8-byte aligned only
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(eqlinear_\w+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_function():
+    L = eql.lib()
+    names = declared_functions()
+    assert len(names) == 8
+    for n in names:
+        assert hasattr(L, n), "missing export %s" % n
+        assert hasattr(eql, n), "binding lacks %s" % n
+
+
+def test_version_and_status_strings():
+    assert eql.eqlinear_abi_version() == 100
+    for s in range(5):
+        assert eql.eqlinear_status_string(s)
+    assert eql.eqlinear_status_string(99) == "unknown status"
+
+
+def test_packed_weight_bytes():
+    # out * ceil(in / G) * G * T * sizeof(elt), G = 16 / sizeof(elt)
+    assert eql.eqlinear_packed_weight_bytes(3, 5, 4, eql.EQL_F16) == 3 * 8 * 4 * 2
+    assert eql.eqlinear_packed_weight_bytes(3, 9, 4, eql.EQL_F16) == 3 * 16 * 4 * 2
+    assert eql.eqlinear_packed_weight_bytes(1024, 1024, 4, eql.EQL_F16) == 1024 * 1024 * 4 * 2
+    assert eql.eqlinear_packed_weight_bytes(64, 64, 8, eql.EQL_F32) == 64 * 64 * 8 * 4
+    assert eql.eqlinear_packed_weight_bytes(7, 3, 3, eql.EQL_F32) == 7 * 4 * 3 * 4
+    assert eql.eqlinear_packed_weight_bytes(3, 3, 0, eql.EQL_F32) == 0
+    assert eql.eqlinear_packed_weight_bytes(3, 3, 17, eql.EQL_F32) == 0
+    assert eql.eqlinear_packed_weight_bytes(3, 3, 4, 7) == 0
+
+
+def test_workspace_bytes():
+    assert eql.eqlinear_bwd_w_workspace_bytes(0, 4, 4, 4, eql.EQL_F16) == 0
+    n = eql.eqlinear_bwd_w_workspace_bytes(65536, 1024, 1024, 4, eql.EQL_F16)
+    assert n > 0 and n % (4 * 1024 * 1024 * 4) == 0          # whole fp32 partial spectra
+    assert eql.eqlinear_bwd_w_workspace_bytes(10, 4, 4, 0, eql.EQL_F16) == 0
+
+
+def raw(fn, *args):
+    return getattr(eql.lib(), fn)(*args)
+
+
+@pytest.mark.parametrize("fn", ["eqlinear_fwd", "eqlinear_bwd_x"])
+def test_fwd_validation(fn):
+    F16, F32 = eql.EQL_F16, eql.EQL_F32
+    ok = (A16, A16B, A16 + 0x1000)
+    assert raw(fn, *ok, 8, 4, 4, 4, 5, None) == eql.EQL_EINVAL            # dtype
+    assert raw(fn, *ok, 8, 4, 4, 0, F16, None) == eql.EQL_EINVAL          # T < 1
+    assert raw(fn, *ok, 8, 4, 4, 17, F16, None) == eql.EQL_EUNSUPPORTED   # T > 16
+    assert raw(fn, *ok, -1, 4, 4, 4, F16, None) == eql.EQL_EINVAL         # N < 0
+    assert raw(fn, *ok, 8, 0, 4, 4, F16, None) == eql.EQL_EINVAL          # C' < 1
+    assert raw(fn, *ok, 8, 4, 0, 4, F32, None) == eql.EQL_EINVAL          # D' < 1
+    assert raw(fn, *ok, 8, 1 << 22, 4, 4, F32, None) == eql.EQL_EINVAL    # C'T >= 2^24
+    assert raw(fn, *ok, 1 << 31, 4, 4, 4, F32, None) == eql.EQL_EINVAL   # N >= 2^31
+    assert raw(fn, None, A16B, A16, 8, 4, 4, 4, F16, None) == eql.EQL_EINVAL
+    assert raw(fn, A16, None, A16B, 8, 4, 4, 4, F16, None) == eql.EQL_EINVAL
+    assert raw(fn, A16, A16B, None, 8, 4, 4, 4, F16, None) == eql.EQL_EINVAL
+    assert raw(fn, MIS, A16B, A16, 8, 4, 4, 4, F16, None) == eql.EQL_EALIGN
+    assert raw(fn, A16, MIS, A16B, 8, 4, 4, 4, F16, None) == eql.EQL_EALIGN
+    assert raw(fn, A16, A16B, MIS, 8, 4, 4, 4, F32, None) == eql.EQL_EALIGN
+    # N == 0 is a no-op that launches nothing, even with null buffers.
+    assert raw(fn, None, None, None, 0, 4, 4, 4, F16, None) == eql.EQL_OK
+
+
+def test_pack_validation():
+    F16 = eql.EQL_F16
+    assert raw("eqlinear_pack_weight", A16, A16B, 4, 4, 4, F16, 2, None) == eql.EQL_EINVAL   # mode
+    assert raw("eqlinear_pack_weight", None, A16B, 4, 4, 4, F16, 0, None) == eql.EQL_EINVAL
+    assert raw("eqlinear_pack_weight", A16, None, 4, 4, 4, F16, 1, None) == eql.EQL_EINVAL
+    assert raw("eqlinear_pack_weight", MIS, A16B, 4, 4, 4, F16, 0, None) == eql.EQL_EALIGN
+    assert raw("eqlinear_pack_weight", A16, A16B, 4, 4, 20, F16, 0, None) == eql.EQL_EUNSUPPORTED
+    assert raw("eqlinear_pack_weight", A16, A16B, 0, 4, 4, F16, 0, None) == eql.EQL_EINVAL
+
+
+def test_bwd_w_validation():
+    F16 = eql.EQL_F16
+    need = eql.eqlinear_bwd_w_workspace_bytes(64, 4, 4, 4, F16)
+    f = "eqlinear_bwd_w"
+    assert raw(f, A16, A16B, A16 + 0x100, A16 + 0x200, need - 1, 64, 4, 4, 4, F16, None) == eql.EQL_EINVAL
+    assert raw(f, None, A16B, A16 + 0x100, A16 + 0x200, need, 64, 4, 4, 4, F16, None) == eql.EQL_EINVAL
+    assert raw(f, A16, A16B, None, A16 + 0x200, need, 64, 4, 4, 4, F16, None) == eql.EQL_EINVAL
+    assert raw(f, A16, A16B, A16 + 0x100, None, need, 64, 4, 4, 4, F16, None) == eql.EQL_EINVAL
+    assert raw(f, A16, MIS, A16 + 0x100, A16 + 0x200, need, 64, 4, 4, 4, F16, None) == eql.EQL_EALIGN
+    assert raw(f, A16, A16B, A16 + 0x100, A16 + 0x208, need, 64, 4, 4, 4, F16, None) == eql.EQL_EALIGN
+    assert raw(f, A16, A16B, A16 + 0x100, A16 + 0x200, need, 64, 4, 4, 0, F16, None) == eql.EQL_EINVAL
+    assert raw(f, A16, A16B, A16 + 0x100, A16 + 0x200, need, 64, 4, 4, 4, 9, None) == eql.EQL_EINVAL
+
+
+def test_binding_raises_on_error_and_rejects_host_tensors():
+    import torch
+    with pytest.raises(eql.EqlError) as ei:
+        eql.eqlinear_fwd(MIS, A16, A16B, 8, 4, 4, 4, eql.EQL_F16, stream=0)
+    assert ei.value.status == eql.EQL_EALIGN
+    with pytest.raises(ValueError):
+        eql.eqlinear_fwd(torch.zeros(8, 16), A16, A16B, 8, 4, 4, 4, eql.EQL_F32, stream=0)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(eql, "_lib", None)
+    monkeypatch.setattr(eql, "_LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(ImportError):
+        eql.lib()
