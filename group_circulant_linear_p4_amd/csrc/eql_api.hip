@@ -13,11 +13,17 @@ namespace {
 
 constexpr int64_t kMaxGrid = (1LL << 24) - 1;  // workgroups per launch (x 256 threads < 2^32)
 constexpr int kTargetWorkgroups = 256;         // one per compute unit of an MI355X
+constexpr int64_t kMaxRowBytes = 1LL << 23;    // bytes of one activation row (buffer offsets)
 
 bool dtype_ok(int dtype) { return dtype == EQL_F32 || dtype == EQL_F16; }
 int elt_bytes(int dtype) { return dtype == EQL_F16 ? 2 : 4; }
 int group_channels(int dtype) { return 16 / elt_bytes(dtype); }
-int64_t groups_of(int64_t ch, int dtype) { return (ch + group_channels(dtype) - 1) / group_channels(dtype); }
+// 16-byte channel groups of the packed weight's input axis, padded to a whole
+// number of kernel K stages (kPackGroupAlign groups).
+int64_t padded_groups(int64_t ch, int dtype) {
+  const int64_t g = (ch + group_channels(dtype) - 1) / group_channels(dtype);
+  return (g + kPackGroupAlign - 1) / kPackGroupAlign * kPackGroupAlign;
+}
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -38,7 +44,8 @@ int check_sizes(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype) {
   if (!dtype_ok(dtype) || T < 1) return EQL_EINVAL;
   if (T > EQL_MAX_T) return EQL_EUNSUPPORTED;
   if (N < 0 || Cp < 1 || Dp < 1) return EQL_EINVAL;
-  if (N >= (1LL << 31) || Cp * T >= (1LL << 24) || Dp * T >= (1LL << 24)) return EQL_EINVAL;
+  if (N >= (1LL << 31) || Cp * T * elt_bytes(dtype) > kMaxRowBytes || Dp * T * elt_bytes(dtype) > kMaxRowBytes)
+    return EQL_EINVAL;
   return EQL_OK;
 }
 
@@ -56,8 +63,9 @@ int run_fwd(const void* x, const void* wp, void* y, int64_t N, int64_t Cin, int6
 
   const int nbm = fwd_nb_max(T);
   const int64_t rowTiles = ceil_div(N, kFwdRows);
+  const bool rowsAligned = (Cin * T * elt_bytes(dtype)) % 16 == 0;
   int nb = nbm;
-  if (nbm > 1 && rowTiles * ceil_div(Dout, 32 * nbm) < kTargetWorkgroups) nb = 1;
+  if (!rowsAligned || (nbm > 1 && rowTiles * ceil_div(Dout, 32 * nbm) < kTargetWorkgroups)) nb = 1;
   const int64_t colTiles = ceil_div(Dout, 32 * nb);
   if (colTiles > kMaxGrid) return EQL_EINVAL;
 
@@ -65,9 +73,12 @@ int run_fwd(const void* x, const void* wp, void* y, int64_t N, int64_t Cin, int6
   a.wp = wp;
   a.Cin = (int)Cin;
   a.Dout = (int)Dout;
-  a.Jtot = (int)groups_of(Cin, dtype);
+  a.Jpad = (int)padded_groups(Cin, dtype);
+  const int64_t wpBytes = Dout * a.Jpad * 16LL * T;
+  if (wpBytes >= (1LL << 32)) return EQL_EINVAL;
+  a.wpBytes = (uint32_t)wpBytes;
   a.colTiles = (int)colTiles;
-  a.aligned16 = (Cin * T * elt_bytes(dtype)) % 16 == 0;
+  a.aligned16 = rowsAligned;
   a.tw = make_twiddles(T);
 
   // Rows in pieces small enough for one grid.
@@ -127,7 +138,7 @@ const char* eqlinear_status_string(int status) {
 
 size_t eqlinear_packed_weight_bytes(int64_t out_ch, int64_t in_ch, int T, int dtype) {
   if (check_sizes(0, in_ch, out_ch, T, dtype) != EQL_OK) return 0;
-  return (size_t)out_ch * (size_t)groups_of(in_ch, dtype) * group_channels(dtype) * T * elt_bytes(dtype);
+  return (size_t)out_ch * (size_t)padded_groups(in_ch, dtype) * 16 * T;
 }
 
 int eqlinear_pack_weight(const void* w, void* w_packed, int64_t Dp, int64_t Cp, int T, int dtype,
@@ -145,7 +156,7 @@ int eqlinear_pack_weight(const void* w, void* w_packed, int64_t Dp, int64_t Cp, 
   a.transposed = mode == EQL_PACK_BWDX;
   a.outCh = (int)(a.transposed ? Cp : Dp);
   a.inCh = (int)(a.transposed ? Dp : Cp);
-  a.Jin = (int)groups_of(a.inCh, dtype);
+  a.Jin = (int)padded_groups(a.inCh, dtype);
   a.tw = make_twiddles(T);
   const int64_t threads = (int64_t)a.outCh * a.Jin * group_channels(dtype);
   const int64_t grid = ceil_div(threads, 256);

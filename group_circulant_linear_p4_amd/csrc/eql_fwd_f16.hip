@@ -3,12 +3,18 @@
 
 namespace eql {
 
+// Aligned rows: the full-width and the one-column-block tile.  Unaligned rows
+// (narrow loads): the one-column-block tile only.
 template <int T>
 static hipError_t fwd_one(int NB, const FwdArgs& a, unsigned grid, hipStream_t s) {
   constexpr int NBM = fwd_nb_max(T), JC = fwd_jc(T);
-  if (NB == NBM) return launch_kernel((const void*)&eql_fwd_kernel<T, _Float16, NBM, JC>, grid, a, s);
+  if (!a.aligned16) {
+    if (NB != 1) return hipErrorInvalidValue;
+    return launch_kernel((const void*)&eql_fwd_kernel<T, _Float16, 1, JC, false>, grid, a, s);
+  }
+  if (NB == NBM) return launch_kernel((const void*)&eql_fwd_kernel<T, _Float16, NBM, JC, true>, grid, a, s);
   if constexpr (NBM != 1) {
-    if (NB == 1) return launch_kernel((const void*)&eql_fwd_kernel<T, _Float16, 1, JC>, grid, a, s);
+    if (NB == 1) return launch_kernel((const void*)&eql_fwd_kernel<T, _Float16, 1, JC, true>, grid, a, s);
   }
   return hipErrorInvalidValue;
 }

@@ -14,10 +14,15 @@ namespace eql {
 // NB = 32-column blocks per wave: T*NB*16 fp32 accumulators per lane stay <= 256.
 __host__ __device__ constexpr int fwd_nb_max(int T) { return T <= 4 ? 4 : (T <= 8 ? 2 : 1); }
 // Channel groups per K chunk (two per k-step).
-__host__ __device__ constexpr int fwd_jc(int T) { return T <= 4 ? 4 : 2; }
+__host__ __device__ constexpr int fwd_jc(int) { return 2; }
 // bwd_w: column blocks per wave and k-steps per row chunk.
 __host__ __device__ constexpr int bwdw_nb(int T) { return fwd_nb_max(T); }
 __host__ __device__ constexpr int bwdw_ksc(int T) { return T <= 4 ? 2 : 1; }
+
+// The packed weight's input axis is padded to a multiple of this many 16-byte
+// groups, so that every K stage of the forward kernel reads whole groups.
+constexpr int kPackGroupAlign = 4;
+static_assert(kPackGroupAlign % fwd_jc(1) == 0 && kPackGroupAlign % fwd_jc(16) == 0, "stage size");
 
 // elt: 2 = fp16, 4 = fp32.  Each returns the launch status.
 hipError_t launch_fwd_f16(int T, int NB, const FwdArgs& a, unsigned grid, hipStream_t s);

@@ -82,10 +82,12 @@ typedef enum {
  * change sign.
  *
  * Layout: G = 16 / sizeof(element) (8 for fp16, 4 for fp32) input channels form
- * one 16-byte group; Jin = ceil(in / G).  Element (o, i, plane p) is stored at
+ * one 16-byte group; Jin = ceil(in / G) rounded up to a multiple of 4.  Element
+ * (o, i, plane p) is stored at
  *     ((o * Jin + i / G) * T + p) * G + i % G
- * and entries with i >= in are zero.  Size = out * Jin * G * T elements, given by
- * eqlinear_packed_weight_bytes(out, in, T, dtype).
+ * and entries with i >= in are zero.  Size = out * Jin * G * T elements
+ * (out * Jin * 16 * T bytes), given by eqlinear_packed_weight_bytes(out, in, T,
+ * dtype); it must stay below 2^32 bytes.
  * The transform runs in fp32 and rounds once to `dtype`.
  */
 size_t eqlinear_packed_weight_bytes(int64_t out_ch, int64_t in_ch, int T, int dtype);

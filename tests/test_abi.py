@@ -40,12 +40,13 @@ def test_version_and_status_strings():
 
 
 def test_packed_weight_bytes():
-    # out * ceil(in / G) * G * T * sizeof(elt), G = 16 / sizeof(elt)
-    assert eql.eqlinear_packed_weight_bytes(3, 5, 4, eql.EQL_F16) == 3 * 8 * 4 * 2
-    assert eql.eqlinear_packed_weight_bytes(3, 9, 4, eql.EQL_F16) == 3 * 16 * 4 * 2
+    # out * Jin * 16 * T bytes, Jin = ceil(in / G) rounded up to a multiple of 4,
+    # G = 16 / sizeof(elt)
+    assert eql.eqlinear_packed_weight_bytes(3, 5, 4, eql.EQL_F16) == 3 * 4 * 16 * 4
+    assert eql.eqlinear_packed_weight_bytes(3, 33, 4, eql.EQL_F16) == 3 * 8 * 16 * 4
     assert eql.eqlinear_packed_weight_bytes(1024, 1024, 4, eql.EQL_F16) == 1024 * 1024 * 4 * 2
     assert eql.eqlinear_packed_weight_bytes(64, 64, 8, eql.EQL_F32) == 64 * 64 * 8 * 4
-    assert eql.eqlinear_packed_weight_bytes(7, 3, 3, eql.EQL_F32) == 7 * 4 * 3 * 4
+    assert eql.eqlinear_packed_weight_bytes(7, 3, 3, eql.EQL_F32) == 7 * 4 * 16 * 3
     assert eql.eqlinear_packed_weight_bytes(3, 3, 0, eql.EQL_F32) == 0
     assert eql.eqlinear_packed_weight_bytes(3, 3, 17, eql.EQL_F32) == 0
     assert eql.eqlinear_packed_weight_bytes(3, 3, 4, 7) == 0

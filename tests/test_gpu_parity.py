@@ -159,7 +159,7 @@ def test_workload_full_size_sampled(key):
 # ------------------------------------------------------------------ pack layout
 def unpack(buf, out_ch, in_ch, T, dtype):
     G = 16 // np.dtype(NPDT[dtype]).itemsize
-    jin = -(-in_ch // G)
+    jin = -(-(-(-in_ch // G)) // 4) * 4          # ceil(in / G) rounded up to a multiple of 4
     a = host(buf).view(NPDT[dtype]).astype(np.float64).reshape(out_ch, jin, T, G)
     planes = a.transpose(0, 1, 3, 2).reshape(out_ch, jin * G, T)
     assert np.all(planes[:, in_ch:, :] == 0)
