@@ -42,7 +42,11 @@ def parse():
     ap.add_argument("--workload", default="c5", choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip timing the unrolled dense GEMM comparator")
-    ap.add_argument("--cpu-rows", type=int, default=8192)
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="rows of the CPU-oracle sample (0: sized to about 12 s of work)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after timing, run a plain device copy of this size (a reference for "
+                         "profiler traffic counters)")
     return ap.parse_args()
 
 
@@ -173,6 +177,15 @@ def main():
     roofline["kernel"] = {"fwd": "eqlinear_fwd", "bwd_x": "eqlinear_bwd_x", "bwd_w": "eqlinear_bwd_w"}[dom]
     roofline["ms_per_launch"] = round(per[dom], 4)
 
+    if args.copy_probe_mib > 0:
+        nbytes = args.copy_probe_mib << 20
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     dense = None
     if not args.no_dense:
         dense = dense_comparator(torch, x, w, dy, T, reps=max(5, min(args.steps, 20)))
@@ -186,7 +199,7 @@ def main():
     if not args.no_cpu_baseline:
         del x, dy, y, dx
         torch.cuda.empty_cache()
-        cpu = cpu_baseline(wl, x_h, w_h, dy_h, min(args.cpu_rows, N), n_passes)
+        cpu = cpu_baseline(wl, x_h, w_h, dy_h, args.cpu_rows, n_passes)
 
     out = {
         "metric": METRIC,
@@ -248,20 +261,29 @@ def dense_comparator(torch, x, w, dy, T, reps):
     return res
 
 
-def cpu_baseline(wl, x_h, w_h, dy_h, rows, n_passes):
-    """The fp64 oracle on the first `rows` rows of the workload, all three passes."""
+def cpu_baseline(wl, x_h, w_h, dy_h, rows, n_passes, target_s=12.0):
+    """The fp64 oracle on the first `rows` rows of the workload, all three passes.
+    rows == 0: a 1024-row probe sizes the sample to about `target_s` seconds."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         cores = len(os.sched_getaffinity(0))
-    xs, dys = x_h[:rows], dy_h[:rows]
-    t0 = time.perf_counter()
-    oracle.fwd(xs, w_h)
-    oracle.bwd_x(dys, w_h)
-    oracle.bwd_w(xs, dys, wl.T)
-    dt = time.perf_counter() - t0
+
+    def run(r):
+        xs, dys = x_h[:r], dy_h[:r]
+        t0 = time.perf_counter()
+        oracle.fwd(xs, w_h)
+        oracle.bwd_x(dys, w_h)
+        oracle.bwd_w(xs, dys, wl.T)
+        return time.perf_counter() - t0
+
+    if rows <= 0:
+        probe = min(1024, wl.N)
+        t_probe = run(probe)
+        rows = int(min(wl.N, max(probe, probe * target_s / max(t_probe, 1e-3))))
+    dt = run(rows)
     flops = n_passes * 2.0 * rows * wl.D * wl.C
     return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": "rows 0..%d of the same workload, forward + input gradient + weight gradient, "

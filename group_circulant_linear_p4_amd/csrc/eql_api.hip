@@ -78,7 +78,8 @@ int run_fwd(const void* x, const void* wp, void* y, int64_t N, int64_t Cin, int6
   if (wpBytes >= (1LL << 32)) return EQL_EINVAL;
   a.wpBytes = (uint32_t)wpBytes;
   a.colTiles = (int)colTiles;
-  a.aligned16 = rowsAligned;
+  a.loadMode = !rowsAligned ? kLoadNarrow
+               : (Cin % ((int64_t)kPackGroupAlign * group_channels(dtype)) == 0 ? kLoadFull : kLoadAligned);
   a.tw = make_twiddles(T);
 
   // Rows in pieces small enough for one grid.

@@ -19,8 +19,9 @@
 //   * the packed spectrum of w for the workgroup's BN channels streams into an
 //     NSTAGE-deep LDS ring with buffer loads that write LDS directly (no VGPR
 //     staging).  A ring row holds the JC*T 16-byte units of one output channel,
-//     XOR-swizzled on the low three unit bits so that the 16-byte MFMA B-operand
-//     reads of 8 consecutive channels hit 8 different bank groups;
+//     XOR-swizzled so that the 16-byte MFMA B-operand reads of 16 consecutive
+//     channels (one LDS cycle on the 64-bank LDS) touch 16 different 16-byte
+//     bank groups;
 //   * per k-step and 32-column block: real planes take one MFMA, a complex pair
 //     four (Re += Xr Wr + (-Xi) Wi, Im += Xi Wr + Xr Wi);
 //   * the epilogue reads the T accumulators of one (row, channel) from the same
@@ -38,7 +39,7 @@ struct FwdArgs {
   const void* x;    // [N][Cin*T]
   const void* wp;   // packed spectrum, out = Dout, in = Cin (groups padded to Jpad)
   void* y;          // [N][Dout*T]
-  int N, Cin, Dout, Jpad, colTiles, numTiles, aligned16;
+  int N, Cin, Dout, Jpad, colTiles, numTiles, loadMode;
   uint32_t wpBytes;  // size of the packed weight in bytes (< 2^32)
   Twiddles tw;
 };
@@ -62,10 +63,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // Offsets at or beyond this value are outside every buffer: the load returns zero.
 constexpr uint32_t kOob = 0x80000000u;
 
-// ALIGNED: every x row starts on a 16-byte boundary (C'*T*sizeof(Elt) % 16 == 0),
-// so x is read with 16-byte loads; otherwise with loads of the widest power of two
-// dividing T*sizeof(Elt).
-template <int T, typename Elt, int NB, int JC, bool ALIGNED>
+// How x is read.
+//   kLoadNarrow: rows are not 16-byte aligned; loads of the widest power of two
+//                dividing T*sizeof(Elt), each checked against C'.
+//   kLoadAligned: 16-byte loads, each checked against C' (the last stage is partial).
+//   kLoadFull: 16-byte loads, C' fills every group of the packed weight (a multiple
+//              of 4 groups): no per-load check.
+enum : int { kLoadNarrow = 0, kLoadAligned = 1, kLoadFull = 2 };
+
+// Swizzle of ring row o: XOR applied to the unit index so that 16 consecutive rows
+// read at the same unit land on 16 distinct (unit mod 16) positions.
+template <int RP>
+__device__ __forceinline__ int ring_swz(int o) {
+  if constexpr (RP == 8) return (o >> 1) & 7;
+  else return o & 15;
+}
+
+template <int T, typename Elt, int NB, int JC, int LOAD>
 __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
   // The body uses AMDGPU-only types (buffer resources); the host pass only needs
   // the kernel's signature to emit its launch stub.
@@ -77,12 +91,12 @@ __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
   constexpr int KS = JC / 2;              // k-steps per stage
   constexpr int BN = 32 * NB;
   constexpr int R = JC * T;               // units of one output channel per stage
-  constexpr int RP = (R + 7) / 8 * 8;     // ... padded to a multiple of 8 (swizzle span)
+  constexpr int RP = R <= 8 ? 8 : (R + 15) / 16 * 16;  // ... padded to the swizzle span
   constexpr int IPW = BN * RP / 256;      // direct-to-LDS loads per wave per stage
   constexpr int NS = kFwdStages;
   constexpr int ELT = (int)sizeof(Elt);
   constexpr int GB = G * T * ELT;         // bytes of one lane's x block per k-step (16*T)
-  constexpr int NW = ALIGNED ? 16 : pow2_part(T * ELT);  // x load width
+  constexpr int NW = LOAD == kLoadNarrow ? pow2_part(T * ELT) : 16;  // x load width
   constexpr int XL = KS * GB / NW;        // x loads per stage
   // Loads issued after weight stage st when stage st starts: x of stages st..st+2
   // and weight stages st+1, st+2.
@@ -109,13 +123,13 @@ __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
   const uint32_t xLaneOff = (uint32_t)(wave * 32 + lrow) * rowBytes;
 
   // Direct-to-LDS source offsets: position P = (wave*IPW + i)*64 + lane of a stage
-  // holds unit r = (P % RP) ^ (o & 7) of output channel o = P / RP.
+  // holds unit r = (P % RP) ^ ring_swz(o) of output channel o = P / RP.
   uint32_t bOff[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
     const int P = (wave * IPW + i) * 64 + lane;
     const int o = P / RP, pos = P - o * RP;
-    const int r = pos ^ (o & 7);
+    const int r = pos ^ ring_swz<RP>(o);
     const int og = min(col0 + o, a.Dout - 1);
     const int rr = r < R ? r : 0;  // padding positions load an arbitrary valid unit
     bOff[i] = ((uint32_t)og * a.Jpad + rr / T) * T * 16u + (uint32_t)(rr % T) * 16u;
@@ -135,8 +149,9 @@ __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
   uint32_t raw[2][KS][4 * T];
   u32x4 af[2][KS][T + NP];
 
-  // x of stage st into raw buffer `rb` (channels past C', and so every stage past
-  // the end, read as zero).
+  // x of stage st into raw buffer `rb`.  Channels past C' read as zero, except in
+  // kLoadFull mode where the stages past the end read arbitrary in-bounds data
+  // that is transformed but never multiplied.
   auto issue_x = [&](int st, auto rbTag) {
     constexpr int rb = decltype(rbTag)::value;
 #pragma unroll
@@ -146,7 +161,7 @@ __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
 #pragma unroll
       for (int b = 0; b < GB; b += NW) {
         const int chv = cfirst + b / (T * ELT);
-        const uint32_t off = chv < a.Cin ? base + b : kOob;
+        const uint32_t off = (LOAD == kLoadFull || chv < a.Cin) ? base + b : kOob;
         if constexpr (NW == 16) {
           const u32x4 val = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
           raw[rb][s][b / 4 + 0] = val[0];
@@ -211,7 +226,7 @@ __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
 #pragma unroll
     for (int p = 0; p < T; ++p) {
       const int r = (2 * s + khalf) * T + p;
-      bf[p] = slot[o * RP + (r ^ (o & 7))];
+      bf[p] = slot[o * RP + (r ^ ring_swz<RP>(o))];
     }
   };
 

@@ -3,18 +3,26 @@
 
 namespace eql {
 
-// Aligned rows: the full-width and the one-column-block tile.  Unaligned rows
-// (narrow loads): the one-column-block tile only.
+// Load modes (see eql_fwd.h): full and checked aligned loads with the full-width
+// and the one-column-block tile; narrow loads with the one-column-block tile only.
+template <int T, int NB, int MODE>
+static hipError_t fwd_launch(const FwdArgs& a, unsigned grid, hipStream_t s) {
+  return launch_kernel((const void*)&eql_fwd_kernel<T, float, NB, fwd_jc(T), MODE>, grid, a, s);
+}
+
 template <int T>
 static hipError_t fwd_one(int NB, const FwdArgs& a, unsigned grid, hipStream_t s) {
-  constexpr int NBM = fwd_nb_max(T), JC = fwd_jc(T);
-  if (!a.aligned16) {
-    if (NB != 1) return hipErrorInvalidValue;
-    return launch_kernel((const void*)&eql_fwd_kernel<T, float, 1, JC, false>, grid, a, s);
+  constexpr int NBM = fwd_nb_max(T);
+  if (a.loadMode == kLoadNarrow) return NB == 1 ? fwd_launch<T, 1, kLoadNarrow>(a, grid, s) : hipErrorInvalidValue;
+  if (NB == NBM) {
+    return a.loadMode == kLoadFull ? fwd_launch<T, NBM, kLoadFull>(a, grid, s)
+                                   : fwd_launch<T, NBM, kLoadAligned>(a, grid, s);
   }
-  if (NB == NBM) return launch_kernel((const void*)&eql_fwd_kernel<T, float, NBM, JC, true>, grid, a, s);
   if constexpr (NBM != 1) {
-    if (NB == 1) return launch_kernel((const void*)&eql_fwd_kernel<T, float, 1, JC, true>, grid, a, s);
+    if (NB == 1) {
+      return a.loadMode == kLoadFull ? fwd_launch<T, 1, kLoadFull>(a, grid, s)
+                                     : fwd_launch<T, 1, kLoadAligned>(a, grid, s);
+    }
   }
   return hipErrorInvalidValue;
 }
