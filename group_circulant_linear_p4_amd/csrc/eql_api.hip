@@ -1,6 +1,8 @@
 // C ABI of the EQ-Linear library (declared in include/eqlinear.h): argument
 // validation, tile / split policy and launches on the caller's stream.  Nothing
 // here allocates device memory or synchronises the host.
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -51,6 +53,21 @@ int check_sizes(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? EQL_OK : EQL_EHIP; }
 
+// Compute units of the current device (cached per device; 256 on MI355X).  The
+// persistent kernels launch one workgroup per compute unit.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kTargetWorkgroups;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = kTargetWorkgroups;
+  cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
 // Shared by the forward pass and the input gradient: out = in * W^T for the packed
 // weight with (out, in) channel counts (Dout, Cin).
 int run_fwd(const void* x, const void* wp, void* y, int64_t N, int64_t Cin, int64_t Dout, int T,
@@ -82,7 +99,8 @@ int run_fwd(const void* x, const void* wp, void* y, int64_t N, int64_t Cin, int6
                : (Cin % ((int64_t)kPackGroupAlign * group_channels(dtype)) == 0 ? kLoadFull : kLoadAligned);
   a.tw = make_twiddles(T);
 
-  // Rows in pieces small enough for one grid.
+  const int cus = device_cus();
+  // Rows in pieces small enough for the tile indices.
   const int64_t maxRows = (kMaxGrid / colTiles) * kFwdRows;
   const size_t inRow = (size_t)Cin * T * elt_bytes(dtype), outRow = (size_t)Dout * T * elt_bytes(dtype);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -92,8 +110,9 @@ int run_fwd(const void* x, const void* wp, void* y, int64_t N, int64_t Cin, int6
     a.y = static_cast<char*>(y) + (size_t)r0 * outRow;
     a.N = (int)rows;
     a.numTiles = (int)(ceil_div(rows, kFwdRows) * colTiles);
-    const hipError_t e = dtype == EQL_F16 ? launch_fwd_f16(T, nb, a, (unsigned)a.numTiles, s)
-                                          : launch_fwd_f32(T, nb, a, (unsigned)a.numTiles, s);
+    const unsigned grid = (unsigned)std::min<int64_t>(a.numTiles, cus);
+    const hipError_t e = dtype == EQL_F16 ? launch_fwd_f16(T, nb, a, grid, s)
+                                          : launch_fwd_f32(T, nb, a, grid, s);
     if (e != hipSuccess) return EQL_EHIP;
   }
   return EQL_OK;

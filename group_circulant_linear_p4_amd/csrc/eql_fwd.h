@@ -5,9 +5,10 @@
 // and shared memory).  The input-gradient pass runs the same kernel on the
 // conjugate-transposed packed weight.
 //
-// Work decomposition (gfx950, wave64, one 256-thread workgroup per CU):
-//   * a workgroup owns 128 rows x BN = 32*NB output channels for all T planes;
-//     each of its 4 waves owns 32 rows;
+// Work decomposition (gfx950, wave64, one persistent 256-thread workgroup per CU):
+//   * an output tile is 128 rows x BN = 32*NB output channels for all T planes;
+//     each of the 4 waves owns 32 rows; a workgroup walks its tiles as one stream
+//     of K stages, so loads run ahead across tile boundaries;
 //   * the K loop runs over "stages" of JC 16-byte channel groups (two groups per
 //     MFMA k-step);
 //   * x goes straight from HBM/L2 into registers in MFMA A-operand order: lane l
@@ -45,7 +46,6 @@ struct FwdArgs {
 };
 
 constexpr int kFwdRows = 128;   // rows per workgroup (4 waves x 32)
-constexpr int kFwdStages = 4;   // depth of the LDS ring for the packed weight
 
 // s_waitcnt on vector-memory loads only (lgkm and exp counters left unconstrained).
 template <int N>
@@ -62,6 +62,84 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 // Offsets at or beyond this value are outside every buffer: the load returns zero.
 constexpr uint32_t kOob = 0x80000000u;
+
+#if defined(__HIP_DEVICE_COMPILE__)
+// Raw buffer descriptor words (gfx9 family: dword3 = 0x00020000).
+struct BufDesc {
+  u32x4 w;
+};
+__device__ __forceinline__ BufDesc make_desc(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  BufDesc d;
+  d.w = (u32x4){(uint32_t)b, (uint32_t)(b >> 32) & 0xFFFFu, bytes, 0x00020000u};
+  return d;
+}
+
+// 16 bytes per lane from buffer offset `voff` straight into LDS at
+// lds_base + 16 * lane (no VGPR destination).  Written as an asm statement so that
+// the compiler does not add a wait for all LDS-bound loads before every later LDS
+// read (it cannot tell the ring slots apart); completion is tracked explicitly
+// with wait_vmcnt at the places that consume the data.
+//   * The hazard recognizer does not look inside the statement, so it carries its
+//     own wait states: 5 before the load (a VALU write of an SGPR read by a VMEM
+//     instruction) and 1 between the M0 write and the load that reads it.
+//   * The descriptor and LDS base are wave-uniform; readfirstlane keeps them in
+//     SGPRs even where the compiler cannot prove uniformity.  M0 is reserved by
+//     the compiler (never allocated to other values), so it needs no clobber.
+__device__ __forceinline__ void dma16(const BufDesc& d, uint32_t voff, uint32_t lds_base) {
+  const u32x4 w = {(uint32_t)__builtin_amdgcn_readfirstlane(d.w[0]), (uint32_t)__builtin_amdgcn_readfirstlane(d.w[1]),
+                   (uint32_t)__builtin_amdgcn_readfirstlane(d.w[2]), (uint32_t)__builtin_amdgcn_readfirstlane(d.w[3])};
+  asm volatile("s_nop 4\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(w)
+               : "memory");
+}
+
+// Descriptor of `bytes` bytes at `base` (words built from scalar values).
+__device__ __forceinline__ BufDesc desc_at(uint64_t base, uint32_t bytes) {
+  BufDesc d;
+  d.w = (u32x4){(uint32_t)base, (uint32_t)(base >> 32) & 0xFFFFu, bytes, 0x00020000u};
+  return d;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+#endif
+
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// p4 group DFT of 8 fp16 channels (raw[2e], raw[2e+1] hold (x0,x1), (x2,x3) of
+// channel e) into the A-operand units X0, X2, Xr, Xi and -Xi (8 halves each).
+//   Xr = x0 - x2 and -Xi = x1 - x3 come from one packed fp16 subtraction per
+//   channel (a single rounding of the exact difference); X0 = (x0+x1) + (x2+x3)
+//   and X2 = (x0-x1) + (x2-x3) are fp32 dot products of the fp16 pairs, rounded
+//   once to fp16.  The 1/2 of the p4 forward transform is folded into the packed
+//   weight's real planes.
+__device__ __forceinline__ void dft_p4_f16(const uint32_t (&raw)[16], u32x4 (&out)[5]) {
+  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+  const f16x2 pm = {(_Float16)1.0f, (_Float16)-1.0f};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {  // channel pair (2q, 2q+1) -> word q of each unit
+    const f16x2 a0 = __builtin_bit_cast(f16x2, raw[4 * q + 0]), b0 = __builtin_bit_cast(f16x2, raw[4 * q + 1]);
+    const f16x2 a1 = __builtin_bit_cast(f16x2, raw[4 * q + 2]), b1 = __builtin_bit_cast(f16x2, raw[4 * q + 3]);
+    const f16x2 d0 = a0 - b0, d1 = a1 - b1;  // (Xr, -Xi) of each channel
+    const float x0e = __builtin_amdgcn_fdot2(a0, ones, __builtin_amdgcn_fdot2(b0, ones, 0.0f, false), false);
+    const float x0o = __builtin_amdgcn_fdot2(a1, ones, __builtin_amdgcn_fdot2(b1, ones, 0.0f, false), false);
+    const float x2e = __builtin_amdgcn_fdot2(a0, pm, __builtin_amdgcn_fdot2(b0, pm, 0.0f, false), false);
+    const float x2o = __builtin_amdgcn_fdot2(a1, pm, __builtin_amdgcn_fdot2(b1, pm, 0.0f, false), false);
+    const f16x2 X0 = {(_Float16)x0e, (_Float16)x0o};
+    const f16x2 X2 = {(_Float16)x2e, (_Float16)x2o};
+    const uint32_t nxi = __builtin_bit_cast(uint32_t, __builtin_shufflevector(d0, d1, 1, 3));
+    out[0][q] = __builtin_bit_cast(uint32_t, X0);
+    out[1][q] = __builtin_bit_cast(uint32_t, X2);
+    out[2][q] = __builtin_bit_cast(uint32_t, __builtin_shufflevector(d0, d1, 0, 2));
+    out[3][q] = nxi ^ 0x80008000u;
+    out[4][q] = nxi;
+  }
+}
+#endif
 
 // How x is read.
 //   kLoadNarrow: rows are not 16-byte aligned; loads of the widest power of two
@@ -90,102 +168,202 @@ __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
   constexpr int NP = n_pairs(T);
   constexpr int KS = JC / 2;              // k-steps per stage
   constexpr int BN = 32 * NB;
-  constexpr int R = JC * T;               // units of one output channel per stage
+  constexpr int R = JC * T;               // 16-byte units of one channel row per stage
   constexpr int RP = R <= 8 ? 8 : (R + 15) / 16 * 16;  // ... padded to the swizzle span
-  constexpr int IPW = BN * RP / 256;      // direct-to-LDS loads per wave per stage
-  constexpr int NS = kFwdStages;
   constexpr int ELT = (int)sizeof(Elt);
+  // x through an LDS ring (buffer loads straight into LDS) when rows are 16-byte
+  // aligned and the ring fits; otherwise x is read into registers synchronously.
+  constexpr bool XLDS = LOAD != kLoadNarrow && T <= 8;
+  constexpr int STAGE_UNITS = BN * RP + (XLDS ? kFwdRows * RP : 0);
+  constexpr int NS = (4 * STAGE_UNITS * 16 <= 160 * 1024) ? 4 : 3;  // ring depth
+  constexpr int DIST = NS - 1;            // stages loaded ahead
+  constexpr int IPW = BN * RP / 256;      // weight DMA loads per wave per stage
+  constexpr int IPWX = XLDS ? 32 * RP / 64 : 0;  // x DMA loads per wave per stage
   constexpr int GB = G * T * ELT;         // bytes of one lane's x block per k-step (16*T)
-  constexpr int NW = LOAD == kLoadNarrow ? pow2_part(T * ELT) : 16;  // x load width
-  constexpr int XL = KS * GB / NW;        // x loads per stage
-  // Loads issued after weight stage st when stage st starts: x of stages st..st+2
-  // and weight stages st+1, st+2.
-  constexpr int WAIT_B = 3 * XL + 2 * IPW;
-  constexpr bool kWaitExact = WAIT_B < 64;
-  static_assert(JC % 2 == 0 && (BN * RP) % 256 == 0, "tile shape");
+  constexpr int NW = LOAD == kLoadNarrow ? pow2_part(T * ELT) : 16;  // register-path width
+  constexpr int XL = XLDS ? 0 : KS * GB / NW;  // register-path x loads per stage
+  static_assert(JC % 2 == 0 && (BN * RP) % 256 == 0 && (32 * RP) % 64 == 0, "tile shape");
+  static_assert(NS * STAGE_UNITS * 16 <= 160 * 1024, "LDS budget");
+  // vmcnt at the top of a stage (see the pipeline notes below); a count beyond the
+  // counter's range falls back to waiting for every load.
+  constexpr int WAIT_TOP_N = XLDS ? (DIST - 2) * (IPW + IPWX) : (DIST - 1) * (XL + IPW);
+  constexpr int WAIT_TOP = WAIT_TOP_N < 64 ? WAIT_TOP_N : 0;
+  constexpr int WAIT_PRO = XLDS ? (DIST - 1) * (IPW + IPWX) : 0;
+  static_assert(WAIT_PRO < 64 && IPW < 64, "vmcnt range");
 
-  __shared__ u32x4 ring[NS][BN * RP];
+  __shared__ u32x4 ringB[NS][BN * RP];
+  __shared__ u32x4 ringX[XLDS ? NS : 1][XLDS ? kFwdRows * RP : 1];
+
+  // Persistent schedule: workgroup b takes the tiles xcd_remap(b + k*gridDim.x)
+  // for k = 0, 1, ... and walks them as one stream of K stages, so the loads of a
+  // tile's first stages overlap the previous tile's last stages and epilogue.  With
+  // gridDim.x a multiple of 8, all of a workgroup's tiles map to its own XCD, and
+  // the XCD's concurrent workgroups share row blocks of x in its L2.
+  const int b0 = blockIdx.x, grid = gridDim.x;
+  if (b0 >= a.numTiles) return;
+  const int myTiles = (a.numTiles - b0 + grid - 1) / grid;
+  const int nst = a.Jpad / JC;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lrow = lane & 31, khalf = lane >> 5;
-  const int tile = xcd_remap(blockIdx.x, a.numTiles);
-  const int rowTile = tile / a.colTiles, colTile = tile - rowTile * a.colTiles;
-  const int row0 = rowTile * kFwdRows, col0 = colTile * BN;
-  const int nst = a.Jpad / JC;
   const uint32_t rowBytes = (uint32_t)a.Cin * T * ELT;
+  const uint32_t colStride = (uint32_t)a.Jpad * T * 16u;  // packed bytes per output channel
 
-  // x rows of this workgroup: rows past N fall outside the descriptor and read 0.
-  const int tileRows = min(kFwdRows, a.N - row0);
-  const __amdgpu_buffer_rsrc_t xr =
-      make_rsrc(static_cast<const char*>(a.x) + (size_t)row0 * rowBytes, (uint32_t)tileRows * rowBytes);
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.wp, a.wpBytes);
-  const uint32_t xLaneOff = (uint32_t)(wave * 32 + lrow) * rowBytes;
+  auto tile_row0 = [&](int k) __attribute__((always_inline)) {
+    return (xcd_remap(b0 + k * grid, a.numTiles) / a.colTiles) * kFwdRows;
+  };
+  auto tile_col0 = [&](int k) __attribute__((always_inline)) {
+    const int t = xcd_remap(b0 + k * grid, a.numTiles);
+    return (t - (t / a.colTiles) * a.colTiles) * BN;
+  };
 
-  // Direct-to-LDS source offsets: position P = (wave*IPW + i)*64 + lane of a stage
-  // holds unit r = (P % RP) ^ ring_swz(o) of output channel o = P / RP.
+  // Weight ring: position P = (wave*IPW + i)*64 + lane of a stage holds unit
+  // r = (P % RP) ^ ring_swz(o) of output channel o = P / RP.  Offsets are relative
+  // to the stage's first byte in output channel col0; channels past D' fall
+  // outside the descriptor and read zero.
   uint32_t bOff[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
     const int P = (wave * IPW + i) * 64 + lane;
     const int o = P / RP, pos = P - o * RP;
     const int r = pos ^ ring_swz<RP>(o);
-    const int og = min(col0 + o, a.Dout - 1);
-    const int rr = r < R ? r : 0;  // padding positions load an arbitrary valid unit
-    bOff[i] = ((uint32_t)og * a.Jpad + rr / T) * T * 16u + (uint32_t)(rr % T) * 16u;
+    const int rr = r < R ? r : 0;  // padding positions load an arbitrary unit
+    bOff[i] = (uint32_t)o * colStride + (uint32_t)rr * 16u;
+  }
+  // x ring (each wave loads and reads only its own 32 rows): position
+  // P = wave*32*RP + i*64 + lane holds unit u = (P % RP) ^ ring_swz(row) of row
+  // P / RP; unit u of a stage is bytes [16u, 16u+16) of the row's JC*G channels.
+  // Rows past N fall outside the descriptor and read zero.
+  uint32_t xOff[IPWX > 0 ? IPWX : 1];
+  int xCh[IPWX > 0 ? IPWX : 1];
+#pragma unroll
+  for (int i = 0; i < IPWX; ++i) {
+    const int P = wave * 32 * RP + i * 64 + lane;
+    const int row = P / RP, pos = P - row * RP;
+    const int u = pos ^ ring_swz<RP>(row);
+    const int uu = u < R ? u : 0;
+    xOff[i] = (uint32_t)row * rowBytes + (uint32_t)uu * 16u;
+    xCh[i] = (uu * 16) / (T * ELT);  // channel (within the stage) of the unit's first element
   }
 
-  // Weight stage st into ring slot st % NS.  Stages past the end read nothing
-  // (out-of-range offsets), so the loop body needs no branch.
-  auto issue_b = [&](int st) {
-    const uint32_t stOff = st < nst ? (uint32_t)st * JC * T * 16u : kOob;
-    u32x4* dst = &ring[st % NS][wave * IPW * 64];
+  // Stage g of the stream = stage st of this workgroup's tile k (g = k*nst + st).
+  // Every stage issues the same loads; past the stream they have an empty range
+  // and read nothing.  Tile geometry is recomputed only when the loader crosses
+  // into the next tile; per stage only the scalar descriptor base moves.
+  int issK = 0, issSt = 0;  // next stage to load
+  uint64_t bTileBase = 0, xTileBase = 0;
+  uint32_t bTileBytes = 0, xTileBytes = 0;
+  auto set_issue_tile = [&](int k) __attribute__((always_inline)) {
+    if (k < myTiles) {
+      const int row0 = tile_row0(k), col0 = tile_col0(k);
+      bTileBase = reinterpret_cast<uint64_t>(a.wp) + (uint64_t)col0 * colStride;
+      bTileBytes = (uint32_t)(a.Dout - col0) * colStride;
+      xTileBase = reinterpret_cast<uint64_t>(a.x) + (uint64_t)row0 * rowBytes;
+      xTileBytes = (uint32_t)min(kFwdRows, a.N - row0) * rowBytes;
+    } else {
+      bTileBytes = 0;
+      xTileBytes = 0;
+    }
+  };
+  set_issue_tile(0);
+  auto issue_stage = [&](int g) __attribute__((always_inline)) {
+    {
+      // Bytes left in the tile from this stage on (0 past the stream, and for x 0
+      // once the stage starts beyond the row's last channel, in the padding).
+      const uint32_t st0 = (uint32_t)issSt * JC * T * 16u;
+      const BufDesc d = desc_at(bTileBase + st0, (issK < myTiles && bTileBytes > st0) ? bTileBytes - st0 : 0u);
+      const uint32_t dst = lds_addr(&ringB[g % NS][wave * IPW * 64]);
 #pragma unroll
-    for (int i = 0; i < IPW; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          wr, (__attribute__((address_space(3))) void*)(dst + i * 64), 16, bOff[i] + stOff, 0, 0, 0);
+      for (int i = 0; i < IPW; ++i) dma16(d, bOff[i], dst + i * 1024u);
+    }
+    if constexpr (XLDS) {
+      const int c0 = issSt * JC * G;
+      const uint32_t st0 = (uint32_t)c0 * T * ELT;
+      const BufDesc d = desc_at(xTileBase + st0, (issK < myTiles && xTileBytes > st0) ? xTileBytes - st0 : 0u);
+      const uint32_t dst = lds_addr(&ringX[g % NS][wave * 32 * RP]);
+#pragma unroll
+      for (int i = 0; i < IPWX; ++i) {
+        const uint32_t off = (LOAD == kLoadFull || c0 + xCh[i] < a.Cin) ? xOff[i] : kOob;
+        dma16(d, off, dst + i * 1024u);
+      }
+    }
+    if (++issSt == nst) {
+      issSt = 0;
+      set_issue_tile(++issK);
+    }
   };
 
-  uint32_t raw[2][KS][4 * T];
+  uint32_t raw[KS][4 * T];
   u32x4 af[2][KS][T + NP];
 
-  // x of stage st into raw buffer `rb`.  Channels past C' read as zero, except in
-  // kLoadFull mode where the stages past the end read arbitrary in-bounds data
-  // that is transformed but never multiplied.
-  auto issue_x = [&](int st, auto rbTag) {
-    constexpr int rb = decltype(rbTag)::value;
+  // Register path: x of stream stage g for this lane (row lrow, group 2s+khalf).
+  auto load_xreg = [&](int g) __attribute__((always_inline)) {
+    if constexpr (!XLDS) {
+      const int k = g / nst, st = g - k * nst;
+      const bool live = k < myTiles;
+      const int row0 = live ? tile_row0(k) : 0;
+      const __amdgpu_buffer_rsrc_t xr =
+          make_rsrc(static_cast<const char*>(a.x) + (size_t)row0 * rowBytes,
+                    (uint32_t)max(0, min(kFwdRows, a.N - row0)) * rowBytes);
+      const uint32_t xLaneOff = (uint32_t)(wave * 32 + lrow) * rowBytes;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const int cfirst = (st * JC + 2 * s + khalf) * G;
-      const uint32_t base = xLaneOff + (uint32_t)cfirst * T * ELT;
+      for (int s = 0; s < KS; ++s) {
+        const int cfirst = (st * JC + 2 * s + khalf) * G;
+        const uint32_t base = xLaneOff + (uint32_t)cfirst * T * ELT;
 #pragma unroll
-      for (int b = 0; b < GB; b += NW) {
-        const int chv = cfirst + b / (T * ELT);
-        const uint32_t off = (LOAD == kLoadFull || chv < a.Cin) ? base + b : kOob;
-        if constexpr (NW == 16) {
-          const u32x4 val = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
-          raw[rb][s][b / 4 + 0] = val[0];
-          raw[rb][s][b / 4 + 1] = val[1];
-          raw[rb][s][b / 4 + 2] = val[2];
-          raw[rb][s][b / 4 + 3] = val[3];
-        } else if constexpr (NW == 8) {
-          const u32x2 val = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(xr, off, 0, 0));
-          raw[rb][s][b / 4 + 0] = val[0];
-          raw[rb][s][b / 4 + 1] = val[1];
-        } else if constexpr (NW == 4) {
-          raw[rb][s][b / 4] = __builtin_amdgcn_raw_buffer_load_b32(xr, off, 0, 0);
-        } else {
-          const uint32_t hv = __builtin_amdgcn_raw_buffer_load_b16(xr, off, 0, 0);
-          if ((b & 2) == 0) raw[rb][s][b / 4] = hv;
-          else raw[rb][s][b / 4] |= hv << 16;
+        for (int b = 0; b < GB; b += NW) {
+          const int chv = cfirst + b / (T * ELT);
+          const uint32_t off = (live && (LOAD == kLoadFull || chv < a.Cin)) ? base + b : kOob;
+          if constexpr (NW == 16) {
+            const u32x4 val = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+            raw[s][b / 4 + 0] = val[0];
+            raw[s][b / 4 + 1] = val[1];
+            raw[s][b / 4 + 2] = val[2];
+            raw[s][b / 4 + 3] = val[3];
+          } else if constexpr (NW == 8) {
+            const u32x2 val = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(xr, off, 0, 0));
+            raw[s][b / 4 + 0] = val[0];
+            raw[s][b / 4 + 1] = val[1];
+          } else if constexpr (NW == 4) {
+            raw[s][b / 4] = __builtin_amdgcn_raw_buffer_load_b32(xr, off, 0, 0);
+          } else {
+            const uint32_t hv = __builtin_amdgcn_raw_buffer_load_b16(xr, off, 0, 0);
+            if ((b & 2) == 0) raw[s][b / 4] = hv;
+            else raw[s][b / 4] |= hv << 16;
+          }
         }
       }
     }
   };
 
-  // Group DFT of raw buffer `rb` into A-operand buffer `ab`.
-  auto transform = [&](auto rbTag, auto abTag) {
-    constexpr int rb = decltype(rbTag)::value, ab = decltype(abTag)::value;
+  // LDS path: this lane's x of stream stage g (k-step s: units (2s+khalf)*T .. +T).
+  auto read_xlds = [&](int g) __attribute__((always_inline)) {
+    if constexpr (XLDS) {
+      const u32x4* slot = ringX[g % NS];
+      const int row = wave * 32 + lrow;
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int v = 0; v < T; ++v) {
+          const int u = (2 * s + khalf) * T + v;
+          const u32x4 val = slot[row * RP + (u ^ ring_swz<RP>(row))];
+          raw[s][4 * v + 0] = val[0];
+          raw[s][4 * v + 1] = val[1];
+          raw[s][4 * v + 2] = val[2];
+          raw[s][4 * v + 3] = val[3];
+        }
+    }
+  };
+
+  // Group DFT of the raw stage into A-operand buffer `ab`.
+  auto transform = [&](auto abTag) __attribute__((always_inline)) {
+    constexpr int ab = decltype(abTag)::value;
+    if constexpr (T == 4 && ELT == 2) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) dft_p4_f16(raw[s], af[ab][s]);
+      return;
+    }
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       float pl[T][G];
@@ -196,13 +374,13 @@ __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
         for (int h = 0; h < T; ++h) {
           const int i = e * T + h;
           if constexpr (ELT == 2) {
-            const uint16_t bits = (uint16_t)(raw[rb][s][i / 2] >> ((i & 1) * 16));
+            const uint16_t bits = (uint16_t)(raw[s][i / 2] >> ((i & 1) * 16));
             v[h] = (float)__builtin_bit_cast(_Float16, bits);
           } else {
-            v[h] = __builtin_bit_cast(float, raw[rb][s][i]);
+            v[h] = __builtin_bit_cast(float, raw[s][i]);
           }
         }
-        Dft<T, true>::run(v, o, a.tw);
+        Dft<T, false>::run(v, o, a.tw);
 #pragma unroll
         for (int p = 0; p < T; ++p) pl[p][e] = o[p];
       }
@@ -214,14 +392,16 @@ __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
   };
 
   f32x16 acc[T][NB];
+  auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int p = 0; p < T; ++p)
+    for (int p = 0; p < T; ++p)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[p][nb][r] = 0.0f;
+        for (int r = 0; r < 16; ++r) acc[p][nb][r] = 0.0f;
+  };
 
-  auto load_bfrag = [&](u32x4 (&bf)[T], const u32x4* slot, int s, int nb) {
+  auto load_bfrag = [&](u32x4 (&bf)[T], const u32x4* slot, int s, int nb) __attribute__((always_inline)) {
     const int o = nb * 32 + lrow;
 #pragma unroll
     for (int p = 0; p < T; ++p) {
@@ -230,7 +410,7 @@ __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
     }
   };
 
-  auto mfma_block = [&](const u32x4 (&bf)[T], auto abTag, int s, int nb) {
+  auto mfma_block = [&](const u32x4 (&bf)[T], auto abTag, int s, int nb) __attribute__((always_inline)) {
     constexpr int ab = decltype(abTag)::value;
 #pragma unroll
     for (int p = 0; p < NR; ++p) E::mfma(acc[p][nb], af[ab][s][p], bf[p]);
@@ -244,37 +424,70 @@ __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
     }
   };
 
+  // Epilogue of tile k: accumulator slot r of lane l holds row 8*(r/4) + 4*(l/32) +
+  // r%4 and column l%32 of each 32x32 block.
+  Elt* __restrict__ yout = static_cast<Elt*>(a.y);
+  auto epilogue = [&](int k) __attribute__((always_inline)) {
+    const int row0 = tile_row0(k), col0 = tile_col0(k);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int col = col0 + nb * 32 + lrow;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = row0 + wave * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+        if (row < a.N && col < a.Dout) {
+          float P[T], yv[T];
+#pragma unroll
+          for (int p = 0; p < T; ++p) P[p] = acc[p][nb][r];
+          Idft<T, false>::run(P, yv, a.tw);
+          store_group<T, Elt>(yout + ((size_t)row * a.Dout + col) * T, yv);
+        }
+      }
+    }
+  };
+
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
 
-  // Prologue: weight stages 0..2 and x stages 0, 1 in flight; x stage 0
-  // transformed; x stage 2 in flight.
-  issue_b(0);
-  issue_b(1);
-  issue_b(2);
-  issue_x(0, I0{});
-  issue_x(1, I1{});
-  if constexpr (2 * XL < 64) wait_vmcnt<XL>();  // x stage 0 (and everything before it)
-  else wait_vmcnt<0>();
-  transform(I0{}, I0{});
-  issue_x(2, I0{});
+  // Pipeline.  Stream stage j (weight, and x on the LDS path) is loaded DIST
+  // stages ahead, at the top of stage j - DIST, into ring slot j % NS (the slot of
+  // stage j - DIST - 1, which every wave has finished with once it passes that
+  // stage's barrier).  Stage g multiplies weight stage g with the A fragments of x
+  // stage g while the DFT of x stage g+1 (already in LDS) fills the other fragment
+  // buffer.  At the top of stage g the loads issued after x stage g+1 are those of
+  // stages g+2 .. g+DIST-1: WAIT_TOP of them may still be outstanding.  Register
+  // path: x stage g+1 is loaded at the top of stage g, before the weight loads, and
+  // waited for (all but the IPW weight loads behind it).
+  zero_acc();
+#pragma unroll
+  for (int j = 0; j < DIST; ++j) issue_stage(j);
+  if constexpr (XLDS) {
+    wait_vmcnt<WAIT_PRO>();  // x stage 0
+    read_xlds(0);
+  } else {
+    load_xreg(0);
+    wait_vmcnt<0>();
+  }
+  transform(I0{});
 
-  // Stage st.  x stage j lives in raw[j & 1] and af[j & 1]; `cur` = st & 1 is a
-  // compile-time constant so that the fragments stay in registers.  Every stage
-  // issues the same loads (weight st+3, x st+3), in range or not, so the wait for
-  // weight stage st is a constant count.
-  auto stage = [&](int st, auto curTag) {
+  auto stage = [&](int g, auto curTag) __attribute__((always_inline)) {
     constexpr int cur = decltype(curTag)::value;
     using Cur = std::integral_constant<int, cur>;
     using Nxt = std::integral_constant<int, cur ^ 1>;
-    if constexpr (kWaitExact) wait_vmcnt<WAIT_B>();
-    else wait_vmcnt<0>();
-    // Plain barrier (no fence): the ring reads of stage st-1 have been consumed by
-    // MFMAs, and a fence would also wait for the prefetches in flight.
+    wait_vmcnt<WAIT_TOP>();
+    // Plain barrier (no fence): ring reads of stage g-1 have been consumed, and a
+    // fence would also wait for the loads in flight.
     __builtin_amdgcn_s_barrier();
-    issue_b(st + 3);  // refills the slot of stage st-1
+    if constexpr (XLDS) {
+      issue_stage(g + DIST);
+      read_xlds(g + 1);
+    } else {
+      load_xreg(g + 1);
+      issue_stage(g + DIST);
+      wait_vmcnt<IPW>();
+    }
 
-    const u32x4* slot = ring[st % NS];
+    const u32x4* slot = ringB[g % NS];
     u32x4 bcur[T], bnext[T];
     load_bfrag(bcur, slot, 0, 0);
 #pragma unroll
@@ -282,43 +495,28 @@ __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
       const int s = idx / NB, nb = idx % NB;
       if (idx + 1 < KS * NB) load_bfrag(bnext, slot, (idx + 1) / NB, (idx + 1) % NB);
       mfma_block(bcur, Cur{}, s, nb);
-      if (idx == 0) transform(Nxt{}, Nxt{});  // x stage st+1; overlaps the MFMA chains
+      if (idx == 0) transform(Nxt{});  // x stage g+1; overlaps the MFMA chains
       if (idx + 1 < KS * NB) {
 #pragma unroll
         for (int p = 0; p < T; ++p) bcur[p] = bnext[p];
       }
     }
-    issue_x(st + 3, Nxt{});
   };
 
-  int st = 0;
-  for (; st + 1 < nst; st += 2) {
-    stage(st, I0{});
-    stage(st + 1, I1{});
+  // nst is even (the packed input axis is a multiple of 4 groups, two per stage),
+  // so every tile starts on fragment buffer 0.
+  int g = 0;
+  for (int k = 0; k < myTiles; ++k) {
+    for (int st = 0; st < nst; st += 2, g += 2) {
+      stage(g, I0{});
+      stage(g + 1, I1{});
+    }
+    epilogue(k);
+    zero_acc();
   }
-  if (st < nst) stage(st, I0{});
   // Drain the look-ahead loads (all out of range) before the workgroup's LDS can
   // be reused.
   wait_vmcnt<0>();
-
-  // Epilogue: accumulator slot r of lane l holds row 8*(r/4) + 4*(l/32) + r%4 and
-  // column l%32 of each 32x32 block.
-  Elt* __restrict__ yout = static_cast<Elt*>(a.y);
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int col = col0 + nb * 32 + lrow;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = row0 + wave * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
-      if (row < a.N && col < a.Dout) {
-        float P[T], yv[T];
-#pragma unroll
-        for (int p = 0; p < T; ++p) P[p] = acc[p][nb][r];
-        Idft<T, false>::run(P, yv, a.tw);
-        store_group<T, Elt>(yout + ((size_t)row * a.Dout + col) * T, yv);
-      }
-    }
-  }
 #endif  // __HIP_DEVICE_COMPILE__
 }
 

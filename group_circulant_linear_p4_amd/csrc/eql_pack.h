@@ -3,7 +3,7 @@
 // products need the DFT of w, and conjugate symmetry keeps half of it).
 //
 // One thread per (out, in) pair of the packed matrix (plus the zero padding of the
-// input axis up to a whole 16-byte group).  It reads the T shared parameters,
+// input axis up to the padded group count).  It reads the T shared parameters,
 // transforms them in fp32 (p4: butterflies only) and rounds each plane once to
 // the element type.  In the input-gradient mode the weight is the transposed,
 // group-reversed w~[c][d][t] = w[d][c][(-t) mod T]; its spectrum is the conjugate,
@@ -39,6 +39,12 @@ __global__ void __launch_bounds__(256) eql_pack_kernel(const PackArgs a) {
     float v[T];
     load_group<T, Elt>(static_cast<const Elt*>(a.w) + ((size_t)d * a.Cp + c) * T, v);
     Dft<T, false>::run(v, pl, a.tw);
+    if constexpr (T == 4) {
+      // p4: the 1/2 of the forward transform's real planes lives in the weight
+      // (exact: a power of two), so the activation transform is adds only.
+      pl[0] *= 0.5f;
+      pl[1] *= 0.5f;
+    }
     if (a.transposed) {
 #pragma unroll
       for (int p = NR + 1; p < T; p += 2) pl[p] = -pl[p];

@@ -77,6 +77,9 @@ typedef enum {
  *   then for k = 1 .. ceil(T/2)-1, two planes:
  *                               sum_t w_t cos(2 pi t k / T)          (Re)
  *                              -sum_t w_t sin(2 pi t k / T)          (Im)
+ * For T = 4 the two real planes (k = 0 and k = 2) are stored multiplied by 1/2:
+ * the p4 transform's halving is carried by the weight, so the activations'
+ * transform needs only additions and subtractions (the scale is exact).
  * In EQL_PACK_BWDX mode the weight is w~[c][d][t] = w[d][c][(-t) mod T]
  * (out = c, in = d), whose spectrum is the complex conjugate: the Im planes
  * change sign.
