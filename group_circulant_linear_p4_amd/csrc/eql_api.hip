@@ -118,24 +118,41 @@ int run_fwd(const void* x, const void* wp, void* y, int64_t N, int64_t Cin, int6
   return EQL_OK;
 }
 
-struct SplitPlan {
-  int64_t S, rowsPerSplit, dTiles, cTiles;
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+// Weight-gradient plan.  The workspace holds, in order (each section 256-byte
+// aligned): the half spectra of dy and of x as MFMA operand units (2G rows per
+// k-step, zero rows past N), then S fp32 partial spectra [S][T][Dp][Cp].
+struct BwdwPlan {
+  int64_t kgCount = 0, S = 0, kgPerSplit = 0, dTiles = 0, cTiles = 0;
+  int nb = 1;
+  size_t dyhBytes = 0, xhBytes = 0, partBytes = 0;
+  size_t total() const { return dyhBytes + xhBytes + partBytes; }
 };
 
-// Row ranges of the weight-gradient reduction: enough ranges to give every
-// compute unit one workgroup, each range a whole number of row chunks.
-SplitPlan plan_bwdw(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype) {
-  SplitPlan p{};
-  const int64_t chunk = (int64_t)bwdw_ksc(T) * 2 * group_channels(dtype);
+constexpr int64_t kMinStepsPerSplit = 16;  // keeps partial-spectrum traffic small
+
+BwdwPlan plan_bwdw(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype) {
+  BwdwPlan p;
+  // Column tile: the widest one unless a half-width tile pads C' less.
+  p.nb = bwdw_nb_max(T);
+  if (p.nb > 1) {
+    const int half = p.nb / 2;
+    if (ceil_div(Cp, 32 * half) * half < ceil_div(Cp, 32 * p.nb) * p.nb) p.nb = half;
+  }
   p.dTiles = ceil_div(Dp, kBwdwRowsD);
-  p.cTiles = ceil_div(Cp, 32 * bwdw_nb(T));
+  p.cTiles = ceil_div(Cp, 32 * p.nb);
   if (N == 0) return p;
+  p.kgCount = ceil_div(N, 2 * group_channels(dtype));
+  // Row ranges (k-step ranges): enough to give every compute unit one item.
   const int64_t tiles = p.dTiles * p.cTiles;
   int64_t S = tiles >= kTargetWorkgroups ? 1 : kTargetWorkgroups / tiles;
-  const int64_t maxS = ceil_div(N, chunk);
-  if (S > maxS) S = maxS;
-  p.rowsPerSplit = ceil_div(ceil_div(N, S), chunk) * chunk;
-  p.S = ceil_div(N, p.rowsPerSplit);
+  S = std::min<int64_t>(S, std::max<int64_t>(1, p.kgCount / kMinStepsPerSplit));
+  p.kgPerSplit = ceil_div(p.kgCount, S);
+  p.S = ceil_div(p.kgCount, p.kgPerSplit);
+  p.dyhBytes = align256((size_t)p.kgCount * T * 2 * (size_t)Dp * 16);
+  p.xhBytes = align256((size_t)p.kgCount * T * 2 * (size_t)Cp * 16);
+  p.partBytes = (size_t)p.S * T * (size_t)Dp * (size_t)Cp * sizeof(float);
   return p;
 }
 
@@ -202,52 +219,67 @@ int eqlinear_bwd_x(const void* dy, const void* w_packed_bwdx, void* dx, int64_t 
 
 size_t eqlinear_bwd_w_workspace_bytes(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype) {
   if (check_sizes(N, Cp, Dp, T, dtype) != EQL_OK) return 0;
-  const SplitPlan p = plan_bwdw(N, Cp, Dp, T, dtype);
-  return (size_t)p.S * T * (size_t)Dp * (size_t)Cp * sizeof(float);
+  return plan_bwdw(N, Cp, Dp, T, dtype).total();
 }
 
 int eqlinear_bwd_w(const void* x, const void* dy, void* dw, void* workspace, size_t ws_bytes,
                    int64_t N, int64_t Cp, int64_t Dp, int T, int dtype, void* stream) {
   int st = check_sizes(N, Cp, Dp, T, dtype);
   if (st != EQL_OK) return st;
-  const SplitPlan p = plan_bwdw(N, Cp, Dp, T, dtype);
-  const size_t need = (size_t)p.S * T * (size_t)Dp * (size_t)Cp * sizeof(float);
+  const BwdwPlan p = plan_bwdw(N, Cp, Dp, T, dtype);
   if (!dw || (N > 0 && (!x || !dy || !workspace))) return EQL_EINVAL;
-  if (ws_bytes < need) return EQL_EINVAL;
+  if (ws_bytes < p.total()) return EQL_EINVAL;
   if (!aligned16(dw) || (N > 0 && (!aligned16(x) || !aligned16(dy) || !aligned16(workspace))))
     return EQL_EALIGN;
-  const int64_t tiles = p.S * p.dTiles * p.cTiles;
+  const int64_t items = p.S * p.dTiles * p.cTiles;
+  const int64_t gdy = ceil_div(p.kgCount * 2 * Dp, 256), gx = ceil_div(p.kgCount * 2 * Cp, 256);
   const int64_t rgrid = ceil_div(Dp * Cp, 256);
-  if (tiles > kMaxGrid || rgrid > kMaxGrid) return EQL_EINVAL;
+  if (items > kMaxGrid || gdy > kMaxGrid || gx > kMaxGrid || rgrid > kMaxGrid) return EQL_EINVAL;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Twiddles tw = make_twiddles(T);
+  char* ws = static_cast<char*>(workspace);
+  float* part = reinterpret_cast<float*>(ws + p.dyhBytes + p.xhBytes);
+  const bool f16 = dtype == EQL_F16;
   if (p.S > 0) {
+    SpecArgs sp{};
+    sp.N = (int)N;
+    sp.kgCount = (int)p.kgCount;
+    sp.tw = tw;
+    sp.m = dy;
+    sp.out = ws;
+    sp.K = (int)Dp;
+    hipError_t e = f16 ? launch_spec_f16(T, sp, (unsigned)gdy, s) : launch_spec_f32(T, sp, (unsigned)gdy, s);
+    if (e != hipSuccess) return EQL_EHIP;
+    sp.m = x;
+    sp.out = ws + p.dyhBytes;
+    sp.K = (int)Cp;
+    e = f16 ? launch_spec_f16(T, sp, (unsigned)gx, s) : launch_spec_f32(T, sp, (unsigned)gx, s);
+    if (e != hipSuccess) return EQL_EHIP;
+
     BwdwArgs a{};
-    a.x = x;
-    a.dy = dy;
-    a.ws = static_cast<float*>(workspace);
-    a.N = (int)N;
-    a.Cp = (int)Cp;
+    a.dyh = ws;
+    a.xh = ws + p.dyhBytes;
+    a.ws = part;
     a.Dp = (int)Dp;
-    a.rowsPerSplit = (int)p.rowsPerSplit;
-    a.cTiles = (int)p.cTiles;
+    a.Cp = (int)Cp;
+    a.kgCount = (int)p.kgCount;
+    a.kgPerSplit = (int)p.kgPerSplit;
     a.dTiles = (int)p.dTiles;
-    a.numTiles = (int)tiles;
-    a.tw = tw;
-    const hipError_t e = dtype == EQL_F16 ? launch_bwdw_f16(T, a, (unsigned)tiles, s)
-                                          : launch_bwdw_f32(T, a, (unsigned)tiles, s);
+    a.cTiles = (int)p.cTiles;
+    a.numItems = (int)items;
+    e = f16 ? launch_bwdw_f16(T, p.nb, a, (unsigned)items, s) : launch_bwdw_f32(T, p.nb, a, (unsigned)items, s);
     if (e != hipSuccess) return EQL_EHIP;
   }
   BwdwReduceArgs r{};
-  r.ws = static_cast<const float*>(workspace);
+  r.ws = part;
   r.dw = dw;
   r.S = (int)p.S;
   r.Dp = (int)Dp;
   r.Cp = (int)Cp;
   r.tw = tw;
-  return status_of(dtype == EQL_F16 ? launch_bwdw_reduce_f16(T, r, (unsigned)rgrid, s)
-                                    : launch_bwdw_reduce_f32(T, r, (unsigned)rgrid, s));
+  return status_of(f16 ? launch_bwdw_reduce_f16(T, r, (unsigned)rgrid, s)
+                       : launch_bwdw_reduce_f32(T, r, (unsigned)rgrid, s));
 }
 
 }  // extern "C"

@@ -4,8 +4,18 @@
 namespace eql {
 
 template <int T>
-static hipError_t bwdw_one(const BwdwArgs& a, unsigned grid, hipStream_t s) {
-  return launch_kernel((const void*)&eql_bwdw_kernel<T, float, bwdw_nb(T), bwdw_ksc(T)>, grid, a, s);
+static hipError_t spec_one(const SpecArgs& a, unsigned grid, hipStream_t s) {
+  return launch_kernel((const void*)&eql_spec_kernel<T, float>, grid, a, s);
+}
+
+template <int T>
+static hipError_t bwdw_one(int NB, const BwdwArgs& a, unsigned grid, hipStream_t s) {
+  constexpr int NBM = bwdw_nb_max(T);
+  if (NB == NBM) return launch_kernel((const void*)&eql_bwdw_gemm<T, float, NBM>, grid, a, s);
+  if constexpr (NBM > 1) {
+    if (NB == NBM / 2) return launch_kernel((const void*)&eql_bwdw_gemm<T, float, NBM / 2>, grid, a, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int T>
@@ -13,8 +23,14 @@ static hipError_t reduce_one(const BwdwReduceArgs& a, unsigned grid, hipStream_t
   return launch_kernel((const void*)&eql_bwdw_reduce<T, float>, grid, a, s);
 }
 
-hipError_t launch_bwdw_f32(int T, const BwdwArgs& a, unsigned grid, hipStream_t s) {
-#define EQL_CASE(t) return bwdw_one<t>(a, grid, s);
+hipError_t launch_spec_f32(int T, const SpecArgs& a, unsigned grid, hipStream_t s) {
+#define EQL_CASE(t) return spec_one<t>(a, grid, s);
+  EQL_FOR_EACH_T(T, EQL_CASE)
+#undef EQL_CASE
+}
+
+hipError_t launch_bwdw_f32(int T, int NB, const BwdwArgs& a, unsigned grid, hipStream_t s) {
+#define EQL_CASE(t) return bwdw_one<t>(NB, a, grid, s);
   EQL_FOR_EACH_T(T, EQL_CASE)
 #undef EQL_CASE
 }

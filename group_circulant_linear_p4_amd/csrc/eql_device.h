@@ -102,12 +102,13 @@ struct Dft<4, kScaled> {
 
 // ---------------------------------------------------------------------------
 // Inverse transform of T planes back to T group values.
-// kSigma2 = false: planes computed from sigma-scaled activations and unscaled
-// weights (forward / input gradient).  kSigma2 = true: both operands were
-// sigma-scaled activations (weight gradient).  For T != 4 sigma = 1 and the two
-// coincide: y_g = (1/T) (P0 + (-1)^g P_N + 2 sum_k (cos P_re - sin P_im)).
+// kPlain = true, and every T != 4: the plain inverse of unscaled planes,
+//   y_g = (1/T) (P0 + (-1)^g P_N + 2 sum_k (cos P_re - sin P_im)).
+// kPlain = false with T = 4: the forward / input-gradient epilogue, whose real
+// planes carry an extra 1/2 (from the packed weight), making every coefficient
+// +-1/2.
 // ---------------------------------------------------------------------------
-template <int T, bool kSigma2>
+template <int T, bool kPlain>
 struct Idft {
   static __device__ __forceinline__ void run(const float (&P)[T], float (&y)[T], const Twiddles& tw) {
     constexpr int NR = n_real_planes(T);
@@ -126,7 +127,7 @@ struct Idft {
   }
 };
 
-// p4 inverse.  With activations scaled by 1/2 on the real planes every
+// p4 forward / input-gradient inverse.  With the real planes carrying 1/2 every
 // coefficient is +-1/2:  y = 1/2 ((P0 +- P2) +- Pr / Pi).
 template <>
 struct Idft<4, false> {
@@ -139,19 +140,6 @@ struct Idft<4, false> {
   }
 };
 
-// p4 inverse for the weight gradient (both operands scaled by 1/2 on the real
-// planes, so those planes carry 1/4):  dw = (P0 +- P2) +- Pr / Pi / 2.
-template <>
-struct Idft<4, true> {
-  static __device__ __forceinline__ void run(const float (&P)[4], float (&y)[4], const Twiddles&) {
-    const float a = P[0] + P[1], b = P[0] - P[1];
-    const float r = 0.5f * P[2], i = 0.5f * P[3];
-    y[0] = a + r;
-    y[1] = b - i;
-    y[2] = a - r;
-    y[3] = b + i;
-  }
-};
 
 // ---------------------------------------------------------------------------
 // Element types.  A "unit" is 16 bytes: 8 fp16 or 4 fp32 values.

@@ -1,0 +1,68 @@
+// Buffer-descriptor loads, including loads that write LDS directly, for gfx950.
+#pragma once
+
+#include "eql_device.h"
+
+namespace eql {
+
+// s_waitcnt on vector-memory loads only (lgkm and exp counters left unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+#if defined(__HIP_DEVICE_COMPILE__)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+#endif
+
+// Offsets at or beyond this value are outside every buffer: the load returns zero.
+constexpr uint32_t kOob = 0x80000000u;
+
+#if defined(__HIP_DEVICE_COMPILE__)
+// Raw buffer descriptor words (gfx9 family: dword3 = 0x00020000).
+struct BufDesc {
+  u32x4 w;
+};
+__device__ __forceinline__ BufDesc make_desc(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  BufDesc d;
+  d.w = (u32x4){(uint32_t)b, (uint32_t)(b >> 32) & 0xFFFFu, bytes, 0x00020000u};
+  return d;
+}
+
+// 16 bytes per lane from buffer offset `voff` straight into LDS at
+// lds_base + 16 * lane (no VGPR destination).  Written as an asm statement so that
+// the compiler does not add a wait for all LDS-bound loads before every later LDS
+// read (it cannot tell the ring slots apart); completion is tracked explicitly
+// with wait_vmcnt at the places that consume the data.
+//   * The hazard recognizer does not look inside the statement, so it carries its
+//     own wait states: 5 before the load (a VALU write of an SGPR read by a VMEM
+//     instruction) and 1 between the M0 write and the load that reads it.
+//   * The descriptor and LDS base are wave-uniform; readfirstlane keeps them in
+//     SGPRs even where the compiler cannot prove uniformity.  M0 is reserved by
+//     the compiler (never allocated to other values), so it needs no clobber.
+__device__ __forceinline__ void dma16(const BufDesc& d, uint32_t voff, uint32_t lds_base) {
+  const u32x4 w = {(uint32_t)__builtin_amdgcn_readfirstlane(d.w[0]), (uint32_t)__builtin_amdgcn_readfirstlane(d.w[1]),
+                   (uint32_t)__builtin_amdgcn_readfirstlane(d.w[2]), (uint32_t)__builtin_amdgcn_readfirstlane(d.w[3])};
+  asm volatile("s_nop 4\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(w)
+               : "memory");
+}
+
+// Descriptor of `bytes` bytes at `base` (words built from scalar values).
+__device__ __forceinline__ BufDesc desc_at(uint64_t base, uint32_t bytes) {
+  BufDesc d;
+  d.w = (u32x4){(uint32_t)base, (uint32_t)(base >> 32) & 0xFFFFu, bytes, 0x00020000u};
+  return d;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+#endif
+
+}  // namespace eql

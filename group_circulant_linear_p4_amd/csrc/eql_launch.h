@@ -15,9 +15,9 @@ namespace eql {
 __host__ __device__ constexpr int fwd_nb_max(int T) { return T <= 4 ? 4 : (T <= 8 ? 2 : 1); }
 // Channel groups per K chunk (two per k-step).
 __host__ __device__ constexpr int fwd_jc(int) { return 2; }
-// bwd_w: column blocks per wave and k-steps per row chunk.
-__host__ __device__ constexpr int bwdw_nb(int T) { return fwd_nb_max(T); }
-__host__ __device__ constexpr int bwdw_ksc(int T) { return T <= 4 ? 2 : 1; }
+// bwd_w GEMM: 32-column blocks per wave, the full-width tile and (when that is
+// above 1) a half-width one for narrow C'.
+__host__ __device__ constexpr int bwdw_nb_max(int T) { return fwd_nb_max(T); }
 
 // The packed weight's input axis is padded to a multiple of this many 16-byte
 // groups, so that every K stage of the forward kernel reads whole groups.
@@ -27,8 +27,10 @@ static_assert(kPackGroupAlign % fwd_jc(1) == 0 && kPackGroupAlign % fwd_jc(16) =
 // elt: 2 = fp16, 4 = fp32.  Each returns the launch status.
 hipError_t launch_fwd_f16(int T, int NB, const FwdArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_fwd_f32(int T, int NB, const FwdArgs& a, unsigned grid, hipStream_t s);
-hipError_t launch_bwdw_f16(int T, const BwdwArgs& a, unsigned grid, hipStream_t s);
-hipError_t launch_bwdw_f32(int T, const BwdwArgs& a, unsigned grid, hipStream_t s);
+hipError_t launch_spec_f16(int T, const SpecArgs& a, unsigned grid, hipStream_t s);
+hipError_t launch_spec_f32(int T, const SpecArgs& a, unsigned grid, hipStream_t s);
+hipError_t launch_bwdw_f16(int T, int NB, const BwdwArgs& a, unsigned grid, hipStream_t s);
+hipError_t launch_bwdw_f32(int T, int NB, const BwdwArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_bwdw_reduce_f16(int T, const BwdwReduceArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_bwdw_reduce_f32(int T, const BwdwReduceArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_pack_f16(int T, const PackArgs& a, unsigned grid, hipStream_t s);

@@ -34,9 +34,9 @@
  *  - Return value: an eql_status.  Arguments are validated before anything is
  *    launched; on any error nothing is launched and no memory is touched.
  *    N == 0 is valid and launches nothing.
- *  - Sizes: 1 <= T <= EQL_MAX_T, C' >= 1, D' >= 1, N >= 0; N*C'*T, N*D'*T and the
- *    weight size must stay below 2^31 elements per tensor row block of the grid
- *    (N < 2^31, C'*T < 2^24, D'*T < 2^24).
+ *  - Sizes: 1 <= T <= EQL_MAX_T, C' >= 1, D' >= 1, 0 <= N < 2^31, and one
+ *    activation row (C'*T or D'*T elements) at most 2^23 bytes; EQL_EINVAL
+ *    otherwise, also when a launch would need more than 2^24 - 1 workgroups.
  */
 #ifndef EQLINEAR_H
 #define EQLINEAR_H
@@ -124,20 +124,26 @@ int eqlinear_bwd_x(const void* dy, const void* w_packed_bwdx, void* dx, int64_t 
                    int64_t Cp, int64_t Dp, int T, int dtype, void* stream);
 
 /*
- * Scratch bytes eqlinear_bwd_w needs for this shape (fp32 split-K partials of the
- * per-frequency weight gradient).  Depends only on the arguments.
+ * Scratch bytes eqlinear_bwd_w needs for this shape.  Depends only on the
+ * arguments (0 when N == 0 or the arguments are invalid).  The workspace holds the
+ * half spectra of dy and x (each about the size of that tensor: T real planes per
+ * channel, rows padded to a multiple of 2 * 16 / sizeof(element)) followed by S
+ * fp32 partial spectra of the gradient, S * T * Dp * Cp * 4 bytes, one per row
+ * range of the reduction over N.
  */
 size_t eqlinear_bwd_w_workspace_bytes(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype);
 
 /*
  * Weight gradient: dw[d][c][t] = sum_n sum_g dy[n][d*T+g] x[n][c*T+((g-t) mod T)],
- * the dense gradient dy^T x summed over the entries tied to w[d][c][t].  Computed
- * per frequency as dY_k^T conj(X_k) (a GEMM with K = N, split over N into
- * `workspace`), then summed in a fixed order (deterministic), inverse-transformed
- * and rounded to `dtype`.  x: [N][Cp*T], dy: [N][Dp*T] read; dw: [Dp][Cp][T]
- * overwritten (zeros when N == 0, which launches one small kernel);
- * workspace: device memory of at least eqlinear_bwd_w_workspace_bytes bytes
- * (contents on entry ignored; EQL_EINVAL if ws_bytes is smaller).
+ * the dense gradient dy^T x summed over the entries tied to w[d][c][t].  Three
+ * launches: the group transforms of dy and x (fp32, rounded once to `dtype`) into
+ * the workspace; per frequency the channel GEMM dY_k^T conj(X_k) (K = N, fp32
+ * accumulation, one partial per row range); the sum of the partials in a fixed
+ * order (deterministic), the inverse transform and the rounding to `dtype`.
+ * x: [N][Cp*T], dy: [N][Dp*T] read; dw: [Dp][Cp][T] overwritten (zeros when
+ * N == 0, which launches one small kernel); workspace: device memory of at least
+ * eqlinear_bwd_w_workspace_bytes bytes, 16-byte aligned (contents on entry
+ * ignored, clobbered; EQL_EINVAL if ws_bytes is smaller).
  */
 int eqlinear_bwd_w(const void* x, const void* dy, void* dw, void* workspace, size_t ws_bytes,
                    int64_t N, int64_t Cp, int64_t Dp, int T, int dtype, void* stream);
