@@ -122,7 +122,8 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 // Weight-gradient plan.  The workspace holds, in order (each section 256-byte
 // aligned): the half spectra of dy and of x as MFMA operand units (2G rows per
-// k-step, zero rows past N), then S fp32 partial spectra [S][T][Dp][Cp].
+// k-step, zero rows past N, channels padded to whole GEMM tiles), then S fp32
+// partial spectra [S][T][Dp][Cp].
 struct BwdwPlan {
   int64_t kgCount = 0, S = 0, kgPerSplit = 0, dTiles = 0, cTiles = 0;
   int nb = 1;
@@ -150,8 +151,8 @@ BwdwPlan plan_bwdw(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype) {
   S = std::min<int64_t>(S, std::max<int64_t>(1, p.kgCount / kMinStepsPerSplit));
   p.kgPerSplit = ceil_div(p.kgCount, S);
   p.S = ceil_div(p.kgCount, p.kgPerSplit);
-  p.dyhBytes = align256((size_t)p.kgCount * T * 2 * (size_t)Dp * 16);
-  p.xhBytes = align256((size_t)p.kgCount * T * 2 * (size_t)Cp * 16);
+  p.dyhBytes = align256((size_t)p.kgCount * p.dTiles * kBwdwRowsD * T * 2 * 16);
+  p.xhBytes = align256((size_t)p.kgCount * p.cTiles * (32 * p.nb) * T * 2 * 16);
   p.partBytes = (size_t)p.S * T * (size_t)Dp * (size_t)Cp * sizeof(float);
   return p;
 }
@@ -232,7 +233,8 @@ int eqlinear_bwd_w(const void* x, const void* dy, void* dw, void* workspace, siz
   if (!aligned16(dw) || (N > 0 && (!aligned16(x) || !aligned16(dy) || !aligned16(workspace))))
     return EQL_EALIGN;
   const int64_t items = p.S * p.dTiles * p.cTiles;
-  const int64_t gdy = ceil_div(p.kgCount * 2 * Dp, 256), gx = ceil_div(p.kgCount * 2 * Cp, 256);
+  const int64_t gdy = ceil_div(p.kgCount * 2 * p.dTiles * kBwdwRowsD, 256);
+  const int64_t gx = ceil_div(p.kgCount * 2 * p.cTiles * 32 * p.nb, 256);
   const int64_t rgrid = ceil_div(Dp * Cp, 256);
   if (items > kMaxGrid || gdy > kMaxGrid || gx > kMaxGrid || rgrid > kMaxGrid) return EQL_EINVAL;
 
@@ -249,11 +251,15 @@ int eqlinear_bwd_w(const void* x, const void* dy, void* dw, void* workspace, siz
     sp.m = dy;
     sp.out = ws;
     sp.K = (int)Dp;
+    sp.W = kBwdwRowsD;
+    sp.kTiles = (int)p.dTiles;
     hipError_t e = f16 ? launch_spec_f16(T, sp, (unsigned)gdy, s) : launch_spec_f32(T, sp, (unsigned)gdy, s);
     if (e != hipSuccess) return EQL_EHIP;
     sp.m = x;
     sp.out = ws + p.dyhBytes;
     sp.K = (int)Cp;
+    sp.W = 32 * p.nb;
+    sp.kTiles = (int)p.cTiles;
     e = f16 ? launch_spec_f16(T, sp, (unsigned)gx, s) : launch_spec_f32(T, sp, (unsigned)gx, s);
     if (e != hipSuccess) return EQL_EHIP;
 

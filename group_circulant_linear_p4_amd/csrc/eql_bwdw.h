@@ -11,9 +11,10 @@
 //   1. eql_spec_kernel: the group DFT of x and of dy, once per element, rounded once
 //      to the element type and stored in the workspace as MFMA operand units: unit
 //      (kg, p, half, k) holds plane p of channel k for the G rows
-//      kg*2G + half*G .. +G (G = 16 / sizeof(element); rows past N are zero).
-//      Layout [kg][p][half][k], so the units one k-step of a channel tile needs
-//      form 2T contiguous runs.  Purely bandwidth bound.
+//      kg*2G + half*G .. +G (G = 16 / sizeof(element); rows past N and channels
+//      past the padded width are zero).  Channels are cut into tiles of the GEMM's
+//      tile width W, layout [kg][k / W][p][half][k % W], so the units one k-step of
+//      one channel tile needs are one contiguous block.  Purely bandwidth bound.
 //   2. eql_bwdw_gemm: the per-plane GEMMs.  A workgroup owns 128 output channels d
 //      (4 waves x 32) by BN = 32*NB input channels c for one range of k-steps;
 //      both operands stream into NS-deep LDS rings by buffer->LDS loads, so the
@@ -32,14 +33,14 @@ namespace eql {
 
 struct SpecArgs {
   const void* m;    // [N][K*T]
-  void* out;        // units [kgCount][T][2][K]
-  int N, K, kgCount;
+  void* out;        // units [kgCount][kTiles][T][2][W]
+  int N, K, kgCount, W, kTiles;
   Twiddles tw;
 };
 
 struct BwdwArgs {
-  const void* dyh;  // dY units [kgCount][T][2][Dp]
-  const void* xh;   // X units  [kgCount][T][2][Cp]
+  const void* dyh;  // dY units [kgCount][dTiles][T][2][128]
+  const void* xh;   // X units  [kgCount][cTiles][T][2][32 NB]
   float* ws;        // [S][T][Dp][Cp] fp32 partial spectra
   int Dp, Cp, kgCount, kgPerSplit, dTiles, cTiles, numItems;
 };
@@ -58,10 +59,10 @@ __global__ void __launch_bounds__(256) eql_spec_kernel(const SpecArgs a) {
   using E = EltT<Elt>;
   constexpr int G = E::kPerUnit;
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-  const size_t total = (size_t)a.kgCount * 2 * a.K;
-  if (idx >= total) return;
-  const int k = (int)(idx % a.K);
-  const size_t rest = idx / a.K;
+  const size_t width = (size_t)a.kTiles * a.W;  // padded channel count
+  if (idx >= (size_t)a.kgCount * 2 * width) return;
+  const int k = (int)(idx % width);
+  const size_t rest = idx / width;
   const int half = (int)(rest & 1);
   const int kg = (int)(rest >> 1);
   const int row0 = kg * 2 * G + half * G;
@@ -70,7 +71,7 @@ __global__ void __launch_bounds__(256) eql_spec_kernel(const SpecArgs a) {
   for (int e = 0; e < G; ++e) {
     float v[T], o[T];
     const int row = row0 + e;
-    if (row < a.N) {
+    if (row < a.N && k < a.K) {
       load_group<T, Elt>(static_cast<const Elt*>(a.m) + ((size_t)row * a.K + k) * T, v);
     } else {
 #pragma unroll
@@ -80,9 +81,10 @@ __global__ void __launch_bounds__(256) eql_spec_kernel(const SpecArgs a) {
 #pragma unroll
     for (int p = 0; p < T; ++p) pl[p][e] = o[p];
   }
-  u32x4* out = static_cast<u32x4*>(a.out);
+  const int kt = k / a.W, kk = k - kt * a.W;
+  u32x4* out = static_cast<u32x4*>(a.out) + (((size_t)kg * a.kTiles + kt) * T * 2 + half) * a.W + kk;
 #pragma unroll
-  for (int p = 0; p < T; ++p) out[(((size_t)kg * T + p) * 2 + half) * a.K + k] = E::pack(pl[p]);
+  for (int p = 0; p < T; ++p) out[(size_t)p * 2 * a.W] = E::pack(pl[p]);
 }
 
 template <int T, typename Elt, int NB>
@@ -97,11 +99,14 @@ __global__ void __launch_bounds__(256) eql_bwdw_gemm(const BwdwArgs a) {
   // ... padded to whole loads of 4 waves x 64 lanes
   constexpr int UAP = (UA + 255) / 256 * 256, UBP = (UB + 255) / 256 * 256;
   constexpr int NS = ((UAP + UBP) * 16 * 4 <= 160 * 1024) ? 4 : (((UAP + UBP) * 16 * 3 <= 160 * 1024) ? 3 : 2);
-  constexpr int DIST = NS - 1;
   constexpr int IPWA = UAP / 256, IPWB = UBP / 256;  // DMA loads per wave per stage
-  constexpr int WAIT_TOP = (DIST - 1) * (IPWA + IPWB);
+  constexpr int IPW = IPWA + IPWB;
+  // Register double buffering of the operand fragments (next k-step read from LDS
+  // while this one's MFMAs run) when two fragment sets fit beside the address
+  // registers; otherwise one set, read after the barrier of its own k-step.
+  constexpr bool PIPE = 2 * (T + NB * T) * 4 <= 192;
   static_assert(NS * (UAP + UBP) * 16 <= 160 * 1024, "LDS budget");
-  static_assert(WAIT_TOP < 64, "vmcnt range");
+  static_assert((NS - 1) * IPW < 64, "vmcnt range");
 
   __shared__ u32x4 ringA[NS][UAP];
   __shared__ u32x4 ringB[NS][UBP];
@@ -119,48 +124,51 @@ __global__ void __launch_bounds__(256) eql_bwdw_gemm(const BwdwArgs a) {
   const int kgEnd = min(a.kgCount, kgBegin + a.kgPerSplit);
   const int nst = max(0, kgEnd - kgBegin);
 
-  // DMA source offsets within a stage block (unit P of the block is run
-  // s = P / width, element j = P % width, i.e. global unit (kg*2T + s)*K + k0 + j).
-  // Units past K read neighbouring data that only reaches output channels that are
-  // never stored; the descriptor range keeps every access inside the buffer.
+  // A stage block (one k-step of one channel tile) is contiguous in the workspace
+  // and lands in the ring in the same order: unit P of the block at slot unit P.
+  // Padding units of the last wave load (UBP > UB) re-read unit 0.
   uint32_t aOff[IPWA], bOff[IPWB];
 #pragma unroll
   for (int i = 0; i < IPWA; ++i) {
     const int P = (wave * IPWA + i) * 64 + lane;
-    const int s = P / kBwdwRowsD, j = P - s * kBwdwRowsD;
-    aOff[i] = P < UA ? ((uint32_t)s * a.Dp + (uint32_t)(d0 + j)) * 16u : 0u;  // padding: any unit
+    aOff[i] = P < UA ? (uint32_t)P * 16u : 0u;
   }
 #pragma unroll
   for (int i = 0; i < IPWB; ++i) {
     const int P = (wave * IPWB + i) * 64 + lane;
-    const int s = P / BN, j = P - s * BN;
-    bOff[i] = P < UB ? ((uint32_t)s * a.Cp + (uint32_t)(c0 + j)) * 16u : 0u;
+    bOff[i] = P < UB ? (uint32_t)P * 16u : 0u;
   }
-  const uint64_t aBase = reinterpret_cast<uint64_t>(a.dyh), bBase = reinterpret_cast<uint64_t>(a.xh);
-  const uint64_t aStage = (uint64_t)2 * T * a.Dp * 16, bStage = (uint64_t)2 * T * a.Cp * 16;
-  const uint64_t aTotal = aStage * a.kgCount, bTotal = bStage * a.kgCount;
+  const uint64_t aBase = reinterpret_cast<uint64_t>(a.dyh) + (uint64_t)dTile * UA * 16;
+  const uint64_t bBase = reinterpret_cast<uint64_t>(a.xh) + (uint64_t)cTile * UB * 16;
+  const uint64_t aStage = (uint64_t)a.dTiles * UA * 16, bStage = (uint64_t)a.cTiles * UB * 16;
 
   // Stage j of this item (k-step kgBegin + j) into ring slot j % NS.  Stages past
   // the item read nothing (empty range), so every stage issues the same loads.
-  auto issue = [&](int j) __attribute__((always_inline)) {
+  // Loads 0 .. IPWA-1 fill the A block, IPWA .. IPW-1 the B block.
+  struct StageDesc {
+    BufDesc da, db;
+    uint32_t dsta, dstb;
+  };
+  auto stage_desc = [&](int j) __attribute__((always_inline)) {
     const bool live = j < nst;
     const uint64_t kg = (uint64_t)(kgBegin + (live ? j : 0));
-    {
-      const uint64_t base = aBase + kg * aStage;
-      const uint64_t left = aTotal - kg * aStage;
-      const BufDesc d = desc_at(base, live ? (uint32_t)min(left, (uint64_t)0xFFFFFFF0u) : 0u);
-      const uint32_t dst = lds_addr(&ringA[j % NS][wave * IPWA * 64]);
+    StageDesc sd;
+    sd.da = desc_at(aBase + kg * aStage, live ? (uint32_t)(UA * 16) : 0u);
+    sd.db = desc_at(bBase + kg * bStage, live ? (uint32_t)(UB * 16) : 0u);
+    sd.dsta = lds_addr(&ringA[j % NS][wave * IPWA * 64]);
+    sd.dstb = lds_addr(&ringB[j % NS][wave * IPWB * 64]);
+    return sd;
+  };
+  auto issue_one = [&](const StageDesc& sd, int i) __attribute__((always_inline)) {
+    if (i < IPWA)
+      dma16(sd.da, aOff[i], sd.dsta + i * 1024u);
+    else
+      dma16(sd.db, bOff[i - IPWA], sd.dstb + (i - IPWA) * 1024u);
+  };
+  auto issue = [&](int j) __attribute__((always_inline)) {
+    const StageDesc sd = stage_desc(j);
 #pragma unroll
-      for (int i = 0; i < IPWA; ++i) dma16(d, aOff[i], dst + i * 1024u);
-    }
-    {
-      const uint64_t base = bBase + kg * bStage;
-      const uint64_t left = bTotal - kg * bStage;
-      const BufDesc d = desc_at(base, live ? (uint32_t)min(left, (uint64_t)0xFFFFFFF0u) : 0u);
-      const uint32_t dst = lds_addr(&ringB[j % NS][wave * IPWB * 64]);
-#pragma unroll
-      for (int i = 0; i < IPWB; ++i) dma16(d, bOff[i], dst + i * 1024u);
-    }
+    for (int i = 0; i < IPW; ++i) issue_one(sd, i);
   };
 
   f32x16 acc[T][NB];
@@ -171,40 +179,109 @@ __global__ void __launch_bounds__(256) eql_bwdw_gemm(const BwdwArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[p][nb][r] = 0.0f;
 
-  // Pipeline: stage j is loaded DIST stages ahead, at the top of stage j - DIST,
-  // into the slot of stage j - DIST - 1 (free once every wave passed that stage's
-  // barrier).  At the top of stage j, the loads issued after it are those of
-  // stages j+1 .. j+DIST-1: WAIT_TOP of them may still be outstanding.
-#pragma unroll
-  for (int j = 0; j < DIST; ++j) issue(j);
-
-  for (int j = 0; j < nst; ++j) {
-    wait_vmcnt<WAIT_TOP>();
-    __builtin_amdgcn_s_barrier();
-    issue(j + DIST);
+  // Operand fragments of one k-step: lane (lcol, khalf) holds plane p of output
+  // channel d0 + 32*wave + lcol (A) / input channel c0 + 32*nb + lcol (B) for rows
+  // khalf*G .. +G of the step.
+  struct Frags {
+    u32x4 a[T];
+    u32x4 b[NB][T];
+  };
+  auto read_frags = [&](int j, Frags& f) __attribute__((always_inline)) {
     const u32x4* sa = ringA[j % NS];
     const u32x4* sb = ringB[j % NS];
-    u32x4 af[T + NP];
 #pragma unroll
-    for (int p = 0; p < T; ++p) af[p] = sa[(p * 2 + khalf) * kBwdwRowsD + wave * 32 + lcol];
+    for (int p = 0; p < T; ++p) f.a[p] = sa[(p * 2 + khalf) * kBwdwRowsD + wave * 32 + lcol];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int p = 0; p < T; ++p) f.b[nb][p] = sb[(p * 2 + khalf) * BN + nb * 32 + lcol];
+  };
+  // MFMAs of one k-step.  With `sd` given, the IPW loads of a later stage are issued
+  // between them, one after every MFMAS / IPW MFMAs: issue is in order, so a burst
+  // of loads would hold the MFMAs back until the address unit had taken every one
+  // of them.  The scheduling barriers keep that order.
+  constexpr int MFMAS = NB * (NR + 4 * NP);
+  constexpr int EVERY = MFMAS / IPW > 0 ? MFMAS / IPW : 1;
+  auto mma = [&](const Frags& f, const StageDesc* sd) __attribute__((always_inline)) {
     // -dYr for Im G = dYi Xr + (-dYr) Xi.
+    u32x4 negr[NP > 0 ? NP : 1];
 #pragma unroll
-    for (int q = 0; q < NP; ++q) af[T + q] = neg_unit(af[NR + 2 * q], E::kSignMask);
+    for (int q = 0; q < NP; ++q) negr[q] = neg_unit(f.a[NR + 2 * q], E::kSignMask);
+    int m = 0, ld = 0;
+    auto after_mfma = [&]() __attribute__((always_inline)) {
+      ++m;
+      if (sd && m % EVERY == 0 && ld < IPW) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue_one(*sd, ld++);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      u32x4 bf[T];
 #pragma unroll
-      for (int p = 0; p < T; ++p) bf[p] = sb[(p * 2 + khalf) * BN + nb * 32 + lcol];
-#pragma unroll
-      for (int p = 0; p < NR; ++p) E::mfma(acc[p][nb], af[p], bf[p]);
+      for (int p = 0; p < NR; ++p) {
+        E::mfma(acc[p][nb], f.a[p], f.b[nb][p]);
+        after_mfma();
+      }
 #pragma unroll
       for (int q = 0; q < NP; ++q) {
         const int rp = NR + 2 * q, ip = rp + 1;
-        E::mfma(acc[rp][nb], af[rp], bf[rp]);
-        E::mfma(acc[rp][nb], af[ip], bf[ip]);
-        E::mfma(acc[ip][nb], af[ip], bf[rp]);
-        E::mfma(acc[ip][nb], af[T + q], bf[ip]);
+        E::mfma(acc[rp][nb], f.a[rp], f.b[nb][rp]);
+        after_mfma();
+        E::mfma(acc[rp][nb], f.a[ip], f.b[nb][ip]);
+        after_mfma();
+        E::mfma(acc[ip][nb], f.a[ip], f.b[nb][rp]);
+        after_mfma();
+        E::mfma(acc[ip][nb], negr[q], f.b[nb][ip]);
+        after_mfma();
       }
+    }
+    if (sd) {
+#pragma unroll
+      for (; ld < IPW; ++ld) issue_one(*sd, ld);
+    }
+  };
+
+  if constexpr (PIPE) {
+    // Slot j % NS holds stage j; it is refilled with stage j + NS at the top of
+    // k-step j, once every wave has its fragments of stage j in registers (its LDS
+    // reads returned: lgkmcnt(0) before the barrier).  At that point the loads
+    // issued after stage j+1 are those of stages j+2 .. j+NS-1.
+#pragma unroll
+    for (int j = 0; j < NS; ++j) issue(j);
+    wait_vmcnt<(NS - 1) * IPW>();
+    __builtin_amdgcn_s_barrier();
+    Frags f0, f1;
+    read_frags(0, f0);
+    auto step = [&](int j, const Frags& cur, Frags& nxt) __attribute__((always_inline)) {
+      wait_vmcnt<(NS - 2) * IPW>();
+      wait_lgkm0();
+      __builtin_amdgcn_s_barrier();
+      const StageDesc sd = stage_desc(j + NS);
+      read_frags(j + 1, nxt);
+      mma(cur, &sd);
+    };
+    int j = 0;
+    for (; j + 1 < nst; j += 2) {
+      step(j, f0, f1);
+      step(j + 1, f1, f0);
+    }
+    if (j < nst) step(j, f0, f1);
+  } else {
+    // Stage j is loaded NS-1 stages ahead, at the top of stage j-NS+1, into the
+    // slot of stage j-NS (free once every wave passed that stage's barrier).  At
+    // the top of stage j the loads issued after it are those of stages
+    // j+1 .. j+NS-2.
+    constexpr int DIST = NS - 1;
+#pragma unroll
+    for (int j = 0; j < DIST; ++j) issue(j);
+    for (int j = 0; j < nst; ++j) {
+      wait_vmcnt<(DIST - 1) * IPW>();
+      __builtin_amdgcn_s_barrier();
+      issue(j + DIST);
+      Frags f;
+      read_frags(j, f);
+      mma(f, nullptr);
     }
   }
   wait_vmcnt<0>();  // drain the look-ahead loads before the LDS is reused

@@ -127,7 +127,8 @@ int eqlinear_bwd_x(const void* dy, const void* w_packed_bwdx, void* dx, int64_t 
  * Scratch bytes eqlinear_bwd_w needs for this shape.  Depends only on the
  * arguments (0 when N == 0 or the arguments are invalid).  The workspace holds the
  * half spectra of dy and x (each about the size of that tensor: T real planes per
- * channel, rows padded to a multiple of 2 * 16 / sizeof(element)) followed by S
+ * channel, rows padded to a multiple of 2 * 16 / sizeof(element), channels to
+ * whole GEMM tiles of 32 to 128) followed by S
  * fp32 partial spectra of the gradient, S * T * Dp * Cp * 4 bytes, one per row
  * range of the reduction over N.
  */
