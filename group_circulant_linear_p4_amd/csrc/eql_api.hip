@@ -122,38 +122,53 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 // Weight-gradient plan.  The workspace holds, in order (each section 256-byte
 // aligned): the half spectra of dy and of x as MFMA operand units (2G rows per
-// k-step, zero rows past N, channels padded to whole GEMM tiles), then S fp32
-// partial spectra [S][T][Dp][Cp].
+// k-step, zero rows past N, channels padded to a multiple of 256), then the fp32
+// partial spectra of the real-plane GEMM [SR][NR][Dp][Cp] and of the complex-pair
+// GEMM [SP][T-NR][Dp][Cp].
+struct GemmPlan {
+  int64_t groups = 0, dTiles = 0, cTiles = 0, S = 0, kgPerSplit = 0;
+  int64_t items() const { return S * groups * dTiles * cTiles; }
+};
+
 struct BwdwPlan {
-  int64_t kgCount = 0, S = 0, kgPerSplit = 0, dTiles = 0, cTiles = 0;
-  int nb = 1;
-  size_t dyhBytes = 0, xhBytes = 0, partBytes = 0;
-  size_t total() const { return dyhBytes + xhBytes + partBytes; }
+  int64_t kgCount = 0, Dpad = 0, Cpad = 0;
+  GemmPlan real, pair;
+  size_t dyhBytes = 0, xhBytes = 0, partRBytes = 0, partPBytes = 0;
+  size_t total() const { return dyhBytes + xhBytes + partRBytes + partPBytes; }
 };
 
 constexpr int64_t kMinStepsPerSplit = 16;  // keeps partial-spectrum traffic small
 
+// Row ranges (k-step ranges) of one GEMM launch: enough to give every compute unit
+// one item.
+void plan_splits(GemmPlan& g, int64_t kgCount) {
+  const int64_t tiles = g.groups * g.dTiles * g.cTiles;
+  if (tiles == 0 || kgCount == 0) return;
+  int64_t S = tiles >= kTargetWorkgroups ? 1 : kTargetWorkgroups / tiles;
+  S = std::min<int64_t>(S, std::max<int64_t>(1, kgCount / kMinStepsPerSplit));
+  g.kgPerSplit = ceil_div(kgCount, S);
+  g.S = ceil_div(kgCount, g.kgPerSplit);
+}
+
 BwdwPlan plan_bwdw(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype) {
   BwdwPlan p;
-  // Column tile: the widest one unless a half-width tile pads C' less.
-  p.nb = bwdw_nb_max(T);
-  if (p.nb > 1) {
-    const int half = p.nb / 2;
-    if (ceil_div(Cp, 32 * half) * half < ceil_div(Cp, 32 * p.nb) * p.nb) p.nb = half;
-  }
-  p.dTiles = ceil_div(Dp, kBwdwRowsD);
-  p.cTiles = ceil_div(Cp, 32 * p.nb);
+  const int nr = n_real_planes(T), np = n_pairs(T);
+  p.Dpad = ceil_div(Dp, kBwdwPad) * kBwdwPad;
+  p.Cpad = ceil_div(Cp, kBwdwPad) * kBwdwPad;
+  p.real.groups = nr;
+  p.real.dTiles = p.Dpad / kBwdwTileD;
+  p.real.cTiles = p.Cpad / 256;
+  p.pair.groups = np;
+  p.pair.dTiles = p.Dpad / kBwdwTileD;
+  p.pair.cTiles = p.Cpad / 128;
   if (N == 0) return p;
   p.kgCount = ceil_div(N, 2 * group_channels(dtype));
-  // Row ranges (k-step ranges): enough to give every compute unit one item.
-  const int64_t tiles = p.dTiles * p.cTiles;
-  int64_t S = tiles >= kTargetWorkgroups ? 1 : kTargetWorkgroups / tiles;
-  S = std::min<int64_t>(S, std::max<int64_t>(1, p.kgCount / kMinStepsPerSplit));
-  p.kgPerSplit = ceil_div(p.kgCount, S);
-  p.S = ceil_div(p.kgCount, p.kgPerSplit);
-  p.dyhBytes = align256((size_t)p.kgCount * p.dTiles * kBwdwRowsD * T * 2 * 16);
-  p.xhBytes = align256((size_t)p.kgCount * p.cTiles * (32 * p.nb) * T * 2 * 16);
-  p.partBytes = (size_t)p.S * T * (size_t)Dp * (size_t)Cp * sizeof(float);
+  plan_splits(p.real, p.kgCount);
+  plan_splits(p.pair, p.kgCount);
+  p.dyhBytes = align256((size_t)p.kgCount * T * 2 * (size_t)p.Dpad * 16);
+  p.xhBytes = align256((size_t)p.kgCount * T * 2 * (size_t)p.Cpad * 16);
+  p.partRBytes = align256((size_t)p.real.S * nr * (size_t)Dp * (size_t)Cp * sizeof(float));
+  p.partPBytes = (size_t)p.pair.S * (T - nr) * (size_t)Dp * (size_t)Cp * sizeof(float);
   return p;
 }
 
@@ -232,18 +247,20 @@ int eqlinear_bwd_w(const void* x, const void* dy, void* dw, void* workspace, siz
   if (ws_bytes < p.total()) return EQL_EINVAL;
   if (!aligned16(dw) || (N > 0 && (!aligned16(x) || !aligned16(dy) || !aligned16(workspace))))
     return EQL_EALIGN;
-  const int64_t items = p.S * p.dTiles * p.cTiles;
-  const int64_t gdy = ceil_div(p.kgCount * 2 * p.dTiles * kBwdwRowsD, 256);
-  const int64_t gx = ceil_div(p.kgCount * 2 * p.cTiles * 32 * p.nb, 256);
+  const int64_t gdy = ceil_div(p.kgCount * 2 * p.Dpad, 256);
+  const int64_t gx = ceil_div(p.kgCount * 2 * p.Cpad, 256);
   const int64_t rgrid = ceil_div(Dp * Cp, 256);
-  if (items > kMaxGrid || gdy > kMaxGrid || gx > kMaxGrid || rgrid > kMaxGrid) return EQL_EINVAL;
+  if (p.real.items() > kMaxGrid || p.pair.items() > kMaxGrid || gdy > kMaxGrid || gx > kMaxGrid ||
+      rgrid > kMaxGrid)
+    return EQL_EINVAL;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const Twiddles tw = make_twiddles(T);
   char* ws = static_cast<char*>(workspace);
-  float* part = reinterpret_cast<float*>(ws + p.dyhBytes + p.xhBytes);
+  float* partR = reinterpret_cast<float*>(ws + p.dyhBytes + p.xhBytes);
+  float* partP = reinterpret_cast<float*>(ws + p.dyhBytes + p.xhBytes + p.partRBytes);
   const bool f16 = dtype == EQL_F16;
-  if (p.S > 0) {
+  if (N > 0) {
     SpecArgs sp{};
     sp.N = (int)N;
     sp.kgCount = (int)p.kgCount;
@@ -251,36 +268,44 @@ int eqlinear_bwd_w(const void* x, const void* dy, void* dw, void* workspace, siz
     sp.m = dy;
     sp.out = ws;
     sp.K = (int)Dp;
-    sp.W = kBwdwRowsD;
-    sp.kTiles = (int)p.dTiles;
+    sp.Kpad = (int)p.Dpad;
     hipError_t e = f16 ? launch_spec_f16(T, sp, (unsigned)gdy, s) : launch_spec_f32(T, sp, (unsigned)gdy, s);
     if (e != hipSuccess) return EQL_EHIP;
     sp.m = x;
     sp.out = ws + p.dyhBytes;
     sp.K = (int)Cp;
-    sp.W = 32 * p.nb;
-    sp.kTiles = (int)p.cTiles;
+    sp.Kpad = (int)p.Cpad;
     e = f16 ? launch_spec_f16(T, sp, (unsigned)gx, s) : launch_spec_f32(T, sp, (unsigned)gx, s);
     if (e != hipSuccess) return EQL_EHIP;
 
-    BwdwArgs a{};
-    a.dyh = ws;
-    a.xh = ws + p.dyhBytes;
-    a.ws = part;
-    a.Dp = (int)Dp;
-    a.Cp = (int)Cp;
-    a.kgCount = (int)p.kgCount;
-    a.kgPerSplit = (int)p.kgPerSplit;
-    a.dTiles = (int)p.dTiles;
-    a.cTiles = (int)p.cTiles;
-    a.numItems = (int)items;
-    e = f16 ? launch_bwdw_f16(T, p.nb, a, (unsigned)items, s) : launch_bwdw_f32(T, p.nb, a, (unsigned)items, s);
-    if (e != hipSuccess) return EQL_EHIP;
+    for (int pair = 0; pair < 2; ++pair) {
+      const GemmPlan& g = pair ? p.pair : p.real;
+      if (g.items() == 0) continue;
+      BwdwArgs a{};
+      a.dyh = ws;
+      a.xh = ws + p.dyhBytes;
+      a.ws = pair ? partP : partR;
+      a.Dp = (int)Dp;
+      a.Cp = (int)Cp;
+      a.Dpad = (int)p.Dpad;
+      a.Cpad = (int)p.Cpad;
+      a.kgCount = (int)p.kgCount;
+      a.kgPerSplit = (int)g.kgPerSplit;
+      a.groups = (int)g.groups;
+      a.dTiles = (int)g.dTiles;
+      a.cTiles = (int)g.cTiles;
+      a.numItems = (int)g.items();
+      e = f16 ? launch_bwdw_f16(T, pair != 0, a, (unsigned)a.numItems, s)
+              : launch_bwdw_f32(T, pair != 0, a, (unsigned)a.numItems, s);
+      if (e != hipSuccess) return EQL_EHIP;
+    }
   }
   BwdwReduceArgs r{};
-  r.ws = part;
+  r.wsR = partR;
+  r.wsP = partP;
   r.dw = dw;
-  r.S = (int)p.S;
+  r.SR = (int)p.real.S;
+  r.SP = (int)p.pair.S;
   r.Dp = (int)Dp;
   r.Cp = (int)Cp;
   r.tw = tw;

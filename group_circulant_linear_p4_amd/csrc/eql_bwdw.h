@@ -12,14 +12,17 @@
 //      to the element type and stored in the workspace as MFMA operand units: unit
 //      (kg, p, half, k) holds plane p of channel k for the G rows
 //      kg*2G + half*G .. +G (G = 16 / sizeof(element); rows past N and channels
-//      past the padded width are zero).  Channels are cut into tiles of the GEMM's
-//      tile width W, layout [kg][k / W][p][half][k % W], so the units one k-step of
-//      one channel tile needs are one contiguous block.  Purely bandwidth bound.
-//   2. eql_bwdw_gemm: the per-plane GEMMs.  A workgroup owns 128 output channels d
-//      (4 waves x 32) by BN = 32*NB input channels c for one range of k-steps;
-//      both operands stream into NS-deep LDS rings by buffer->LDS loads, so the
-//      loop body is LDS reads and MFMAs only.  It writes one fp32 partial spectrum
-//      per row range into the workspace.
+//      past the channel count are zero).  Layout [kg][p][half][Kpad] with the channel
+//      axis padded to a multiple of 256, so a tile's units of one k-step are 2 or 4
+//      contiguous runs.  Purely bandwidth bound.
+//   2. eql_bwdw_gemm<T, Elt, PAIR>: the per-frequency GEMMs, one plane group per
+//      workgroup so that its output tile can be as large as the register file
+//      allows: a real plane takes a 256 (d) x 256 (c) tile, a complex pair a 256 x
+//      128 tile of both planes (4 waves in a 2 x 2 arrangement, 256 accumulator
+//      registers per lane either way).  Per MFMA that moves about 0.56-0.75x the
+//      operand bytes of a tile holding all T planes.  Both operands stream into
+//      NS-deep LDS rings by buffer->LDS loads; the loop body is LDS reads and MFMAs.
+//      Each item writes the fp32 partial spectrum of one row range.
 //   3. eql_bwdw_reduce: sums the partials in a fixed order (deterministic), applies
 //      the inverse group transform and rounds to the element type.
 #pragma once
@@ -31,38 +34,41 @@
 
 namespace eql {
 
+constexpr int kBwdwTileD = 256;  // output channels d per workgroup
+constexpr int kBwdwPad = 256;    // channel padding of the spectra
+
 struct SpecArgs {
   const void* m;    // [N][K*T]
-  void* out;        // units [kgCount][kTiles][T][2][W]
-  int N, K, kgCount, W, kTiles;
+  void* out;        // units [kgCount][T][2][Kpad]
+  int N, K, Kpad, kgCount;
   Twiddles tw;
 };
 
+// One launch covers either every real plane (PAIR = false: planes 0 .. NR-1) or
+// every complex pair (PAIR = true: planes NR .. T-1).
 struct BwdwArgs {
-  const void* dyh;  // dY units [kgCount][dTiles][T][2][128]
-  const void* xh;   // X units  [kgCount][cTiles][T][2][32 NB]
-  float* ws;        // [S][T][Dp][Cp] fp32 partial spectra
-  int Dp, Cp, kgCount, kgPerSplit, dTiles, cTiles, numItems;
+  const void* dyh;  // dY units [kgCount][T][2][Dpad]
+  const void* xh;   // X units  [kgCount][T][2][Cpad]
+  float* ws;        // partials [S][planes of this launch][Dp][Cp]
+  int Dp, Cp, Dpad, Cpad, kgCount, kgPerSplit, groups, dTiles, cTiles, numItems;
 };
 
 struct BwdwReduceArgs {
-  const float* ws;  // [S][T][Dp][Cp]
-  void* dw;         // [Dp][Cp][T]
-  int S, Dp, Cp;
+  const float* wsR;  // [SR][NR][Dp][Cp]
+  const float* wsP;  // [SP][2 NP][Dp][Cp]
+  void* dw;          // [Dp][Cp][T]
+  int SR, SP, Dp, Cp;
   Twiddles tw;
 };
-
-constexpr int kBwdwRowsD = 128;  // output channels d per workgroup (4 waves x 32)
 
 template <int T, typename Elt>
 __global__ void __launch_bounds__(256) eql_spec_kernel(const SpecArgs a) {
   using E = EltT<Elt>;
   constexpr int G = E::kPerUnit;
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-  const size_t width = (size_t)a.kTiles * a.W;  // padded channel count
-  if (idx >= (size_t)a.kgCount * 2 * width) return;
-  const int k = (int)(idx % width);
-  const size_t rest = idx / width;
+  if (idx >= (size_t)a.kgCount * 2 * a.Kpad) return;
+  const int k = (int)(idx % a.Kpad);
+  const size_t rest = idx / a.Kpad;
   const int half = (int)(rest & 1);
   const int kg = (int)(rest >> 1);
   const int row0 = kg * 2 * G + half * G;
@@ -81,66 +87,69 @@ __global__ void __launch_bounds__(256) eql_spec_kernel(const SpecArgs a) {
 #pragma unroll
     for (int p = 0; p < T; ++p) pl[p][e] = o[p];
   }
-  const int kt = k / a.W, kk = k - kt * a.W;
-  u32x4* out = static_cast<u32x4*>(a.out) + (((size_t)kg * a.kTiles + kt) * T * 2 + half) * a.W + kk;
+  u32x4* out = static_cast<u32x4*>(a.out) + ((size_t)kg * T * 2 + half) * a.Kpad + k;
 #pragma unroll
-  for (int p = 0; p < T; ++p) out[(size_t)p * 2 * a.W] = E::pack(pl[p]);
+  for (int p = 0; p < T; ++p) out[(size_t)p * 2 * a.Kpad] = E::pack(pl[p]);
 }
 
-template <int T, typename Elt, int NB>
+template <int T, typename Elt, bool PAIR>
 __global__ void __launch_bounds__(256) eql_bwdw_gemm(const BwdwArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using E = EltT<Elt>;
   constexpr int NR = n_real_planes(T);
-  constexpr int NP = n_pairs(T);
-  constexpr int BN = 32 * NB;
-  constexpr int UA = 2 * T * kBwdwRowsD;   // A units per stage (one k-step)
-  constexpr int UB = 2 * T * BN;           // B units per stage
-  // ... padded to whole loads of 4 waves x 64 lanes
-  constexpr int UAP = (UA + 255) / 256 * 256, UBP = (UB + 255) / 256 * 256;
-  constexpr int NS = ((UAP + UBP) * 16 * 4 <= 160 * 1024) ? 4 : (((UAP + UBP) * 16 * 3 <= 160 * 1024) ? 3 : 2);
-  constexpr int IPWA = UAP / 256, IPWB = UBP / 256;  // DMA loads per wave per stage
+  constexpr int NPL = PAIR ? 2 : 1;          // planes per item
+  constexpr int WC = PAIR ? 128 : 256;       // input channels c per workgroup
+  constexpr int DB = 4;                      // 32-row blocks per wave (128 d)
+  constexpr int CB = WC / 64;                // 32-column blocks per wave (WC / 2 c)
+  constexpr int UA = NPL * 2 * kBwdwTileD;   // A units per stage (one k-step)
+  constexpr int UB = NPL * 2 * WC;           // B units per stage
+  constexpr int NS = 4;
+  constexpr int IPWA = UA / 256, IPWB = UB / 256;  // DMA loads per wave per stage
   constexpr int IPW = IPWA + IPWB;
-  // Register double buffering of the operand fragments (next k-step read from LDS
-  // while this one's MFMAs run) when two fragment sets fit beside the address
-  // registers; otherwise one set, read after the barrier of its own k-step.
-  constexpr bool PIPE = 2 * (T + NB * T) * 4 <= 192;
-  static_assert(NS * (UAP + UBP) * 16 <= 160 * 1024, "LDS budget");
+  static_assert(UA % 256 == 0 && UB % 256 == 0, "whole wave loads");
+  static_assert(NS * (UA + UB) * 16 <= 160 * 1024, "LDS budget");
   static_assert((NS - 1) * IPW < 64, "vmcnt range");
 
-  __shared__ u32x4 ringA[NS][UAP];
-  __shared__ u32x4 ringB[NS][UBP];
+  __shared__ u32x4 ringA[NS][UA];
+  __shared__ u32x4 ringB[NS][UB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wd = wave >> 1, wc = wave & 1;  // 2 x 2 waves
   const int lcol = lane & 31, khalf = lane >> 5;
   const int item = xcd_remap(blockIdx.x, a.numItems);
-  const int per = a.dTiles * a.cTiles;
+  const int per = a.groups * a.dTiles * a.cTiles;
   const int split = item / per;
-  const int rest = item - split * per;
+  int rest = item - split * per;
+  const int grp = rest / (a.dTiles * a.cTiles);
+  rest -= grp * (a.dTiles * a.cTiles);
   const int dTile = rest / a.cTiles, cTile = rest - dTile * a.cTiles;
-  const int d0 = dTile * kBwdwRowsD, c0 = cTile * BN;
+  const int d0 = dTile * kBwdwTileD, c0 = cTile * WC;
+  const int p0 = PAIR ? NR + 2 * grp : grp;  // first plane of the item
   const int kgBegin = split * a.kgPerSplit;
   const int kgEnd = min(a.kgCount, kgBegin + a.kgPerSplit);
   const int nst = max(0, kgEnd - kgBegin);
 
-  // A stage block (one k-step of one channel tile) is contiguous in the workspace
-  // and lands in the ring in the same order: unit P of the block at slot unit P.
-  // Padding units of the last wave load (UBP > UB) re-read unit 0.
+  // A stage is run s = plane*2 + half of the item's planes: A units d0 .. d0+255
+  // of that run, B units c0 .. c0+WC-1; unit P of the stage lands at ring unit P.
   uint32_t aOff[IPWA], bOff[IPWB];
 #pragma unroll
   for (int i = 0; i < IPWA; ++i) {
     const int P = (wave * IPWA + i) * 64 + lane;
-    aOff[i] = P < UA ? (uint32_t)P * 16u : 0u;
+    const int s = P / kBwdwTileD, j = P - s * kBwdwTileD;
+    aOff[i] = ((uint32_t)s * a.Dpad + (uint32_t)(d0 + j)) * 16u;
   }
 #pragma unroll
   for (int i = 0; i < IPWB; ++i) {
     const int P = (wave * IPWB + i) * 64 + lane;
-    bOff[i] = P < UB ? (uint32_t)P * 16u : 0u;
+    const int s = P / WC, j = P - s * WC;
+    bOff[i] = ((uint32_t)s * a.Cpad + (uint32_t)(c0 + j)) * 16u;
   }
-  const uint64_t aBase = reinterpret_cast<uint64_t>(a.dyh) + (uint64_t)dTile * UA * 16;
-  const uint64_t bBase = reinterpret_cast<uint64_t>(a.xh) + (uint64_t)cTile * UB * 16;
-  const uint64_t aStage = (uint64_t)a.dTiles * UA * 16, bStage = (uint64_t)a.cTiles * UB * 16;
+  // Byte offset of k-step kg's first run, and the bytes the item's runs span.
+  const uint64_t aBase = reinterpret_cast<uint64_t>(a.dyh), bBase = reinterpret_cast<uint64_t>(a.xh);
+  const uint64_t aStep = (uint64_t)T * 2 * a.Dpad * 16, bStep = (uint64_t)T * 2 * a.Cpad * 16;
+  const uint64_t aPlane = (uint64_t)p0 * 2 * a.Dpad * 16, bPlane = (uint64_t)p0 * 2 * a.Cpad * 16;
+  const uint32_t aSpan = (uint32_t)NPL * 2 * a.Dpad * 16, bSpan = (uint32_t)NPL * 2 * a.Cpad * 16;
 
   // Stage j of this item (k-step kgBegin + j) into ring slot j % NS.  Stages past
   // the item read nothing (empty range), so every stage issues the same loads.
@@ -153,8 +162,8 @@ __global__ void __launch_bounds__(256) eql_bwdw_gemm(const BwdwArgs a) {
     const bool live = j < nst;
     const uint64_t kg = (uint64_t)(kgBegin + (live ? j : 0));
     StageDesc sd;
-    sd.da = desc_at(aBase + kg * aStage, live ? (uint32_t)(UA * 16) : 0u);
-    sd.db = desc_at(bBase + kg * bStage, live ? (uint32_t)(UB * 16) : 0u);
+    sd.da = desc_at(aBase + kg * aStep + aPlane, live ? aSpan : 0u);
+    sd.db = desc_at(bBase + kg * bStep + bPlane, live ? bSpan : 0u);
     sd.dsta = lds_addr(&ringA[j % NS][wave * IPWA * 64]);
     sd.dstb = lds_addr(&ringB[j % NS][wave * IPWB * 64]);
     return sd;
@@ -165,141 +174,125 @@ __global__ void __launch_bounds__(256) eql_bwdw_gemm(const BwdwArgs a) {
     else
       dma16(sd.db, bOff[i - IPWA], sd.dstb + (i - IPWA) * 1024u);
   };
-  auto issue = [&](int j) __attribute__((always_inline)) {
-    const StageDesc sd = stage_desc(j);
-#pragma unroll
-    for (int i = 0; i < IPW; ++i) issue_one(sd, i);
-  };
 
-  f32x16 acc[T][NB];
+  f32x16 acc[NPL][DB][CB];
 #pragma unroll
-  for (int p = 0; p < T; ++p)
+  for (int q = 0; q < NPL; ++q)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+    for (int i = 0; i < DB; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[p][nb][r] = 0.0f;
+      for (int jc = 0; jc < CB; ++jc)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[q][i][jc][r] = 0.0f;
 
-  // Operand fragments of one k-step: lane (lcol, khalf) holds plane p of output
-  // channel d0 + 32*wave + lcol (A) / input channel c0 + 32*nb + lcol (B) for rows
-  // khalf*G .. +G of the step.
+  // Operand fragments of one k-step: lane (lcol, khalf) holds plane q of output
+  // channel d0 + 128*wd + 32*i + lcol (A) / input channel c0 + (WC/2)*wc + 32*jc +
+  // lcol (B) for rows khalf*G .. +G of the step.
   struct Frags {
-    u32x4 a[T];
-    u32x4 b[NB][T];
+    u32x4 a[NPL][DB];
+    u32x4 b[NPL][CB];
   };
   auto read_frags = [&](int j, Frags& f) __attribute__((always_inline)) {
     const u32x4* sa = ringA[j % NS];
     const u32x4* sb = ringB[j % NS];
 #pragma unroll
-    for (int p = 0; p < T; ++p) f.a[p] = sa[(p * 2 + khalf) * kBwdwRowsD + wave * 32 + lcol];
+    for (int q = 0; q < NPL; ++q) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+      for (int i = 0; i < DB; ++i) f.a[q][i] = sa[(q * 2 + khalf) * kBwdwTileD + wd * 128 + i * 32 + lcol];
 #pragma unroll
-      for (int p = 0; p < T; ++p) f.b[nb][p] = sb[(p * 2 + khalf) * BN + nb * 32 + lcol];
+      for (int jc = 0; jc < CB; ++jc) f.b[q][jc] = sb[(q * 2 + khalf) * WC + wc * (WC / 2) + jc * 32 + lcol];
+    }
   };
-  // MFMAs of one k-step.  With `sd` given, the IPW loads of a later stage are issued
-  // between them, one after every MFMAS / IPW MFMAs: issue is in order, so a burst
-  // of loads would hold the MFMAs back until the address unit had taken every one
-  // of them.  The scheduling barriers keep that order.
-  constexpr int MFMAS = NB * (NR + 4 * NP);
+
+  // MFMAs of one k-step, with the IPW loads of a later stage issued between them,
+  // one after every MFMAS / IPW MFMAs (issue is in order: a burst of loads would
+  // hold the MFMAs back until the address unit had taken every one of them).
+  constexpr int MFMAS = DB * CB * (PAIR ? 4 : 1);
   constexpr int EVERY = MFMAS / IPW > 0 ? MFMAS / IPW : 1;
-  auto mma = [&](const Frags& f, const StageDesc* sd) __attribute__((always_inline)) {
-    // -dYr for Im G = dYi Xr + (-dYr) Xi.
-    u32x4 negr[NP > 0 ? NP : 1];
-#pragma unroll
-    for (int q = 0; q < NP; ++q) negr[q] = neg_unit(f.a[NR + 2 * q], E::kSignMask);
+  auto mma = [&](const Frags& f, const StageDesc& sd) __attribute__((always_inline)) {
     int m = 0, ld = 0;
     auto after_mfma = [&]() __attribute__((always_inline)) {
       ++m;
-      if (sd && m % EVERY == 0 && ld < IPW) {
+      if (m % EVERY == 0 && ld < IPW) {
         __builtin_amdgcn_sched_barrier(0);
-        issue_one(*sd, ld++);
+        issue_one(sd, ld++);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
+    for (int i = 0; i < DB; ++i) {
+      u32x4 negr;
+      if constexpr (PAIR) negr = neg_unit(f.a[0][i], E::kSignMask);  // -dYr
 #pragma unroll
-      for (int p = 0; p < NR; ++p) {
-        E::mfma(acc[p][nb], f.a[p], f.b[nb][p]);
-        after_mfma();
-      }
-#pragma unroll
-      for (int q = 0; q < NP; ++q) {
-        const int rp = NR + 2 * q, ip = rp + 1;
-        E::mfma(acc[rp][nb], f.a[rp], f.b[nb][rp]);
-        after_mfma();
-        E::mfma(acc[rp][nb], f.a[ip], f.b[nb][ip]);
-        after_mfma();
-        E::mfma(acc[ip][nb], f.a[ip], f.b[nb][rp]);
-        after_mfma();
-        E::mfma(acc[ip][nb], negr[q], f.b[nb][ip]);
-        after_mfma();
+      for (int jc = 0; jc < CB; ++jc) {
+        if constexpr (PAIR) {
+          E::mfma(acc[0][i][jc], f.a[0][i], f.b[0][jc]);  // Re += dYr Xr
+          after_mfma();
+          E::mfma(acc[0][i][jc], f.a[1][i], f.b[1][jc]);  //    + dYi Xi
+          after_mfma();
+          E::mfma(acc[1][i][jc], f.a[1][i], f.b[0][jc]);  // Im += dYi Xr
+          after_mfma();
+          E::mfma(acc[1][i][jc], negr, f.b[1][jc]);       //    - dYr Xi
+          after_mfma();
+        } else {
+          E::mfma(acc[0][i][jc], f.a[0][i], f.b[0][jc]);
+          after_mfma();
+        }
       }
     }
-    if (sd) {
 #pragma unroll
-      for (; ld < IPW; ++ld) issue_one(*sd, ld);
-    }
+    for (; ld < IPW; ++ld) issue_one(sd, ld);
   };
 
-  if constexpr (PIPE) {
-    // Slot j % NS holds stage j; it is refilled with stage j + NS at the top of
-    // k-step j, once every wave has its fragments of stage j in registers (its LDS
-    // reads returned: lgkmcnt(0) before the barrier).  At that point the loads
-    // issued after stage j+1 are those of stages j+2 .. j+NS-1.
+  // Slot j % NS holds stage j; it is refilled with stage j + NS at the top of
+  // k-step j, once every wave has its fragments of stage j in registers (its LDS
+  // reads returned: lgkmcnt(0) before the barrier).  At that point the loads
+  // issued after stage j+1 are those of stages j+2 .. j+NS-1.
 #pragma unroll
-    for (int j = 0; j < NS; ++j) issue(j);
-    wait_vmcnt<(NS - 1) * IPW>();
-    __builtin_amdgcn_s_barrier();
-    Frags f0, f1;
-    read_frags(0, f0);
-    auto step = [&](int j, const Frags& cur, Frags& nxt) __attribute__((always_inline)) {
-      wait_vmcnt<(NS - 2) * IPW>();
-      wait_lgkm0();
-      __builtin_amdgcn_s_barrier();
-      const StageDesc sd = stage_desc(j + NS);
-      read_frags(j + 1, nxt);
-      mma(cur, &sd);
-    };
-    int j = 0;
-    for (; j + 1 < nst; j += 2) {
-      step(j, f0, f1);
-      step(j + 1, f1, f0);
-    }
-    if (j < nst) step(j, f0, f1);
-  } else {
-    // Stage j is loaded NS-1 stages ahead, at the top of stage j-NS+1, into the
-    // slot of stage j-NS (free once every wave passed that stage's barrier).  At
-    // the top of stage j the loads issued after it are those of stages
-    // j+1 .. j+NS-2.
-    constexpr int DIST = NS - 1;
+  for (int j = 0; j < NS; ++j) {
+    const StageDesc sd = stage_desc(j);
 #pragma unroll
-    for (int j = 0; j < DIST; ++j) issue(j);
-    for (int j = 0; j < nst; ++j) {
-      wait_vmcnt<(DIST - 1) * IPW>();
-      __builtin_amdgcn_s_barrier();
-      issue(j + DIST);
-      Frags f;
-      read_frags(j, f);
-      mma(f, nullptr);
-    }
+    for (int i = 0; i < IPW; ++i) issue_one(sd, i);
   }
+  wait_vmcnt<(NS - 1) * IPW>();
+  __builtin_amdgcn_s_barrier();
+  Frags f0, f1;
+  read_frags(0, f0);
+  auto step = [&](int j, const Frags& cur, Frags& nxt) __attribute__((always_inline)) {
+    wait_vmcnt<(NS - 2) * IPW>();
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    const StageDesc sd = stage_desc(j + NS);
+    read_frags(j + 1, nxt);
+    mma(cur, sd);
+  };
+  int j = 0;
+  for (; j + 1 < nst; j += 2) {
+    step(j, f0, f1);
+    step(j + 1, f1, f0);
+  }
+  if (j < nst) step(j, f0, f1);
   wait_vmcnt<0>();  // drain the look-ahead loads before the LDS is reused
 
-  // Partial spectrum of this row range: slot r of lane l is output channel
-  // d = 8*(r/4) + 4*(l/32) + r%4 (MFMA rows) and input channel c = l%32.
+  // Partial spectrum of this row range: slot r of lane l in block (i, jc) is output
+  // channel d = 8*(r/4) + 4*(l/32) + r%4 (MFMA rows) and input channel c = l%32 of
+  // the block.
+  const int planes = PAIR ? 2 * n_pairs(T) : NR;
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int c = c0 + nb * 32 + lcol;
+  for (int q = 0; q < NPL; ++q) {
+    const int pidx = PAIR ? 2 * grp + q : grp;
+    float* out = a.ws + ((size_t)split * planes + pidx) * a.Dp * a.Cp;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int d = d0 + wave * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
-      if (d < a.Dp && c < a.Cp) {
+    for (int i = 0; i < DB; ++i)
 #pragma unroll
-        for (int p = 0; p < T; ++p)
-          a.ws[(((size_t)split * T + p) * a.Dp + d) * a.Cp + c] = acc[p][nb][r];
+      for (int jc = 0; jc < CB; ++jc) {
+        const int c = c0 + wc * (WC / 2) + jc * 32 + lcol;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int d = d0 + wd * 128 + i * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+          if (d < a.Dp && c < a.Cp) out[(size_t)d * a.Cp + c] = acc[q][i][jc][r];
+        }
       }
-    }
   }
 #endif  // __HIP_DEVICE_COMPILE__
 }
@@ -309,15 +302,23 @@ __global__ void __launch_bounds__(256) eql_bwdw_gemm(const BwdwArgs a) {
 //   dw[t] = (1/T) (G0 + (-1)^t G_{T/2} + 2 sum_k (cos Re G_k - sin Im G_k)).
 template <int T, typename Elt>
 __global__ void __launch_bounds__(256) eql_bwdw_reduce(const BwdwReduceArgs a) {
+  constexpr int NR = n_real_planes(T);
+  constexpr int NC = T - NR;  // planes of the complex pairs
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   const size_t plane = (size_t)a.Dp * a.Cp;
   if (idx >= plane) return;
   float P[T];
 #pragma unroll
   for (int p = 0; p < T; ++p) P[p] = 0.0f;
-  for (int s = 0; s < a.S; ++s) {
+  for (int s = 0; s < a.SR; ++s) {
 #pragma unroll
-    for (int p = 0; p < T; ++p) P[p] += a.ws[((size_t)s * T + p) * plane + idx];
+    for (int p = 0; p < NR; ++p) P[p] += a.wsR[((size_t)s * NR + p) * plane + idx];
+  }
+  if constexpr (NC > 0) {
+    for (int s = 0; s < a.SP; ++s) {
+#pragma unroll
+      for (int p = 0; p < NC; ++p) P[NR + p] += a.wsP[((size_t)s * NC + p) * plane + idx];
+    }
   }
   float g[T];
   Idft<T, true>::run(P, g, a.tw);

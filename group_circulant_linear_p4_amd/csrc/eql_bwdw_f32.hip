@@ -9,12 +9,9 @@ static hipError_t spec_one(const SpecArgs& a, unsigned grid, hipStream_t s) {
 }
 
 template <int T>
-static hipError_t bwdw_one(int NB, const BwdwArgs& a, unsigned grid, hipStream_t s) {
-  constexpr int NBM = bwdw_nb_max(T);
-  if (NB == NBM) return launch_kernel((const void*)&eql_bwdw_gemm<T, float, NBM>, grid, a, s);
-  if constexpr (NBM > 1) {
-    if (NB == NBM / 2) return launch_kernel((const void*)&eql_bwdw_gemm<T, float, NBM / 2>, grid, a, s);
-  }
+static hipError_t bwdw_one(bool pair, const BwdwArgs& a, unsigned grid, hipStream_t s) {
+  if (!pair) return launch_kernel((const void*)&eql_bwdw_gemm<T, float, false>, grid, a, s);
+  if constexpr (n_pairs(T) > 0) return launch_kernel((const void*)&eql_bwdw_gemm<T, float, true>, grid, a, s);
   return hipErrorInvalidValue;
 }
 
@@ -29,8 +26,8 @@ hipError_t launch_spec_f32(int T, const SpecArgs& a, unsigned grid, hipStream_t 
 #undef EQL_CASE
 }
 
-hipError_t launch_bwdw_f32(int T, int NB, const BwdwArgs& a, unsigned grid, hipStream_t s) {
-#define EQL_CASE(t) return bwdw_one<t>(NB, a, grid, s);
+hipError_t launch_bwdw_f32(int T, bool pair, const BwdwArgs& a, unsigned grid, hipStream_t s) {
+#define EQL_CASE(t) return bwdw_one<t>(pair, a, grid, s);
   EQL_FOR_EACH_T(T, EQL_CASE)
 #undef EQL_CASE
 }

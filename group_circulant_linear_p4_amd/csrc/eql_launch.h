@@ -15,9 +15,6 @@ namespace eql {
 __host__ __device__ constexpr int fwd_nb_max(int T) { return T <= 4 ? 4 : (T <= 8 ? 2 : 1); }
 // Channel groups per K chunk (two per k-step).
 __host__ __device__ constexpr int fwd_jc(int) { return 2; }
-// bwd_w GEMM: 32-column blocks per wave, the full-width tile and (when that is
-// above 1) a half-width one for narrow C'.
-__host__ __device__ constexpr int bwdw_nb_max(int T) { return fwd_nb_max(T); }
 
 // The packed weight's input axis is padded to a multiple of this many 16-byte
 // groups, so that every K stage of the forward kernel reads whole groups.
@@ -29,8 +26,9 @@ hipError_t launch_fwd_f16(int T, int NB, const FwdArgs& a, unsigned grid, hipStr
 hipError_t launch_fwd_f32(int T, int NB, const FwdArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_spec_f16(int T, const SpecArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_spec_f32(int T, const SpecArgs& a, unsigned grid, hipStream_t s);
-hipError_t launch_bwdw_f16(int T, int NB, const BwdwArgs& a, unsigned grid, hipStream_t s);
-hipError_t launch_bwdw_f32(int T, int NB, const BwdwArgs& a, unsigned grid, hipStream_t s);
+// pair = false: the real planes' GEMM; true: the complex pairs' GEMM (T >= 3).
+hipError_t launch_bwdw_f16(int T, bool pair, const BwdwArgs& a, unsigned grid, hipStream_t s);
+hipError_t launch_bwdw_f32(int T, bool pair, const BwdwArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_bwdw_reduce_f16(int T, const BwdwReduceArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_bwdw_reduce_f32(int T, const BwdwReduceArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_pack_f16(int T, const PackArgs& a, unsigned grid, hipStream_t s);

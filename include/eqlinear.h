@@ -127,20 +127,21 @@ int eqlinear_bwd_x(const void* dy, const void* w_packed_bwdx, void* dx, int64_t 
  * Scratch bytes eqlinear_bwd_w needs for this shape.  Depends only on the
  * arguments (0 when N == 0 or the arguments are invalid).  The workspace holds the
  * half spectra of dy and x (each about the size of that tensor: T real planes per
- * channel, rows padded to a multiple of 2 * 16 / sizeof(element), channels to
- * whole GEMM tiles of 32 to 128) followed by S
- * fp32 partial spectra of the gradient, S * T * Dp * Cp * 4 bytes, one per row
- * range of the reduction over N.
+ * channel, rows padded to a multiple of 2 * 16 / sizeof(element), channels to a
+ * multiple of 256) followed by fp32 partial spectra of the gradient: whole
+ * Dp x Cp planes, one set per row range of the reduction over N (the real
+ * frequencies and the complex pairs are split separately).
  */
 size_t eqlinear_bwd_w_workspace_bytes(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype);
 
 /*
  * Weight gradient: dw[d][c][t] = sum_n sum_g dy[n][d*T+g] x[n][c*T+((g-t) mod T)],
- * the dense gradient dy^T x summed over the entries tied to w[d][c][t].  Three
- * launches: the group transforms of dy and x (fp32, rounded once to `dtype`) into
- * the workspace; per frequency the channel GEMM dY_k^T conj(X_k) (K = N, fp32
- * accumulation, one partial per row range); the sum of the partials in a fixed
- * order (deterministic), the inverse transform and the rounding to `dtype`.
+ * the dense gradient dy^T x summed over the entries tied to w[d][c][t].  Launches:
+ * the group transforms of dy and x (fp32, rounded once to `dtype`) into the
+ * workspace; per frequency the channel GEMM dY_k^T conj(X_k) (K = N, fp32
+ * accumulation, one partial per row range; one launch for the real frequencies and
+ * one for the complex pairs); the sum of the partials in a fixed order
+ * (deterministic), the inverse transform and the rounding to `dtype`.
  * x: [N][Cp*T], dy: [N][Dp*T] read; dw: [Dp][Cp][T] overwritten (zeros when
  * N == 0, which launches one small kernel); workspace: device memory of at least
  * eqlinear_bwd_w_workspace_bytes bytes, 16-byte aligned (contents on entry

@@ -55,18 +55,18 @@ def test_packed_weight_bytes():
 def test_workspace_bytes():
     assert eql.eqlinear_bwd_w_workspace_bytes(0, 4, 4, 4, eql.EQL_F16) == 0
     # Layout: dy and x half spectra as 16-byte units (2G rows per k-step, G = 8 for
-    # fp16; channels padded to whole tiles: 128 for dy, 32*NB for x with NB = 4 for
-    # p4 unless 64-wide tiles pad C' less; each section 256-byte aligned), then whole
-    # fp32 partial spectra.
-    for (N, Cp, Dp, G, code, bn) in ((65536, 1024, 1024, 8, eql.EQL_F16, 128), (37, 5, 3, 4, eql.EQL_F32, 64),
-                                     (100352, 192, 768, 8, eql.EQL_F16, 64)):
+    # fp16 and 4 for fp32; channels padded to a multiple of 256; each section
+    # 256-byte aligned), then fp32 partial spectra: whole [D'][C'] planes, at least
+    # one set of T planes and at most one set per k-step.
+    for (N, Cp, Dp, G, code) in ((65536, 1024, 1024, 8, eql.EQL_F16), (37, 5, 3, 4, eql.EQL_F32),
+                                 (100352, 192, 768, 8, eql.EQL_F16)):
         T = 4
         n = eql.eqlinear_bwd_w_workspace_bytes(N, Cp, Dp, T, code)
         steps = -(-N // (2 * G))
-        spec = sum(-(-(steps * T * 2 * (-(-K // w) * w) * 16) // 256) * 256 for K, w in ((Dp, 128), (Cp, bn)))
+        spec = sum(-(-(steps * T * 2 * (-(-K // 256) * 256) * 16) // 256) * 256 for K in (Dp, Cp))
         part = n - spec
-        assert part > 0 and part % (T * Dp * Cp * 4) == 0
-        assert part // (T * Dp * Cp * 4) <= steps                   # at most one range per k-step
+        plane = Dp * Cp * 4
+        assert T * plane <= part <= steps * T * plane + 256
     assert eql.eqlinear_bwd_w_workspace_bytes(10, 4, 4, 0, eql.EQL_F16) == 0
 
 
