@@ -116,6 +116,21 @@ def test_p4_multi_tile(dtype, shape):
     assert rel_err(dw, oracle.bwd_w(x, dy, 4)) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("T", [3, 4, 8])
+def test_multi_tile_ragged_channels(T, dtype):
+    """Several 256-wide weight-gradient tiles in both channel axes, each with a
+    ragged last tile, more rows than one k-step range, and for odd T a single real
+    plane beside the complex pairs."""
+    N, Cp, Dp = 700, 300, 520
+    print("case T=%d %s N=%d C'=%d D'=%d" % (T, dtype, N, Cp, Dp), flush=True)
+    x, w, dy = inputs(T, N, Cp, Dp, dtype, seed=11 + T)
+    y, dx, dw = Lib(T, dtype).all_passes(x, w, dy)
+    assert rel_err(y, oracle.fwd(x, w)) <= TOL[dtype]
+    assert rel_err(dx, oracle.bwd_x(dy, w)) <= TOL[dtype]
+    assert rel_err(dw, oracle.bwd_w(x, dy, T)) <= TOL[dtype]
+
+
 # ------------------------------------------------------------ the five workloads
 def _sample_rows(N, k=192, seed=5):
     rng = np.random.default_rng(seed)
