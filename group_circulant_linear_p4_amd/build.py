@@ -28,6 +28,10 @@ SOURCES = [
     "eql_fwd_f32.hip",
     "eql_bwdw_f16.hip",
     "eql_bwdw_f32.hip",
+    "eql_bwdw_real_f16.hip",
+    "eql_bwdw_real_f32.hip",
+    "eql_bwdw_pair_f16.hip",
+    "eql_bwdw_pair_f32.hip",
 ]
 
 CFLAGS = [

@@ -122,13 +122,18 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 // Weight-gradient plan.  The workspace holds, in order (each section 256-byte
 // aligned): the half spectra of dy and of x as MFMA operand units (2G rows per
-// k-step, zero rows past N, channels padded to a multiple of 256), then the fp32
-// partial spectra of the real-plane GEMM [SR][NR][Dp][Cp] and of the complex-pair
-// GEMM [SP][T-NR][Dp][Cp].
+// k-step, zero rows past N, channels padded to a multiple of the GEMM tile width),
+// then the fp32 partial spectra of the real-plane GEMM [SR][NR][Dp][Cp] and of the
+// complex-pair GEMM [SP][T-NR][Dp][Cp].
 struct GemmPlan {
+  int DB = 1, CB = 1;  // workgroup tile 64 DB x 64 CB
   int64_t groups = 0, dTiles = 0, cTiles = 0, S = 0, kgPerSplit = 0;
   int64_t items() const { return S * groups * dTiles * cTiles; }
 };
+
+// Tile width of one channel axis: 256 unless padding to it adds more than a third
+// of the channels, else 64.
+int64_t tile_width(int64_t ch) { return ceil_div(ch, 256) * 256 * 3 <= ch * 4 ? 256 : 64; }
 
 struct BwdwPlan {
   int64_t kgCount = 0, Dpad = 0, Cpad = 0;
@@ -153,14 +158,21 @@ void plan_splits(GemmPlan& g, int64_t kgCount) {
 BwdwPlan plan_bwdw(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype) {
   BwdwPlan p;
   const int nr = n_real_planes(T), np = n_pairs(T);
-  p.Dpad = ceil_div(Dp, kBwdwPad) * kBwdwPad;
-  p.Cpad = ceil_div(Cp, kBwdwPad) * kBwdwPad;
+  const int64_t wd = tile_width(Dp), wc = tile_width(Cp);
+  p.Dpad = ceil_div(Dp, wd) * wd;
+  p.Cpad = ceil_div(Cp, wc) * wc;
+  // Real planes: wd x wc tiles; complex pairs hold two planes, so half as wide in c
+  // (at least 64).
+  p.real.DB = (int)(wd / 64);
+  p.real.CB = (int)(wc / 64);
+  p.pair.DB = p.real.DB;
+  p.pair.CB = wc == 256 ? 2 : 1;
   p.real.groups = nr;
-  p.real.dTiles = p.Dpad / kBwdwTileD;
-  p.real.cTiles = p.Cpad / 256;
+  p.real.dTiles = p.Dpad / wd;
+  p.real.cTiles = p.Cpad / wc;
   p.pair.groups = np;
-  p.pair.dTiles = p.Dpad / kBwdwTileD;
-  p.pair.cTiles = p.Cpad / 128;
+  p.pair.dTiles = p.Dpad / wd;
+  p.pair.cTiles = p.Cpad / (64 * p.pair.CB);
   if (N == 0) return p;
   p.kgCount = ceil_div(N, 2 * group_channels(dtype));
   plan_splits(p.real, p.kgCount);
@@ -295,8 +307,12 @@ int eqlinear_bwd_w(const void* x, const void* dy, void* dw, void* workspace, siz
       a.dTiles = (int)g.dTiles;
       a.cTiles = (int)g.cTiles;
       a.numItems = (int)g.items();
-      e = f16 ? launch_bwdw_f16(T, pair != 0, a, (unsigned)a.numItems, s)
-              : launch_bwdw_f32(T, pair != 0, a, (unsigned)a.numItems, s);
+      if (pair)
+        e = f16 ? launch_bwdw_pair_f16(T, g.DB, g.CB, a, (unsigned)a.numItems, s)
+                : launch_bwdw_pair_f32(T, g.DB, g.CB, a, (unsigned)a.numItems, s);
+      else
+        e = f16 ? launch_bwdw_real_f16(T, g.DB, g.CB, a, (unsigned)a.numItems, s)
+                : launch_bwdw_real_f32(T, g.DB, g.CB, a, (unsigned)a.numItems, s);
       if (e != hipSuccess) return EQL_EHIP;
     }
   }

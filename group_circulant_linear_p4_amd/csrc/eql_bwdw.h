@@ -13,16 +13,18 @@
 //      (kg, p, half, k) holds plane p of channel k for the G rows
 //      kg*2G + half*G .. +G (G = 16 / sizeof(element); rows past N and channels
 //      past the channel count are zero).  Layout [kg][p][half][Kpad] with the channel
-//      axis padded to a multiple of 256, so a tile's units of one k-step are 2 or 4
-//      contiguous runs.  Purely bandwidth bound.
-//   2. eql_bwdw_gemm<T, Elt, PAIR>: the per-frequency GEMMs, one plane group per
-//      workgroup so that its output tile can be as large as the register file
-//      allows: a real plane takes a 256 (d) x 256 (c) tile, a complex pair a 256 x
-//      128 tile of both planes (4 waves in a 2 x 2 arrangement, 256 accumulator
-//      registers per lane either way).  Per MFMA that moves about 0.56-0.75x the
-//      operand bytes of a tile holding all T planes.  Both operands stream into
-//      NS-deep LDS rings by buffer->LDS loads; the loop body is LDS reads and MFMAs.
-//      Each item writes the fp32 partial spectrum of one row range.
+//      axis padded to a multiple of the GEMM tile width, so a tile's units of one
+//      k-step are 2 or 4 contiguous runs.  Purely bandwidth bound.
+//   2. eql_bwdw_gemm<T, Elt, PAIR, DB, CB>: the per-frequency GEMMs, one plane group
+//      per workgroup so that its output tile can be as large as the register file
+//      allows: 4 waves in a 2 x 2 arrangement, each with DB x CB blocks of 32 x 32
+//      outputs per plane.  For large channel counts a real plane takes a 256 (d) x
+//      256 (c) tile and a complex pair a 256 x 128 tile of both planes (256
+//      accumulator registers per lane either way); per MFMA that moves about
+//      0.56-0.75x the operand bytes of a tile holding all T planes.  Narrow channel
+//      axes take 64-wide tiles instead of padding to 256.  Both operands stream
+//      into NS-deep LDS rings by buffer->LDS loads; the loop body is LDS reads and
+//      MFMAs.  Each item writes the fp32 partial spectrum of one row range.
 //   3. eql_bwdw_reduce: sums the partials in a fixed order (deterministic), applies
 //      the inverse group transform and rounds to the element type.
 #pragma once
@@ -33,9 +35,6 @@
 #include "eql_dma.h"
 
 namespace eql {
-
-constexpr int kBwdwTileD = 256;  // output channels d per workgroup
-constexpr int kBwdwPad = 256;    // channel padding of the spectra
 
 struct SpecArgs {
   const void* m;    // [N][K*T]
@@ -92,26 +91,26 @@ __global__ void __launch_bounds__(256) eql_spec_kernel(const SpecArgs a) {
   for (int p = 0; p < T; ++p) out[(size_t)p * 2 * a.Kpad] = E::pack(pl[p]);
 }
 
-template <int T, typename Elt, bool PAIR>
+template <int T, typename Elt, bool PAIR, int DB, int CB>
 __global__ void __launch_bounds__(256) eql_bwdw_gemm(const BwdwArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using E = EltT<Elt>;
   constexpr int NR = n_real_planes(T);
   constexpr int NPL = PAIR ? 2 : 1;          // planes per item
-  constexpr int WC = PAIR ? 128 : 256;       // input channels c per workgroup
-  constexpr int DB = 4;                      // 32-row blocks per wave (128 d)
-  constexpr int CB = WC / 64;                // 32-column blocks per wave (WC / 2 c)
-  constexpr int UA = NPL * 2 * kBwdwTileD;   // A units per stage (one k-step)
+  constexpr int WD = 64 * DB;                // output channels d per workgroup
+  constexpr int WC = 64 * CB;                // input channels c per workgroup
+  constexpr int UA = NPL * 2 * WD;           // A units per stage (one k-step)
   constexpr int UB = NPL * 2 * WC;           // B units per stage
+  // ... padded to whole loads of 4 waves x 64 lanes
+  constexpr int UAP = (UA + 255) / 256 * 256, UBP = (UB + 255) / 256 * 256;
   constexpr int NS = 4;
-  constexpr int IPWA = UA / 256, IPWB = UB / 256;  // DMA loads per wave per stage
+  constexpr int IPWA = UAP / 256, IPWB = UBP / 256;  // DMA loads per wave per stage
   constexpr int IPW = IPWA + IPWB;
-  static_assert(UA % 256 == 0 && UB % 256 == 0, "whole wave loads");
-  static_assert(NS * (UA + UB) * 16 <= 160 * 1024, "LDS budget");
+  static_assert(NS * (UAP + UBP) * 16 <= 160 * 1024, "LDS budget");
   static_assert((NS - 1) * IPW < 64, "vmcnt range");
 
-  __shared__ u32x4 ringA[NS][UA];
-  __shared__ u32x4 ringB[NS][UB];
+  __shared__ u32x4 ringA[NS][UAP];
+  __shared__ u32x4 ringB[NS][UBP];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -124,26 +123,27 @@ __global__ void __launch_bounds__(256) eql_bwdw_gemm(const BwdwArgs a) {
   const int grp = rest / (a.dTiles * a.cTiles);
   rest -= grp * (a.dTiles * a.cTiles);
   const int dTile = rest / a.cTiles, cTile = rest - dTile * a.cTiles;
-  const int d0 = dTile * kBwdwTileD, c0 = cTile * WC;
+  const int d0 = dTile * WD, c0 = cTile * WC;
   const int p0 = PAIR ? NR + 2 * grp : grp;  // first plane of the item
   const int kgBegin = split * a.kgPerSplit;
   const int kgEnd = min(a.kgCount, kgBegin + a.kgPerSplit);
   const int nst = max(0, kgEnd - kgBegin);
 
-  // A stage is run s = plane*2 + half of the item's planes: A units d0 .. d0+255
+  // A stage is run s = plane*2 + half of the item's planes: A units d0 .. d0+WD-1
   // of that run, B units c0 .. c0+WC-1; unit P of the stage lands at ring unit P.
+  // Padding positions of the last wave load (P >= UA or UB) re-read unit 0.
   uint32_t aOff[IPWA], bOff[IPWB];
 #pragma unroll
   for (int i = 0; i < IPWA; ++i) {
     const int P = (wave * IPWA + i) * 64 + lane;
-    const int s = P / kBwdwTileD, j = P - s * kBwdwTileD;
-    aOff[i] = ((uint32_t)s * a.Dpad + (uint32_t)(d0 + j)) * 16u;
+    const int s = P / WD, j = P - s * WD;
+    aOff[i] = P < UA ? ((uint32_t)s * a.Dpad + (uint32_t)(d0 + j)) * 16u : 0u;
   }
 #pragma unroll
   for (int i = 0; i < IPWB; ++i) {
     const int P = (wave * IPWB + i) * 64 + lane;
     const int s = P / WC, j = P - s * WC;
-    bOff[i] = ((uint32_t)s * a.Cpad + (uint32_t)(c0 + j)) * 16u;
+    bOff[i] = P < UB ? ((uint32_t)s * a.Cpad + (uint32_t)(c0 + j)) * 16u : 0u;
   }
   // Byte offset of k-step kg's first run, and the bytes the item's runs span.
   const uint64_t aBase = reinterpret_cast<uint64_t>(a.dyh), bBase = reinterpret_cast<uint64_t>(a.xh);
@@ -186,8 +186,8 @@ __global__ void __launch_bounds__(256) eql_bwdw_gemm(const BwdwArgs a) {
         for (int r = 0; r < 16; ++r) acc[q][i][jc][r] = 0.0f;
 
   // Operand fragments of one k-step: lane (lcol, khalf) holds plane q of output
-  // channel d0 + 128*wd + 32*i + lcol (A) / input channel c0 + (WC/2)*wc + 32*jc +
-  // lcol (B) for rows khalf*G .. +G of the step.
+  // channel d0 + (WD/2)*wd + 32*i + lcol (A) / input channel c0 + (WC/2)*wc + 32*jc
+  // + lcol (B) for rows khalf*G .. +G of the step.
   struct Frags {
     u32x4 a[NPL][DB];
     u32x4 b[NPL][CB];
@@ -198,7 +198,7 @@ __global__ void __launch_bounds__(256) eql_bwdw_gemm(const BwdwArgs a) {
 #pragma unroll
     for (int q = 0; q < NPL; ++q) {
 #pragma unroll
-      for (int i = 0; i < DB; ++i) f.a[q][i] = sa[(q * 2 + khalf) * kBwdwTileD + wd * 128 + i * 32 + lcol];
+      for (int i = 0; i < DB; ++i) f.a[q][i] = sa[(q * 2 + khalf) * WD + wd * (WD / 2) + i * 32 + lcol];
 #pragma unroll
       for (int jc = 0; jc < CB; ++jc) f.b[q][jc] = sb[(q * 2 + khalf) * WC + wc * (WC / 2) + jc * 32 + lcol];
     }
@@ -289,7 +289,7 @@ __global__ void __launch_bounds__(256) eql_bwdw_gemm(const BwdwArgs a) {
         const int c = c0 + wc * (WC / 2) + jc * 32 + lcol;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int d = d0 + wd * 128 + i * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+          const int d = d0 + wd * (WD / 2) + i * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
           if (d < a.Dp && c < a.Cp) out[(size_t)d * a.Cp + c] = acc[q][i][jc][r];
         }
       }

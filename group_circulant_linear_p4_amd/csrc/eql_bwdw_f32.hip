@@ -1,4 +1,4 @@
-// Weight-gradient kernel instantiations for the f32 element type, T = 1..16.
+// Weight-gradient transform and reduce instantiations for the f32 element type, T = 1..16.
 #include "eql_launch.h"
 
 namespace eql {
@@ -9,25 +9,12 @@ static hipError_t spec_one(const SpecArgs& a, unsigned grid, hipStream_t s) {
 }
 
 template <int T>
-static hipError_t bwdw_one(bool pair, const BwdwArgs& a, unsigned grid, hipStream_t s) {
-  if (!pair) return launch_kernel((const void*)&eql_bwdw_gemm<T, float, false>, grid, a, s);
-  if constexpr (n_pairs(T) > 0) return launch_kernel((const void*)&eql_bwdw_gemm<T, float, true>, grid, a, s);
-  return hipErrorInvalidValue;
-}
-
-template <int T>
 static hipError_t reduce_one(const BwdwReduceArgs& a, unsigned grid, hipStream_t s) {
   return launch_kernel((const void*)&eql_bwdw_reduce<T, float>, grid, a, s);
 }
 
 hipError_t launch_spec_f32(int T, const SpecArgs& a, unsigned grid, hipStream_t s) {
 #define EQL_CASE(t) return spec_one<t>(a, grid, s);
-  EQL_FOR_EACH_T(T, EQL_CASE)
-#undef EQL_CASE
-}
-
-hipError_t launch_bwdw_f32(int T, bool pair, const BwdwArgs& a, unsigned grid, hipStream_t s) {
-#define EQL_CASE(t) return bwdw_one<t>(pair, a, grid, s);
   EQL_FOR_EACH_T(T, EQL_CASE)
 #undef EQL_CASE
 }

@@ -26,9 +26,12 @@ hipError_t launch_fwd_f16(int T, int NB, const FwdArgs& a, unsigned grid, hipStr
 hipError_t launch_fwd_f32(int T, int NB, const FwdArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_spec_f16(int T, const SpecArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_spec_f32(int T, const SpecArgs& a, unsigned grid, hipStream_t s);
-// pair = false: the real planes' GEMM; true: the complex pairs' GEMM (T >= 3).
-hipError_t launch_bwdw_f16(int T, bool pair, const BwdwArgs& a, unsigned grid, hipStream_t s);
-hipError_t launch_bwdw_f32(int T, bool pair, const BwdwArgs& a, unsigned grid, hipStream_t s);
+// Weight-gradient GEMMs: the real planes' (DB, CB in {4, 1}) and the complex pairs'
+// (DB in {4, 1}, CB in {2, 1}; T >= 3), workgroup tile 64 DB x 64 CB.
+hipError_t launch_bwdw_real_f16(int T, int DB, int CB, const BwdwArgs& a, unsigned grid, hipStream_t s);
+hipError_t launch_bwdw_real_f32(int T, int DB, int CB, const BwdwArgs& a, unsigned grid, hipStream_t s);
+hipError_t launch_bwdw_pair_f16(int T, int DB, int CB, const BwdwArgs& a, unsigned grid, hipStream_t s);
+hipError_t launch_bwdw_pair_f32(int T, int DB, int CB, const BwdwArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_bwdw_reduce_f16(int T, const BwdwReduceArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_bwdw_reduce_f32(int T, const BwdwReduceArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_pack_f16(int T, const PackArgs& a, unsigned grid, hipStream_t s);

@@ -55,15 +55,20 @@ def test_packed_weight_bytes():
 def test_workspace_bytes():
     assert eql.eqlinear_bwd_w_workspace_bytes(0, 4, 4, 4, eql.EQL_F16) == 0
     # Layout: dy and x half spectra as 16-byte units (2G rows per k-step, G = 8 for
-    # fp16 and 4 for fp32; channels padded to a multiple of 256; each section
-    # 256-byte aligned), then fp32 partial spectra: whole [D'][C'] planes, at least
-    # one set of T planes and at most one set per k-step.
+    # fp16 and 4 for fp32; channels padded to the GEMM tile width, 256 unless that
+    # pads more than a third of the channels, else 64; each section 256-byte
+    # aligned), then fp32 partial spectra: whole [D'][C'] planes, at least one set
+    # of T planes and at most one set per k-step.
+    def padded(ch):
+        w = 256 if -(-ch // 256) * 256 * 3 <= ch * 4 else 64
+        return -(-ch // w) * w
+
     for (N, Cp, Dp, G, code) in ((65536, 1024, 1024, 8, eql.EQL_F16), (37, 5, 3, 4, eql.EQL_F32),
                                  (100352, 192, 768, 8, eql.EQL_F16)):
         T = 4
         n = eql.eqlinear_bwd_w_workspace_bytes(N, Cp, Dp, T, code)
         steps = -(-N // (2 * G))
-        spec = sum(-(-(steps * T * 2 * (-(-K // 256) * 256) * 16) // 256) * 256 for K in (Dp, Cp))
+        spec = sum(-(-(steps * T * 2 * padded(K) * 16) // 256) * 256 for K in (Dp, Cp))
         part = n - spec
         plane = Dp * Cp * 4
         assert T * plane <= part <= steps * T * plane + 256
