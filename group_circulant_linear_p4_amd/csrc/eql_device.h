@@ -282,6 +282,15 @@ __device__ __forceinline__ void store_group(Elt* p, const float (&v)[T]) {
   }
 }
 
+// Index of the calling lane in its wave (0..63), computed afresh at each call: an
+// asm statement, so the compiler cannot merge it with an earlier value and keep
+// that one live instead.
+__device__ __forceinline__ int lane_index() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 // XCD-aware tile order.  Consecutive workgroup ids are dispatched round-robin over
 // the 8 XCDs; this remaps them so that each XCD receives a contiguous range of
 // logical tiles (and so shares row blocks of the input in its own L2).

@@ -21,6 +21,43 @@ __device__ __forceinline__ void wait_lgkm0() {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+
+// Stores the T values of one group (rounded to Elt) at byte offset `off` of buffer
+// `r`; accesses at or beyond the buffer's range are dropped by the hardware, so the
+// caller masks rows and columns through the offset instead of a branch.
+template <int T, typename Elt>
+__device__ __forceinline__ void store_group_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, const float (&v)[T]) {
+  constexpr int BYTES = T * (int)sizeof(Elt);
+  constexpr int W = pow2_part(BYTES);
+  if constexpr (W >= 4) {
+    constexpr int WORDS = BYTES / 4;
+    uint32_t w[WORDS];
+#pragma unroll
+    for (int i = 0; i < WORDS; ++i) {
+      if constexpr (sizeof(Elt) == 2) {
+        const _Float16 lo = (_Float16)v[2 * i], hi = (_Float16)v[2 * i + 1];
+        w[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+      } else {
+        w[i] = __builtin_bit_cast(uint32_t, v[i]);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < BYTES; b += W) {
+      if constexpr (W == 16) {
+        __builtin_amdgcn_raw_buffer_store_b128((u32x4){w[b / 4], w[b / 4 + 1], w[b / 4 + 2], w[b / 4 + 3]}, r,
+                                               off + b, 0, 0);
+      } else if constexpr (W == 8) {
+        __builtin_amdgcn_raw_buffer_store_b64((u32x2){w[b / 4], w[b / 4 + 1]}, r, off + b, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b32(w[b / 4], r, off + b, 0, 0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < T; ++e)
+      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (Elt)v[e]), r, off + 2 * e, 0, 0);
+  }
+}
 #endif
 
 // Offsets at or beyond this value are outside every buffer: the load returns zero.

@@ -366,23 +366,29 @@ __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
   };
 
   // Epilogue of tile k: accumulator slot r of lane l holds row 8*(r/4) + 4*(l/32) +
-  // r%4 and column l%32 of each 32x32 block.
-  Elt* __restrict__ yout = static_cast<Elt*>(a.y);
+  // r%4 and column l%32 of each 32x32 block.  Stores go through a buffer
+  // descriptor covering the tile's valid rows; columns past D' take an offset
+  // beyond every range, so no store needs a branch.
+  const uint32_t outRow = (uint32_t)a.Dout * T * ELT;  // bytes of one output row
   auto epilogue = [&](int k) __attribute__((always_inline)) {
     const int row0 = tile_row0(k), col0 = tile_col0(k);
+    const uint32_t rows = (uint32_t)min(kFwdRows, a.N - row0);
+    const __amdgpu_buffer_rsrc_t yr = make_rsrc(static_cast<char*>(a.y) + (size_t)row0 * outRow, rows * outRow);
+    // The lane index is recomputed here rather than kept live through the main
+    // loop, where every register is taken.
+    const int ln = lane_index();
+    const uint32_t laneOff = (uint32_t)(wave * 32 + 4 * (ln >> 5)) * outRow;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int col = col0 + nb * 32 + lrow;
+      const int col = col0 + nb * 32 + (ln & 31);
+      const uint32_t cOff = col < a.Dout ? laneOff + (uint32_t)col * T * ELT : kOob;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = row0 + wave * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
-        if (row < a.N && col < a.Dout) {
-          float P[T], yv[T];
+        float P[T], yv[T];
 #pragma unroll
-          for (int p = 0; p < T; ++p) P[p] = acc[p][nb][r];
-          Idft<T, false>::run(P, yv, a.tw);
-          store_group<T, Elt>(yout + ((size_t)row * a.Dout + col) * T, yv);
-        }
+        for (int p = 0; p < T; ++p) P[p] = acc[p][nb][r];
+        Idft<T, false>::run(P, yv, a.tw);
+        store_group_buf<T, Elt>(yr, cOff + (uint32_t)(8 * (r >> 2) + (r & 3)) * outRow, yv);
       }
     }
   };
