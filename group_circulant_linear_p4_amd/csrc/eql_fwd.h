@@ -58,6 +58,15 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 //   and X2 = (x0-x1) + (x2-x3) are fp32 dot products of the fp16 pairs, rounded
 //   once to fp16.  The 1/2 of the p4 forward transform is folded into the packed
 //   weight's real planes.
+// b.lo*c.lo + b.hi*c.hi in fp32: v_dot2_f32_f16 with the addend given as the inline
+// constant 0 (the two-operand form accumulates into its destination, which then
+// has to be zeroed by a separate move first).
+__device__ __forceinline__ float dot2_f16(f16x2 b, f16x2 c) {
+  float r;
+  asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(b), "v"(c));
+  return r;
+}
+
 __device__ __forceinline__ void dft_p4_f16(const uint32_t (&raw)[16], u32x4 (&out)[5]) {
   const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
   const f16x2 pm = {(_Float16)1.0f, (_Float16)-1.0f};
@@ -66,10 +75,10 @@ __device__ __forceinline__ void dft_p4_f16(const uint32_t (&raw)[16], u32x4 (&ou
     const f16x2 a0 = __builtin_bit_cast(f16x2, raw[4 * q + 0]), b0 = __builtin_bit_cast(f16x2, raw[4 * q + 1]);
     const f16x2 a1 = __builtin_bit_cast(f16x2, raw[4 * q + 2]), b1 = __builtin_bit_cast(f16x2, raw[4 * q + 3]);
     const f16x2 d0 = a0 - b0, d1 = a1 - b1;  // (Xr, -Xi) of each channel
-    const float x0e = __builtin_amdgcn_fdot2(a0, ones, __builtin_amdgcn_fdot2(b0, ones, 0.0f, false), false);
-    const float x0o = __builtin_amdgcn_fdot2(a1, ones, __builtin_amdgcn_fdot2(b1, ones, 0.0f, false), false);
-    const float x2e = __builtin_amdgcn_fdot2(a0, pm, __builtin_amdgcn_fdot2(b0, pm, 0.0f, false), false);
-    const float x2o = __builtin_amdgcn_fdot2(a1, pm, __builtin_amdgcn_fdot2(b1, pm, 0.0f, false), false);
+    const float x0e = __builtin_amdgcn_fdot2(a0, ones, dot2_f16(b0, ones), false);
+    const float x0o = __builtin_amdgcn_fdot2(a1, ones, dot2_f16(b1, ones), false);
+    const float x2e = __builtin_amdgcn_fdot2(a0, pm, dot2_f16(b0, pm), false);
+    const float x2o = __builtin_amdgcn_fdot2(a1, pm, dot2_f16(b1, pm), false);
     const f16x2 X0 = {(_Float16)x0e, (_Float16)x0o};
     const f16x2 X2 = {(_Float16)x2e, (_Float16)x2o};
     const uint32_t nxi = __builtin_bit_cast(uint32_t, __builtin_shufflevector(d0, d1, 1, 3));
