@@ -95,6 +95,40 @@ __device__ __forceinline__ void dma16(const BufDesc& d, uint32_t voff, uint32_t 
                : "memory");
 }
 
+// N loads of dma16 with one descriptor, lane offsets voff[i] and LDS bases
+// lds[i], in one asm statement: its operands are all computed before it, so a
+// single 5-wait-state gap covers the VALU-to-SGPR hazard for the whole batch
+// (only the M0 writes inside it need their 1 wait state each).  M0 is written with
+// s_mov only, so no scalar condition code is touched.
+#define EQL_DMA_ONE(v, l) "s_mov_b32 m0, %" #l "\n\ts_nop 0\n\tbuffer_load_dwordx4 %" #v ", %[desc], 0 offen lds\n\t"
+template <int N>
+__device__ __forceinline__ void dma16_batch(const BufDesc& d, const uint32_t (&voff)[N], const uint32_t (&lds)[N]) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8, "batch size");
+  const u32x4 w = {(uint32_t)__builtin_amdgcn_readfirstlane(d.w[0]), (uint32_t)__builtin_amdgcn_readfirstlane(d.w[1]),
+                   (uint32_t)__builtin_amdgcn_readfirstlane(d.w[2]), (uint32_t)__builtin_amdgcn_readfirstlane(d.w[3])};
+  uint32_t l[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) l[i] = (uint32_t)__builtin_amdgcn_readfirstlane(lds[i]);
+  if constexpr (N == 1) {
+    asm volatile("s_nop 4\n\t" EQL_DMA_ONE(0, 1) : : "v"(voff[0]), "s"(l[0]), [desc] "s"(w) : "memory");
+  } else if constexpr (N == 2) {
+    asm volatile("s_nop 4\n\t" EQL_DMA_ONE(0, 2) EQL_DMA_ONE(1, 3)
+                 : : "v"(voff[0]), "v"(voff[1]), "s"(l[0]), "s"(l[1]), [desc] "s"(w) : "memory");
+  } else if constexpr (N == 4) {
+    asm volatile("s_nop 4\n\t" EQL_DMA_ONE(0, 4) EQL_DMA_ONE(1, 5) EQL_DMA_ONE(2, 6) EQL_DMA_ONE(3, 7)
+                 : : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]),
+                     "s"(l[0]), "s"(l[1]), "s"(l[2]), "s"(l[3]), [desc] "s"(w) : "memory");
+  } else {
+    asm volatile("s_nop 4\n\t" EQL_DMA_ONE(0, 8) EQL_DMA_ONE(1, 9) EQL_DMA_ONE(2, 10) EQL_DMA_ONE(3, 11)
+                 EQL_DMA_ONE(4, 12) EQL_DMA_ONE(5, 13) EQL_DMA_ONE(6, 14) EQL_DMA_ONE(7, 15)
+                 : : "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]),
+                     "v"(voff[4]), "v"(voff[5]), "v"(voff[6]), "v"(voff[7]),
+                     "s"(l[0]), "s"(l[1]), "s"(l[2]), "s"(l[3]), "s"(l[4]), "s"(l[5]), "s"(l[6]), "s"(l[7]),
+                     [desc] "s"(w) : "memory");
+  }
+}
+#undef EQL_DMA_ONE
+
 // Descriptor of `bytes` bytes at `base` (words built from scalar values).
 __device__ __forceinline__ BufDesc desc_at(uint64_t base, uint32_t bytes) {
   BufDesc d;

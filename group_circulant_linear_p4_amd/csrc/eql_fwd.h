@@ -224,19 +224,23 @@ __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
       const uint32_t st0 = (uint32_t)issSt * JC * T * 16u;
       const BufDesc d = desc_at(bTileBase + st0, (issK < myTiles && bTileBytes > st0) ? bTileBytes - st0 : 0u);
       const uint32_t dst = lds_addr(&ringB[g % NS][wave * IPW * 64]);
+      uint32_t l[IPW];
 #pragma unroll
-      for (int i = 0; i < IPW; ++i) dma16(d, bOff[i], dst + i * 1024u);
+      for (int i = 0; i < IPW; ++i) l[i] = dst + i * 1024u;
+      dma16_batch<IPW>(d, bOff, l);
     }
     if constexpr (XLDS) {
       const int c0 = issSt * JC * G;
       const uint32_t st0 = (uint32_t)c0 * T * ELT;
       const BufDesc d = desc_at(xTileBase + st0, (issK < myTiles && xTileBytes > st0) ? xTileBytes - st0 : 0u);
       const uint32_t dst = lds_addr(&ringX[g % NS][wave * 32 * RP]);
+      uint32_t off[IPWX], l[IPWX];
 #pragma unroll
       for (int i = 0; i < IPWX; ++i) {
-        const uint32_t off = (LOAD == kLoadFull || c0 + xCh[i] < a.Cin) ? xOff[i] : kOob;
-        dma16(d, off, dst + i * 1024u);
+        off[i] = (LOAD == kLoadFull || c0 + xCh[i] < a.Cin) ? xOff[i] : kOob;
+        l[i] = dst + i * 1024u;
       }
+      dma16_batch<IPWX>(d, off, l);
     }
     if (++issSt == nst) {
       issSt = 0;
