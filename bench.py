@@ -142,6 +142,8 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
     per = {k: float(np.mean([e[k][0].elapsed_time(e[k][1]) for e in evs])) for k in order}
+    # Device time of each step (the sum of its passes' event windows): spread across steps.
+    step_dev = [sum(e[k][0].elapsed_time(e[k][1]) for k in order) for e in evs]
 
     dense_eq = 2.0 * N * (Dp * T) * (Cp * T)
     actual = 2.0 * (2 * T - 2 if T % 2 == 0 else 2 * T - 1) * N * Dp * Cp if T > 1 else 2.0 * N * Dp * Cp
@@ -217,12 +219,13 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "device_ms_per_step_p10_p50_p90": [round(float(np.percentile(step_dev, q)), 4) for q in (10, 50, 90)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": wl.dtype,
         "data": "synthetic (seeded; x,dy ~ N(0,1), w ~ N(0,1/C)%s)" % (
-            ", 1%% rows x16" if wl.hot_rows_frac else ""),
+            ", %g%% of rows x%g" % (100 * wl.hot_rows_frac, wl.hot_rows_scale) if wl.hot_rows_frac else ""),
         "config": {"workload": wl.name, "T": T, "N": N, "C": Cp * T, "D": Dp * T,
                    "step": "pack(fwd)+pack(bwd_x)+fwd+bwd_x+bwd_w"},
         "passes": passes,
