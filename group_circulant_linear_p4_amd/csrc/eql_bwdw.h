@@ -86,9 +86,11 @@ __global__ void __launch_bounds__(256) eql_spec_kernel(const SpecArgs a) {
 #pragma unroll
     for (int p = 0; p < T; ++p) pl[p][e] = o[p];
   }
+  // Non-temporal: the spectra are read back by the GEMMs only after the whole
+  // transform, long after they would have left the caches.
   u32x4* out = static_cast<u32x4*>(a.out) + ((size_t)kg * T * 2 + half) * a.Kpad + k;
 #pragma unroll
-  for (int p = 0; p < T; ++p) out[(size_t)p * 2 * a.Kpad] = E::pack(pl[p]);
+  for (int p = 0; p < T; ++p) __builtin_nontemporal_store(E::pack(pl[p]), &out[(size_t)p * 2 * a.Kpad]);
 }
 
 template <int T, typename Elt, bool PAIR, int DB, int CB>

@@ -17,6 +17,9 @@ __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (0x7 << 4));
 }
 
+// Cache-policy operand of a buffer store: NT (non-temporal) on gfx940-family parts.
+constexpr int kStoreNT = 2;
+
 #if defined(__HIP_DEVICE_COMPILE__)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -24,7 +27,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 // Stores the T values of one group (rounded to Elt) at byte offset `off` of buffer
 // `r`; accesses at or beyond the buffer's range are dropped by the hardware, so the
-// caller masks rows and columns through the offset instead of a branch.
+// caller masks rows and columns through the offset instead of a branch.  The stores
+// are non-temporal (cache policy NT): outputs are written once and not read again
+// by the kernel, and streaming them past the caches leaves L2 to the operands.
 template <int T, typename Elt>
 __device__ __forceinline__ void store_group_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, const float (&v)[T]) {
   constexpr int BYTES = T * (int)sizeof(Elt);
@@ -47,15 +52,15 @@ __device__ __forceinline__ void store_group_buf(__amdgpu_buffer_rsrc_t r, uint32
         __builtin_amdgcn_raw_buffer_store_b128((u32x4){w[b / 4], w[b / 4 + 1], w[b / 4 + 2], w[b / 4 + 3]}, r,
                                                off + b, 0, 0);
       } else if constexpr (W == 8) {
-        __builtin_amdgcn_raw_buffer_store_b64((u32x2){w[b / 4], w[b / 4 + 1]}, r, off + b, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64((u32x2){w[b / 4], w[b / 4 + 1]}, r, off + b, 0, kStoreNT);
       } else {
-        __builtin_amdgcn_raw_buffer_store_b32(w[b / 4], r, off + b, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(w[b / 4], r, off + b, 0, kStoreNT);
       }
     }
   } else {
 #pragma unroll
     for (int e = 0; e < T; ++e)
-      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (Elt)v[e]), r, off + 2 * e, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (Elt)v[e]), r, off + 2 * e, 0, kStoreNT);
   }
 }
 #endif
