@@ -128,7 +128,8 @@ int eqlinear_bwd_x(const void* dy, const void* w_packed_bwdx, void* dx, int64_t 
  * arguments (0 when N == 0 or the arguments are invalid).  The workspace holds the
  * half spectra of dy and x (each about the size of that tensor: T real planes per
  * channel, rows padded to a multiple of 2 * 16 / sizeof(element), channels to a
- * multiple of 256) followed by fp32 partial spectra of the gradient: whole
+ * multiple of the GEMM tile width: 256, or 64 where padding to 256 would add more
+ * than a third of the channels) followed by fp32 partial spectra of the gradient: whole
  * Dp x Cp planes, one set per row range of the reduction over N (the real
  * frequencies and the complex pairs are split separately).
  */
