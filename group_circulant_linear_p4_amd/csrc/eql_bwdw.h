@@ -82,7 +82,7 @@ __global__ void __launch_bounds__(256) eql_spec_kernel(const SpecArgs a) {
 #pragma unroll
       for (int h = 0; h < T; ++h) v[h] = 0.0f;
     }
-    Dft<T, false>::run(v, o, a.tw);
+    Dft<T>::run(v, o, a.tw);
 #pragma unroll
     for (int p = 0; p < T; ++p) pl[p][e] = o[p];
   }

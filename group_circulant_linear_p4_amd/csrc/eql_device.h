@@ -7,9 +7,10 @@
 //   p = 0                    k = 0       sum_h v_h
 //   p = 1 (even T > 1)       k = T/2     sum_h (-1)^h v_h
 //   p = NR + 2q, NR + 2q + 1 k = q + 1   Re / Im of sum_h v_h exp(-2 pi i h k / T)
-// where NR is the number of real planes.  Activations may carry a per-plane scale
-// sigma_p (p4 uses 1/2 on its two real planes, which keeps |X_p| <= 2 max|x| and
-// makes every transform coefficient 0, +-1 or +-1/2).
+// where NR is the number of real planes.  The packed weight of the forward and
+// input-gradient kernels carries the inverse transform's scale (1/T on the real
+// planes, 2/T on the complex ones), so neither the activation transform nor the
+// epilogue's inverse multiplies by it; for p4 every coefficient left is 0 or +-1.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -59,11 +60,9 @@ __device__ __forceinline__ float mac_msin(float s, float v, int m, const Twiddle
 }
 
 // ---------------------------------------------------------------------------
-// Forward group transform of one length-T vector into T planes.
-// kScaled selects the activation scaling (p4: 1/2 on the real planes); weights are
-// always transformed unscaled.
+// Forward group transform of one length-T vector into T (unscaled) planes.
 // ---------------------------------------------------------------------------
-template <int T, bool kScaled>
+template <int T>
 struct Dft {
   static __device__ __forceinline__ void run(const float (&v)[T], float (&out)[T],
                                              const Twiddles& tw) {
@@ -83,18 +82,13 @@ struct Dft {
 // p4: butterflies only.  The additions are ordered so that a cyclic shift of v
 // permutes / negates the outputs exactly in floating point:
 //   shift by one maps (X0, X2, Xr, Xi) to (X0, -X2, Xi, -Xr).
-template <bool kScaled>
-struct Dft<4, kScaled> {
+template <>
+struct Dft<4> {
   static __device__ __forceinline__ void run(const float (&v)[4], float (&out)[4], const Twiddles&) {
     const float s02 = v[0] + v[2], d02 = v[0] - v[2];
     const float s13 = v[1] + v[3], d13 = v[3] - v[1];
-    if (kScaled) {
-      out[0] = 0.5f * (s02 + s13);
-      out[1] = 0.5f * (s02 - s13);
-    } else {
-      out[0] = s02 + s13;
-      out[1] = s02 - s13;
-    }
+    out[0] = s02 + s13;
+    out[1] = s02 - s13;
     out[2] = d02;
     out[3] = d13;
   }
@@ -102,11 +96,11 @@ struct Dft<4, kScaled> {
 
 // ---------------------------------------------------------------------------
 // Inverse transform of T planes back to T group values.
-// kPlain = true, and every T != 4: the plain inverse of unscaled planes,
+// kPlain = true: the plain inverse of unscaled planes,
 //   y_g = (1/T) (P0 + (-1)^g P_N + 2 sum_k (cos P_re - sin P_im)).
-// kPlain = false with T = 4: the forward / input-gradient epilogue, whose real
-// planes carry an extra 1/2 (from the packed weight), making every coefficient
-// +-1/2.
+// kPlain = false: the forward / input-gradient epilogue, whose planes already
+// carry 1/T (real) and 2/T (complex) from the packed weight,
+//   y_g = P0 + (-1)^g P_N + sum_k (cos P_re - sin P_im).
 // ---------------------------------------------------------------------------
 template <int T, bool kPlain>
 struct Idft {
@@ -122,24 +116,10 @@ struct Idft {
         u = mac_cos<T>(u, P[NR + 2 * q], g * (q + 1), tw);
         u = mac_msin<T>(u, P[NR + 2 * q + 1], g * (q + 1), tw);
       }
-      y[g] = (s + 2.0f * u) * tw.inv_t;
+      y[g] = kPlain ? (s + 2.0f * u) * tw.inv_t : s + u;
     }
   }
 };
-
-// p4 forward / input-gradient inverse.  With the real planes carrying 1/2 every
-// coefficient is +-1/2:  y = 1/2 ((P0 +- P2) +- Pr / Pi).
-template <>
-struct Idft<4, false> {
-  static __device__ __forceinline__ void run(const float (&P)[4], float (&y)[4], const Twiddles&) {
-    const float a = P[0] + P[1], b = P[0] - P[1];
-    y[0] = 0.5f * (a + P[2]);
-    y[1] = 0.5f * (b - P[3]);
-    y[2] = 0.5f * (a - P[2]);
-    y[3] = 0.5f * (b + P[3]);
-  }
-};
-
 
 // ---------------------------------------------------------------------------
 // Element types.  A "unit" is 16 bytes: 8 fp16 or 4 fp32 values.
@@ -165,6 +145,16 @@ struct EltT<_Float16> {
     acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                  __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
   }
+  // Clear a 32x32 tile with one MFMA of zero operands (exact +0).  The zero operand
+  // comes from a volatile move, so separate tiles get separate MFMAs: a constant
+  // would be rematerialised as 16 register writes per tile (and, as generated,
+  // twice).
+  static __device__ __forceinline__ void zero(f32x16& acc) {
+    uint32_t z0;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z0));
+    const f16x8 z = __builtin_bit_cast(f16x8, (u32x4){z0, z0, z0, z0});
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(z, z, (f32x16){}, 0, 0, 0);
+  }
 };
 
 template <>
@@ -185,6 +175,11 @@ struct EltT<float> {
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(af[1], bf[1], acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(af[2], bf[2], acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(af[3], bf[3], acc, 0, 0, 0);
+  }
+  static __device__ __forceinline__ void zero(f32x16& acc) {  // see EltT<_Float16>::zero
+    float z0;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z0));
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(z0, z0, (f32x16){}, 0, 0, 0);
   }
 };
 

@@ -40,8 +40,9 @@ __device__ __forceinline__ void store_group_buf(__amdgpu_buffer_rsrc_t r, uint32
 #pragma unroll
     for (int i = 0; i < WORDS; ++i) {
       if constexpr (sizeof(Elt) == 2) {
-        const _Float16 lo = (_Float16)v[2 * i], hi = (_Float16)v[2 * i + 1];
-        w[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        const h2 pr = {(_Float16)v[2 * i], (_Float16)v[2 * i + 1]};  // one packed RNE convert
+        w[i] = __builtin_bit_cast(uint32_t, pr);
       } else {
         w[i] = __builtin_bit_cast(uint32_t, v[i]);
       }
@@ -50,7 +51,7 @@ __device__ __forceinline__ void store_group_buf(__amdgpu_buffer_rsrc_t r, uint32
     for (int b = 0; b < BYTES; b += W) {
       if constexpr (W == 16) {
         __builtin_amdgcn_raw_buffer_store_b128((u32x4){w[b / 4], w[b / 4 + 1], w[b / 4 + 2], w[b / 4 + 3]}, r,
-                                               off + b, 0, 0);
+                                               off + b, 0, kStoreNT);
       } else if constexpr (W == 8) {
         __builtin_amdgcn_raw_buffer_store_b64((u32x2){w[b / 4], w[b / 4 + 1]}, r, off + b, 0, kStoreNT);
       } else {

@@ -154,9 +154,13 @@ __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
   const int myTiles = (a.numTiles - b0 + grid - 1) / grid;
   const int nst = a.Jpad / JC;
 
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lrow = lane & 31, khalf = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  // Lane-derived values are re-derived after every epilogue from a lane index the
+  // compiler cannot hoist, so none of them (LDS addresses, DMA offsets) is live in
+  // the epilogue, where every register is taken: a spill there would make the
+  // compiler drain all outstanding loads at its reload.
+  int lane = lane_index();
+  int lrow = lane & 31, khalf = lane >> 5;
   const uint32_t rowBytes = (uint32_t)a.Cin * T * ELT;
   const uint32_t colStride = (uint32_t)a.Jpad * T * 16u;  // packed bytes per output channel
 
@@ -173,29 +177,32 @@ __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
   // to the stage's first byte in output channel col0; channels past D' fall
   // outside the descriptor and read zero.
   uint32_t bOff[IPW];
-#pragma unroll
-  for (int i = 0; i < IPW; ++i) {
-    const int P = (wave * IPW + i) * 64 + lane;
-    const int o = P / RP, pos = P - o * RP;
-    const int r = pos ^ ring_swz<RP>(o);
-    const int rr = r < R ? r : 0;  // padding positions load an arbitrary unit
-    bOff[i] = (uint32_t)o * colStride + (uint32_t)rr * 16u;
-  }
-  // x ring (each wave loads and reads only its own 32 rows): position
-  // P = wave*32*RP + i*64 + lane holds unit u = (P % RP) ^ ring_swz(row) of row
-  // P / RP; unit u of a stage is bytes [16u, 16u+16) of the row's JC*G channels.
-  // Rows past N fall outside the descriptor and read zero.
   uint32_t xOff[IPWX > 0 ? IPWX : 1];
   int xCh[IPWX > 0 ? IPWX : 1];
+  auto lane_offsets = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int i = 0; i < IPWX; ++i) {
-    const int P = wave * 32 * RP + i * 64 + lane;
-    const int row = P / RP, pos = P - row * RP;
-    const int u = pos ^ ring_swz<RP>(row);
-    const int uu = u < R ? u : 0;
-    xOff[i] = (uint32_t)row * rowBytes + (uint32_t)uu * 16u;
-    xCh[i] = (uu * 16) / (T * ELT);  // channel (within the stage) of the unit's first element
-  }
+    for (int i = 0; i < IPW; ++i) {
+      const int P = (wave * IPW + i) * 64 + lane;
+      const int o = P / RP, pos = P - o * RP;
+      const int r = pos ^ ring_swz<RP>(o);
+      const int rr = r < R ? r : 0;  // padding positions load an arbitrary unit
+      bOff[i] = (uint32_t)o * colStride + (uint32_t)rr * 16u;
+    }
+    // x ring (each wave loads and reads only its own 32 rows): position
+    // P = wave*32*RP + i*64 + lane holds unit u = (P % RP) ^ ring_swz(row) of row
+    // P / RP; unit u of a stage is bytes [16u, 16u+16) of the row's JC*G channels.
+    // Rows past N fall outside the descriptor and read zero.
+#pragma unroll
+    for (int i = 0; i < IPWX; ++i) {
+      const int P = wave * 32 * RP + i * 64 + lane;
+      const int row = P / RP, pos = P - row * RP;
+      const int u = pos ^ ring_swz<RP>(row);
+      const int uu = u < R ? u : 0;
+      xOff[i] = (uint32_t)row * rowBytes + (uint32_t)uu * 16u;
+      xCh[i] = (uu * 16) / (T * ELT);  // channel (within the stage) of the unit's first element
+    }
+  };
+  lane_offsets();
 
   // Stage g of the stream = stage st of this workgroup's tile k (g = k*nst + st).
   // Every stage issues the same loads; past the stream they have an empty range
@@ -334,7 +341,7 @@ __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
             v[h] = __builtin_bit_cast(float, raw[s][i]);
           }
         }
-        Dft<T, false>::run(v, o, a.tw);
+        Dft<T>::run(v, o, a.tw);
 #pragma unroll
         for (int p = 0; p < T; ++p) pl[p][e] = o[p];
       }
@@ -346,13 +353,18 @@ __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
   };
 
   f32x16 acc[T][NB];
+  // Clearing at the top of each tile.  Up to T = 6 each 32x32 tile is cleared by one
+  // MFMA of zero operands; written as constants the clearing is emitted as two
+  // register writes per accumulator.  From T = 7 on, the MFMA form leaves the
+  // register allocator short and it spills, so the constant form is kept there.
   auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int p = 0; p < T; ++p)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[p][nb][r] = 0.0f;
+      for (int nb = 0; nb < NB; ++nb) {
+        if constexpr (T <= 6) E::zero(acc[p][nb]);
+        else acc[p][nb] = (f32x16){};
+      }
   };
 
   auto load_bfrag = [&](u32x4 (&bf)[T], const u32x4* slot, int s, int nb) __attribute__((always_inline)) {
@@ -418,7 +430,6 @@ __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
   // stages g+2 .. g+DIST-1: WAIT_TOP of them may still be outstanding.  Register
   // path: x stage g+1 is loaded at the top of stage g, before the weight loads, and
   // waited for (all but the IPW weight loads behind it).
-  zero_acc();
 #pragma unroll
   for (int j = 0; j < DIST; ++j) issue_stage(j);
   if constexpr (XLDS) {
@@ -467,12 +478,16 @@ __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
   // so every tile starts on fragment buffer 0.
   int g = 0;
   for (int k = 0; k < myTiles; ++k) {
+    zero_acc();
     for (int st = 0; st < nst; st += 2, g += 2) {
       stage(g, I0{});
       stage(g + 1, I1{});
     }
     epilogue(k);
-    zero_acc();
+    lane = lane_index();
+    lrow = lane & 31;
+    khalf = lane >> 5;
+    lane_offsets();
   }
   // Drain the look-ahead loads (all out of range) before the workgroup's LDS can
   // be reused.

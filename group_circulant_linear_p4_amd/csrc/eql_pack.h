@@ -4,8 +4,8 @@
 //
 // One thread per (out, in) pair of the packed matrix (plus the zero padding of the
 // input axis up to the padded group count).  It reads the T shared parameters,
-// transforms them in fp32 (p4: butterflies only) and rounds each plane once to
-// the element type.  In the input-gradient mode the weight is the transposed,
+// transforms them in fp32 (p4: butterflies only), divides each plane by its share
+// of the inverse transform's scale and rounds it once to the element type.  In the input-gradient mode the weight is the transposed,
 // group-reversed w~[c][d][t] = w[d][c][(-t) mod T]; its spectrum is the conjugate,
 // so the Im planes change sign.
 #pragma once
@@ -38,13 +38,12 @@ __global__ void __launch_bounds__(256) eql_pack_kernel(const PackArgs a) {
     const int c = a.transposed ? o : i;
     float v[T];
     load_group<T, Elt>(static_cast<const Elt*>(a.w) + ((size_t)d * a.Cp + c) * T, v);
-    Dft<T, false>::run(v, pl, a.tw);
-    if constexpr (T == 4) {
-      // p4: the 1/2 of the forward transform's real planes lives in the weight
-      // (exact: a power of two), so the activation transform is adds only.
-      pl[0] *= 0.5f;
-      pl[1] *= 0.5f;
-    }
+    Dft<T>::run(v, pl, a.tw);
+    // The inverse transform's scale lives in the weight: 1/T on the real planes,
+    // 2/T on the complex ones (one correctly rounded division; exact for
+    // power-of-two T), so the kernels that consume the packing multiply by nothing.
+#pragma unroll
+    for (int p = 0; p < T; ++p) pl[p] = (p < NR ? pl[p] : 2.0f * pl[p]) / (float)T;
     if (a.transposed) {
 #pragma unroll
       for (int p = NR + 1; p < T; p += 2) pl[p] = -pl[p];

@@ -77,9 +77,11 @@ typedef enum {
  *   then for k = 1 .. ceil(T/2)-1, two planes:
  *                               sum_t w_t cos(2 pi t k / T)          (Re)
  *                              -sum_t w_t sin(2 pi t k / T)          (Im)
- * For T = 4 the two real planes (k = 0 and k = 2) are stored multiplied by 1/2:
- * the p4 transform's halving is carried by the weight, so the activations'
- * transform needs only additions and subtractions (the scale is exact).
+ * Each plane is stored divided by its share of the inverse transform's scale:
+ * the real planes (k = 0, k = T/2) by T, the Re / Im planes by T/2 (one correctly
+ * rounded fp32 division, exact for power-of-two T outside the subnormal range of
+ * `dtype`).  The kernels that consume the packing then neither scale the
+ * activations' transform nor the inverse; for p4 both are additions only.
  * In EQL_PACK_BWDX mode the weight is w~[c][d][t] = w[d][c][(-t) mod T]
  * (out = c, in = d), whose spectrum is the complex conjugate: the Im planes
  * change sign.

@@ -180,8 +180,8 @@ def unpack(buf, out_ch, in_ch, T, dtype):
     assert np.all(planes[:, in_ch:, :] == 0)
     planes = planes[:, :in_ch, :]
     nr = 2 if (T % 2 == 0 and T > 1) else 1
-    if T == 4:
-        planes[:, :, :2] *= 2.0                    # p4 real planes are stored halved
+    planes[:, :, :nr] *= T                         # stored with the inverse's 1/T ...
+    planes[:, :, nr:] *= T / 2.0                   # ... and 2/T on the complex planes
     spec = np.zeros((out_ch, in_ch, T // 2 + 1), dtype=np.complex128)
     spec[:, :, 0] = planes[:, :, 0]
     if nr == 2:
