@@ -19,14 +19,16 @@ import ctypes
 import os
 
 __all__ = [
-    "EQL_F32", "EQL_F16", "EQL_PACK_FWD", "EQL_PACK_BWDX", "EQL_MAX_T", "EqlError",
+    "EQL_F32", "EQL_F16", "EQL_PACK_FWD", "EQL_PACK_BWDX", "EQL_ACT_NONE", "EQL_ACT_GELU", "EQL_MAX_T",
+    "EqlError",
     "lib", "library_path", "eqlinear_abi_version", "eqlinear_status_string",
-    "eqlinear_packed_weight_bytes", "eqlinear_pack_weight", "eqlinear_fwd", "eqlinear_bwd_x",
+    "eqlinear_packed_weight_bytes", "eqlinear_pack_weight", "eqlinear_fwd", "eqlinear_fwd_fused", "eqlinear_bwd_x",
     "eqlinear_bwd_w_workspace_bytes", "eqlinear_bwd_w",
 ]
 
 EQL_F32, EQL_F16 = 0, 1
 EQL_PACK_FWD, EQL_PACK_BWDX = 0, 1
+EQL_ACT_NONE, EQL_ACT_GELU = 0, 1
 EQL_MAX_T = 16
 EQL_OK, EQL_EINVAL, EQL_EALIGN, EQL_EUNSUPPORTED, EQL_EHIP = 0, 1, 2, 3, 4
 
@@ -62,6 +64,8 @@ def lib() -> ctypes.CDLL:
         L.eqlinear_pack_weight.restype = i32
         L.eqlinear_fwd.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, vp]
         L.eqlinear_fwd.restype = i32
+        L.eqlinear_fwd_fused.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp]
+        L.eqlinear_fwd_fused.restype = i32
         L.eqlinear_bwd_x.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, vp]
         L.eqlinear_bwd_x.restype = i32
         L.eqlinear_bwd_w_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
@@ -132,6 +136,13 @@ def eqlinear_pack_weight(w, w_packed, Dp: int, Cp: int, T: int, dtype, mode: int
 def eqlinear_fwd(x, w_packed, y, N: int, Cp: int, Dp: int, T: int, dtype, stream=None) -> None:
     _check(lib().eqlinear_fwd(_ptr(x), _ptr(w_packed), _ptr(y), N, Cp, Dp, T, _dtype(dtype), _stream(stream)),
            "eqlinear_fwd")
+
+
+def eqlinear_fwd_fused(x, w_packed, bias, residual, y, N: int, Cp: int, Dp: int, T: int, dtype, act: int,
+                       stream=None) -> None:
+    """bias / residual may be None; residual may be y itself."""
+    _check(lib().eqlinear_fwd_fused(_ptr(x), _ptr(w_packed), _ptr(bias), _ptr(residual), _ptr(y), N, Cp, Dp, T,
+                                    _dtype(dtype), int(act), _stream(stream)), "eqlinear_fwd_fused")
 
 
 def eqlinear_bwd_x(dy, w_packed_bwdx, dx, N: int, Cp: int, Dp: int, T: int, dtype, stream=None) -> None:

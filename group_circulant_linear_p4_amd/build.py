@@ -26,6 +26,8 @@ SOURCES = [
     "eql_pack.hip",
     "eql_fwd_f16.hip",
     "eql_fwd_f32.hip",
+    "eql_fwd_fused_f16.hip",
+    "eql_fwd_fused_f32.hip",
     "eql_bwdw_f16.hip",
     "eql_bwdw_f32.hip",
     "eql_bwdw_real_f16.hip",

@@ -70,8 +70,10 @@ int device_cus() {
 
 // Shared by the forward pass and the input gradient: out = in * W^T for the packed
 // weight with (out, in) channel counts (Dout, Cin).
+// epi: the fused epilogue (bias, act, res); otherwise those are ignored.
 int run_fwd(const void* x, const void* wp, void* y, int64_t N, int64_t Cin, int64_t Dout, int T,
-            int dtype, void* stream) {
+            int dtype, void* stream, bool epi = false, const void* bias = nullptr, const void* res = nullptr,
+            int act = 0) {
   int st = check_sizes(N, Cin, Dout, T, dtype);
   if (st != EQL_OK) return st;
   if (N == 0) return EQL_OK;
@@ -98,6 +100,8 @@ int run_fwd(const void* x, const void* wp, void* y, int64_t N, int64_t Cin, int6
   a.loadMode = !rowsAligned ? kLoadNarrow
                : (Cin % ((int64_t)kPackGroupAlign * group_channels(dtype)) == 0 ? kLoadFull : kLoadAligned);
   a.tw = make_twiddles(T);
+  a.bias = bias;
+  a.act = act;
 
   const int cus = device_cus();
   // Rows in pieces small enough for the tile indices.
@@ -108,11 +112,14 @@ int run_fwd(const void* x, const void* wp, void* y, int64_t N, int64_t Cin, int6
     const int64_t rows = N - r0 < maxRows ? N - r0 : maxRows;
     a.x = static_cast<const char*>(x) + (size_t)r0 * inRow;
     a.y = static_cast<char*>(y) + (size_t)r0 * outRow;
+    a.res = res ? static_cast<const char*>(res) + (size_t)r0 * outRow : nullptr;
     a.N = (int)rows;
     a.numTiles = (int)(ceil_div(rows, kFwdRows) * colTiles);
     const unsigned grid = (unsigned)std::min<int64_t>(a.numTiles, cus);
-    const hipError_t e = dtype == EQL_F16 ? launch_fwd_f16(T, nb, a, grid, s)
-                                          : launch_fwd_f32(T, nb, a, grid, s);
+    const hipError_t e = epi ? (dtype == EQL_F16 ? launch_fwd_fused_f16(T, nb, a, grid, s)
+                                                 : launch_fwd_fused_f32(T, nb, a, grid, s))
+                             : (dtype == EQL_F16 ? launch_fwd_f16(T, nb, a, grid, s)
+                                                 : launch_fwd_f32(T, nb, a, grid, s));
     if (e != hipSuccess) return EQL_EHIP;
   }
   return EQL_OK;
@@ -188,7 +195,7 @@ BwdwPlan plan_bwdw(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype) {
 
 extern "C" {
 
-int eqlinear_abi_version(void) { return 100; }
+int eqlinear_abi_version(void) { return 101; }
 
 const char* eqlinear_status_string(int status) {
   switch (status) {
@@ -234,6 +241,17 @@ int eqlinear_pack_weight(const void* w, void* w_packed, int64_t Dp, int64_t Cp, 
 int eqlinear_fwd(const void* x, const void* w_packed, void* y, int64_t N, int64_t Cp, int64_t Dp,
                  int T, int dtype, void* stream) {
   return run_fwd(x, w_packed, y, N, Cp, Dp, T, dtype, stream);
+}
+
+int eqlinear_fwd_fused(const void* x, const void* w_packed, const void* bias, const void* residual,
+                       void* y, int64_t N, int64_t Cp, int64_t Dp, int T, int dtype, int act, void* stream) {
+  if (act != EQL_ACT_NONE && act != EQL_ACT_GELU) return EQL_EINVAL;
+  int st = check_sizes(N, Cp, Dp, T, dtype);
+  if (st != EQL_OK) return st;
+  if (N == 0) return EQL_OK;
+  if (bias && (reinterpret_cast<uintptr_t>(bias) % (uintptr_t)elt_bytes(dtype)) != 0) return EQL_EALIGN;
+  if (residual && !aligned16(residual)) return EQL_EALIGN;
+  return run_fwd(x, w_packed, y, N, Cp, Dp, T, dtype, stream, true, bias, residual, act);
 }
 
 int eqlinear_bwd_x(const void* dy, const void* w_packed_bwdx, void* dx, int64_t N, int64_t Cp,

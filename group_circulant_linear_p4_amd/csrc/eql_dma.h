@@ -64,6 +64,55 @@ __device__ __forceinline__ void store_group_buf(__amdgpu_buffer_rsrc_t r, uint32
       __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (Elt)v[e]), r, off + 2 * e, 0, kStoreNT);
   }
 }
+
+// Raw 32-bit words of one group (the counterpart of store_group_buf): T * size
+// bytes in the widest aligned loads; with 2-byte loads, one value per word.
+// Out-of-range accesses read zero.
+template <int T, typename Elt>
+__host__ __device__ constexpr int group_words() {
+  return pow2_part(T * (int)sizeof(Elt)) >= 4 ? T * (int)sizeof(Elt) / 4 : T;
+}
+
+template <int T, typename Elt>
+__device__ __forceinline__ void load_group_raw(__amdgpu_buffer_rsrc_t r, uint32_t off,
+                                               uint32_t (&w)[group_words<T, Elt>()]) {
+  constexpr int BYTES = T * (int)sizeof(Elt);
+  constexpr int W = pow2_part(BYTES);
+  if constexpr (W >= 4) {
+#pragma unroll
+    for (int b = 0; b < BYTES; b += W) {
+      if constexpr (W == 16) {
+        const u32x4 q = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off + b, 0, 0));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[b / 4 + i] = q[i];
+      } else if constexpr (W == 8) {
+        const u32x2 q = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off + b, 0, 0));
+        w[b / 4] = q[0];
+        w[b / 4 + 1] = q[1];
+      } else {
+        w[b / 4] = __builtin_amdgcn_raw_buffer_load_b32(r, off + b, 0, 0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < T; ++e) w[e] = __builtin_amdgcn_raw_buffer_load_b16(r, off + 2 * e, 0, 0);
+  }
+}
+
+template <int T, typename Elt>
+__device__ __forceinline__ void group_from_raw(const uint32_t (&w)[group_words<T, Elt>()], float (&v)[T]) {
+  constexpr bool kWords = pow2_part(T * (int)sizeof(Elt)) >= 4;
+#pragma unroll
+  for (int e = 0; e < T; ++e) {
+    if constexpr (sizeof(Elt) == 4) {
+      v[e] = __builtin_bit_cast(float, w[e]);
+    } else if constexpr (kWords) {
+      v[e] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[e / 2] >> ((e & 1) * 16)));
+    } else {
+      v[e] = (float)__builtin_bit_cast(_Float16, (uint16_t)w[e]);
+    }
+  }
+}
 #endif
 
 // Offsets at or beyond this value are outside every buffer: the load returns zero.

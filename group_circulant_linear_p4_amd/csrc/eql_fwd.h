@@ -44,6 +44,10 @@ struct FwdArgs {
   int N, Cin, Dout, Jpad, colTiles, numTiles, loadMode;
   uint32_t wpBytes;  // size of the packed weight in bytes (< 2^32)
   Twiddles tw;
+  // Fused epilogue (EPI = 1 instantiations only): y = act(x W^T + bias) + res.
+  const void* bias;  // [Dout] or null
+  const void* res;   // [N][Dout*T] or null (may equal y)
+  int act;           // 0 none, 1 GELU
 };
 
 constexpr int kFwdRows = 128;   // rows per workgroup (4 waves x 32)
@@ -107,7 +111,34 @@ __device__ __forceinline__ int ring_swz(int o) {
   else return o & 15;
 }
 
-template <int T, typename Elt, int NB, int JC, int LOAD>
+// Largest power of two <= v (v >= 1).
+constexpr int floor_pow2(int v) { return v >= 16 ? 16 : v >= 8 ? 8 : v >= 4 ? 4 : v >= 2 ? 2 : 1; }
+
+// erf by formula 7.1.26 of Abramowitz and Stegun, Handbook of Mathematical
+// Functions (|error| <= 1.5e-7 for the formula itself):
+//   erf(a) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-a^2),
+//   t = 1 / (1 + p a), a = |u|, extended as an odd function.
+// The reciprocal and exp2 are the hardware approximations (about 1 ulp).
+__device__ __forceinline__ float erf_as(float u) {
+  const float a = __builtin_fabsf(u);
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, a, 1.0f));
+  float q = __builtin_fmaf(1.061405429f, t, -1.453152027f);
+  q = __builtin_fmaf(q, t, 1.421413741f);
+  q = __builtin_fmaf(q, t, -0.284496736f);
+  q = __builtin_fmaf(q, t, 0.254829592f);
+  const float e = __builtin_amdgcn_exp2f((-1.4426950408889634f * a) * a);  // exp(-a^2)
+  return __builtin_copysignf(__builtin_fmaf(-q * t, e, 1.0f), u);
+}
+
+// GELU in its exact form, v * Phi(v) = v/2 (1 + erf(v / sqrt 2)), in fp32.
+__device__ __forceinline__ float gelu_erf(float v) {
+  const float h = 0.5f * v;
+  return __builtin_fmaf(h, erf_as(v * 0.7071067811865475f), h);
+}
+
+// EPI = 1: the epilogue adds the per-channel bias, applies the activation and adds
+// the residual (all in fp32) before the single rounding to Elt.
+template <int T, typename Elt, int NB, int JC, int LOAD, int EPI>
 __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
   // The body uses AMDGPU-only types (buffer resources); the host pass only needs
   // the kernel's signature to emit its launch stub.
@@ -403,17 +434,58 @@ __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
     // loop, where every register is taken.
     const int ln = lane_index();
     const uint32_t laneOff = (uint32_t)(wave * 32 + 4 * (ln >> 5)) * outRow;
+    // Fused epilogue operands: an absent bias or residual gets an empty range, so
+    // its loads read zero.
+    const __amdgpu_buffer_rsrc_t br = make_rsrc(a.bias, EPI && a.bias ? (uint32_t)a.Dout * ELT : 0u);
+    const __amdgpu_buffer_rsrc_t rr =
+        make_rsrc(EPI && a.res ? static_cast<const char*>(a.res) + (size_t)row0 * outRow : nullptr,
+                  EPI && a.res ? rows * outRow : 0u);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int col = col0 + nb * 32 + (ln & 31);
       const uint32_t cOff = col < a.Dout ? laneOff + (uint32_t)col * T * ELT : kOob;
+      float bv = 0.0f;
+      if constexpr (EPI) {
+        uint32_t b1[1];
+        load_group_raw<1, Elt>(br, col < a.Dout ? (uint32_t)col * ELT : kOob, b1);
+        float bf1[1];
+        group_from_raw<1, Elt>(b1, bf1);
+        bv = bf1[0];
+      }
+      // Fused epilogue: the residual groups of a chunk are loaded before any of its
+      // stores (the compiler may not move a load above a store to y, which the
+      // residual may alias), so one wait covers the chunk.
+      constexpr int RW = group_words<T, Elt>();
+      constexpr int CH = EPI ? floor_pow2(32 / RW < 1 ? 1 : (32 / RW > 16 ? 16 : 32 / RW)) : 16;
+      static_assert(16 % CH == 0, "chunks must tile the 16 accumulator slots");
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float P[T], yv[T];
+      for (int r0 = 0; r0 < 16; r0 += CH) {
+        uint32_t rw[CH][RW];
+        if constexpr (EPI) {
 #pragma unroll
-        for (int p = 0; p < T; ++p) P[p] = acc[p][nb][r];
-        Idft<T, false>::run(P, yv, a.tw);
-        store_group_buf<T, Elt>(yr, cOff + (uint32_t)(8 * (r >> 2) + (r & 3)) * outRow, yv);
+          for (int j = 0; j < CH; ++j)
+            load_group_raw<T, Elt>(rr, cOff + (uint32_t)(8 * ((r0 + j) >> 2) + ((r0 + j) & 3)) * outRow, rw[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+          const int r = r0 + j;
+          float P[T], yv[T];
+#pragma unroll
+          for (int p = 0; p < T; ++p) P[p] = acc[p][nb][r];
+          Idft<T, false>::run(P, yv, a.tw);
+          const uint32_t off = cOff + (uint32_t)(8 * (r >> 2) + (r & 3)) * outRow;
+          if constexpr (EPI) {
+            float rv[T];
+            group_from_raw<T, Elt>(rw[j], rv);
+#pragma unroll
+            for (int g = 0; g < T; ++g) {
+              float v = yv[g] + bv;
+              if (a.act == 1) v = gelu_erf(v);
+              yv[g] = v + rv[g];
+            }
+          }
+          store_group_buf<T, Elt>(yr, off, yv);
+        }
       }
     }
   };

@@ -24,6 +24,8 @@ static_assert(kPackGroupAlign % fwd_jc(1) == 0 && kPackGroupAlign % fwd_jc(16) =
 // elt: 2 = fp16, 4 = fp32.  Each returns the launch status.
 hipError_t launch_fwd_f16(int T, int NB, const FwdArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_fwd_f32(int T, int NB, const FwdArgs& a, unsigned grid, hipStream_t s);
+hipError_t launch_fwd_fused_f16(int T, int NB, const FwdArgs& a, unsigned grid, hipStream_t s);
+hipError_t launch_fwd_fused_f32(int T, int NB, const FwdArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_spec_f16(int T, const SpecArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_spec_f32(int T, const SpecArgs& a, unsigned grid, hipStream_t s);
 // Weight-gradient GEMMs: the real planes' (DB, CB in {4, 1}) and the complex pairs'

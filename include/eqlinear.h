@@ -52,6 +52,12 @@ extern "C" {
 
 typedef enum { EQL_F32 = 0, EQL_F16 = 1 } eql_dtype;
 
+/* Activation of eqlinear_fwd_fused. */
+typedef enum {
+    EQL_ACT_NONE = 0,
+    EQL_ACT_GELU = 1    /* v * Phi(v), Phi the standard normal CDF (erf form) */
+} eql_act;
+
 typedef enum {
     EQL_PACK_FWD = 0,   /* spectrum of w, for eqlinear_fwd                     */
     EQL_PACK_BWDX = 1   /* spectrum of the transposed, group-reversed weight,   */
@@ -115,6 +121,27 @@ int eqlinear_pack_weight(const void* w, void* w_packed, int64_t Dp, int64_t Cp, 
  */
 int eqlinear_fwd(const void* x, const void* w_packed, void* y, int64_t N, int64_t Cp,
                  int64_t Dp, int T, int dtype, void* stream);
+
+/*
+ * Forward with the epilogue of the transformer MLP blocks the layer is built into
+ * ("Nivel de Rede": Flash EQ-ViT and Flash EQ-Swin), in the same single kernel:
+ *     y[n][d*T+g] = act( (x W^T)[n][d*T+g] + bias[d] ) + residual[n][d*T+g]
+ * x, w_packed, y, sizes and errors as eqlinear_fwd.
+ * bias: [Dp] elements of `dtype`, or NULL.  One value per output channel, shared
+ *   by its T group elements: a bias that varied over g would not commute with
+ *   the group action.  Aligned to its element size, else EQL_EALIGN.
+ * act: EQL_ACT_NONE or EQL_ACT_GELU; any other value is EQL_EINVAL.  Pointwise,
+ *   so it commutes with the group action.
+ * residual: [N][Dp*T] elements of `dtype`, or NULL; 16-byte aligned.  It may be
+ *   the same buffer as y (an in-place residual add); any other overlap with y is
+ *   undefined.
+ * The bias, the activation and the residual are applied in fp32 to the fp32
+ * result of the inverse transform; y is rounded once.  bias = residual = NULL
+ * with EQL_ACT_NONE gives exactly eqlinear_fwd's result.
+ */
+int eqlinear_fwd_fused(const void* x, const void* w_packed, const void* bias,
+                       const void* residual, void* y, int64_t N, int64_t Cp, int64_t Dp,
+                       int T, int dtype, int act, void* stream);
 
 /*
  * Input gradient: dx = dy W.  dy: [N][Dp*T] read; w_packed_bwdx: the

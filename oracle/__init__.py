@@ -9,6 +9,8 @@ from .eqlinear_oracle import (  # noqa: F401
     bwd_x,
     bwd_w,
     half_spectrum,
+    gelu,
+    fwd_fused,
     real_gemm_count,
     actual_flops,
     dense_equivalent_flops,

@@ -26,6 +26,9 @@ Functions:
   bwd_x(dy, w)         dx = dy W
   bwd_w(x, dy)         dw[d,c,t] = sum over tied entries of (dy^T x)
   half_spectrum(v)     DFT along the last axis, k = 0..floor(T/2)
+  gelu(v)              v * Phi(v), the exact (erf) form
+  fwd_fused(x, w, bias, residual, act)
+                       y = act(x W^T + bias broadcast over g) + residual
   real_gemm_count(T)   per-frequency real products after conjugate symmetry
 """
 from __future__ import annotations
@@ -101,6 +104,37 @@ def bwd_w(x, dy, T: int) -> np.ndarray:
         for h in range(T):
             dw[:, :, (g - h) % T] += G4[:, g, :, h]
     return dw
+
+
+def gelu(v) -> np.ndarray:
+    """GELU in its exact form: v * Phi(v) = v/2 * (1 + erf(v / sqrt 2)), with Phi the
+    standard normal distribution function (erf is the library routine)."""
+    from scipy.special import erf
+    v = _f64(v)
+    return 0.5 * v * (1.0 + erf(v / np.sqrt(2.0)))
+
+
+def fwd_fused(x, w, bias=None, residual=None, act: str = "none") -> np.ndarray:
+    """y = act(x W^T + b) + r: the layer inside the MLP blocks of the transformers
+    the pages build it into ("Nivel de Rede": Flash EQ-ViT, Flash EQ-Swin).
+
+    bias has one entry per output channel d and is shared by the channel's T group
+    elements (b_dense[d*T+g] = bias[d]); a bias that varied with g would not commute
+    with the group action.  act is "none" or "gelu" (pointwise).  residual has y's
+    shape and is added after the activation.  Readings where the pages are silent:
+    the order bias -> activation -> residual, and GELU in its exact form.
+    """
+    y = fwd(x, w)
+    T = np.asarray(w).shape[2]
+    if bias is not None:
+        y = y + np.repeat(_f64(bias), T)[None, :]
+    if act == "gelu":
+        y = gelu(y)
+    elif act != "none":
+        raise ValueError("act must be 'none' or 'gelu'")
+    if residual is not None:
+        y = y + _f64(residual)
+    return y
 
 
 def half_spectrum(v) -> np.ndarray:

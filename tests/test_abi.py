@@ -26,14 +26,14 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_function():
     L = eql.lib()
     names = declared_functions()
-    assert len(names) == 8
+    assert len(names) == 9
     for n in names:
         assert hasattr(L, n), "missing export %s" % n
         assert hasattr(eql, n), "binding lacks %s" % n
 
 
 def test_version_and_status_strings():
-    assert eql.eqlinear_abi_version() == 100
+    assert eql.eqlinear_abi_version() == 101
     for s in range(5):
         assert eql.eqlinear_status_string(s)
     assert eql.eqlinear_status_string(99) == "unknown status"
@@ -99,6 +99,23 @@ def test_fwd_validation(fn):
     assert raw(fn, A16, A16B, MIS, 8, 4, 4, 4, F32, None) == eql.EQL_EALIGN
     # N == 0 is a no-op that launches nothing, even with null buffers.
     assert raw(fn, None, None, None, 0, 4, 4, 4, F16, None) == eql.EQL_OK
+
+
+def test_fwd_fused_validation():
+    F16, F32 = eql.EQL_F16, eql.EQL_F32
+    GELU = eql.EQL_ACT_GELU
+    x, wp, y = A16, A16B, A16 + 0x1000
+    fn = "eqlinear_fwd_fused"
+    assert raw(fn, x, wp, None, None, y, 8, 4, 4, 4, F16, 2, None) == eql.EQL_EINVAL        # act
+    assert raw(fn, x, wp, None, None, y, 8, 4, 4, 4, F16, -1, None) == eql.EQL_EINVAL       # act
+    assert raw(fn, x, wp, None, None, y, 8, 4, 4, 4, 5, GELU, None) == eql.EQL_EINVAL       # dtype
+    assert raw(fn, x, wp, None, None, y, 8, 4, 4, 17, F16, GELU, None) == eql.EQL_EUNSUPPORTED
+    assert raw(fn, None, wp, None, None, y, 8, 4, 4, 4, F16, GELU, None) == eql.EQL_EINVAL
+    assert raw(fn, x, wp, A16 + 1, None, y, 8, 4, 4, 4, F16, GELU, None) == eql.EQL_EALIGN  # bias, fp16
+    assert raw(fn, x, wp, A16 + 2, None, y, 8, 4, 4, 4, F32, GELU, None) == eql.EQL_EALIGN  # bias, fp32
+    assert raw(fn, x, wp, None, MIS, y, 8, 4, 4, 4, F16, GELU, None) == eql.EQL_EALIGN      # residual
+    assert raw(fn, MIS, wp, None, None, y, 8, 4, 4, 4, F16, GELU, None) == eql.EQL_EALIGN
+    assert raw(fn, None, None, None, None, None, 0, 4, 4, 4, F16, GELU, None) == eql.EQL_OK
 
 
 def test_pack_validation():

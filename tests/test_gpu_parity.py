@@ -171,6 +171,92 @@ def test_workload_full_size_sampled(key):
     assert np.isfinite(y).all() and np.isfinite(dx).all() and np.isfinite(dw).all()
 
 
+# -------------------------------------------------------------- fused epilogue
+def fused_d(T, dtype, x_d, wp, b_d, r_d, y, N, Cp, Dp, act):
+    eql.eqlinear_fwd_fused(x_d, wp, b_d, r_d, y, N, Cp, Dp, T, DT[dtype],
+                           eql.EQL_ACT_GELU if act == "gelu" else eql.EQL_ACT_NONE)
+    return y
+
+
+FUSED_CASES = [(True, "gelu", False), (True, "none", True), (False, "gelu", True), (True, "gelu", True)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("T", [3, 4, 8, 16])
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: "b%d_%s_r%d" % (c[0], c[1], c[2]))
+def test_fwd_fused_matches_oracle(T, dtype, case):
+    use_b, act, use_r = case
+    N, Cp, Dp = 300, 33, 70                      # three row tiles, ragged channel counts
+    print("case fused T=%d %s %s" % (T, dtype, case), flush=True)
+    wl = W.Workload("t", "test", T, N, Cp, Dp, dtype, ("fwd",), seed=21 + T)
+    x, w = W.make_x(wl), W.make_w(wl)
+    b = W.make_bias(wl) if use_b else None
+    r = W.make_residual(wl) if use_r else None
+    L = Lib(T, dtype)
+    x_d, w_d = dev(x), dev(w)
+    wp = L.pack(w_d, Dp, Cp, eql.EQL_PACK_FWD)
+    y = torch.empty((N, Dp * T), dtype=x_d.dtype, device=DEV)
+    fused_d(T, dtype, x_d, wp, dev(b) if use_b else None, dev(r) if use_r else None, y, N, Cp, Dp, act)
+    ref = oracle.fwd_fused(x, w, bias=b, residual=r, act=act)
+    assert rel_err(host(y), ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_fwd_fused_in_place_residual_and_plain_equivalence(dtype):
+    T, N, Cp, Dp = 4, 261, 40, 96
+    print("case fused in-place %s" % dtype, flush=True)
+    wl = W.Workload("t", "test", T, N, Cp, Dp, dtype, ("fwd",), seed=5)
+    x, w, b, r = W.make_x(wl), W.make_w(wl), W.make_bias(wl), W.make_residual(wl)
+    L = Lib(T, dtype)
+    x_d, w_d = dev(x), dev(w)
+    wp = L.pack(w_d, Dp, Cp, eql.EQL_PACK_FWD)
+    y = dev(r).clone()                                       # residual buffer doubles as the output
+    fused_d(T, dtype, x_d, wp, dev(b), y, y, N, Cp, Dp, "gelu")
+    assert rel_err(host(y), oracle.fwd_fused(x, w, bias=b, residual=r, act="gelu")) <= TOL[dtype]
+    # Nothing fused: bitwise the plain forward.
+    y0 = L.fwd_d(x_d, wp, N, Cp, Dp)
+    y1 = torch.empty_like(y0)
+    fused_d(T, dtype, x_d, wp, None, None, y1, N, Cp, Dp, "none")
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_fwd_fused_matches_torch_fp32_epilogue(dtype):
+    """Against plain PyTorch fp32 ops applied to the unfused kernel's fp32-rounded
+    output: F.gelu(y + b) + r."""
+    T, N, Cp, Dp = 4, 520, 64, 160
+    print("case fused vs torch %s" % dtype, flush=True)
+    wl = W.Workload("t", "test", T, N, Cp, Dp, dtype, ("fwd",), seed=8)
+    x, w, b, r = W.make_x(wl), W.make_w(wl), W.make_bias(wl), W.make_residual(wl)
+    L = Lib(T, dtype)
+    x_d, w_d, b_d, r_d = dev(x), dev(w), dev(b), dev(r)
+    wp = L.pack(w_d, Dp, Cp, eql.EQL_PACK_FWD)
+    y = torch.empty((N, Dp * T), dtype=x_d.dtype, device=DEV)
+    fused_d(T, dtype, x_d, wp, b_d, r_d, y, N, Cp, Dp, "gelu")
+    plain = L.fwd_d(x_d, wp, N, Cp, Dp).float()
+    ref = torch.nn.functional.gelu(plain + b_d.float().repeat_interleave(T)) + r_d.float()
+    torch.cuda.synchronize()
+    assert rel_err(host(y.float()), host(ref)) <= TOL[dtype]
+
+
+def test_fwd_fused_mlp_expansion_full_size_sampled():
+    """The EQ-ViT-S MLP expansion (c2) at full size with bias and GELU; sampled rows."""
+    wl = W.WORKLOADS["c2"]
+    T, N, Cp, Dp = wl.T, wl.N, wl.Cp, wl.Dp
+    print("case fused %s" % wl.name, flush=True)
+    x, w, b = W.make_x(wl), W.make_w(wl), W.make_bias(wl)
+    L = Lib(T, wl.dtype)
+    x_d, w_d = dev(x), dev(w)
+    wp = L.pack(w_d, Dp, Cp, eql.EQL_PACK_FWD)
+    y = torch.empty((N, Dp * T), dtype=x_d.dtype, device=DEV)
+    fused_d(T, wl.dtype, x_d, wp, dev(b), None, y, N, Cp, Dp, "gelu")
+    rows = _sample_rows(N)
+    yh = host(y)
+    assert np.isfinite(yh).all()
+    assert rel_err(yh[rows], oracle.fwd_fused(x[rows], w, bias=b, act="gelu")) <= TOL[wl.dtype]
+
+
 # ------------------------------------------------------------------ pack layout
 def unpack(buf, out_ch, in_ch, T, dtype):
     G = 16 // np.dtype(NPDT[dtype]).itemsize

@@ -27,7 +27,8 @@ def rand(*shape):
 
 
 def _ns(**over):
-    base = dict(unroll=O.unroll, fwd=O.fwd, bwd_x=O.bwd_x, bwd_w=O.bwd_w, half_spectrum=O.half_spectrum)
+    base = dict(unroll=O.unroll, fwd=O.fwd, bwd_x=O.bwd_x, bwd_w=O.bwd_w, half_spectrum=O.half_spectrum,
+                gelu=O.gelu, fwd_fused=O.fwd_fused)
     base.update(over)
     return types.SimpleNamespace(**base)
 
@@ -123,8 +124,60 @@ def pin_spectrum(o, T=7):
     return bool(np.allclose(o.half_spectrum(v), np.fft.rfft(v, axis=-1), atol=1e-12))
 
 
+# Fused epilogue (bias broadcast over g, GELU, residual).
+def pin_gelu_table(o):
+    """GELU(v) = v Phi(v) against the standard normal distribution table (5 digits):
+    Phi(1) = 0.84134, Phi(2) = 0.97725, Phi(-0.5) = 0.30854, Phi(0) = 0.5."""
+    table = {1.0: 0.84134, 2.0: 0.97725, -0.5: 0.30854, 0.0: 0.5}
+    v = np.array(sorted(table))
+    want = v * np.array([table[k] for k in sorted(table)])
+    return bool(np.all(np.abs(o.gelu(v) - want) <= 1e-5 * np.maximum(1.0, np.abs(v))))
+
+
+def pin_gelu_odd_part(o):
+    """Phi(v) + Phi(-v) = 1, so GELU(v) - GELU(-v) = v for every v."""
+    v = np.linspace(-6.0, 6.0, 97)
+    return bool(np.allclose(o.gelu(v) - o.gelu(-v), v, atol=1e-12))
+
+
+def pin_fused_brute_force(o, T=3, N=2, Cp=2, Dp=2):
+    """Plain loops with math.erf: y[n, dT+g] = gelu(sum_{c,h} x[n, cT+h] w[d, c, (g-h) mod T]
+    + b[d]) + r[n, dT+g]."""
+    import math
+    x, w, b, r = rand(N, Cp * T), rand(Dp, Cp, T), rand(Dp), rand(N, Dp * T)
+    got = o.fwd_fused(x, w, bias=b, residual=r, act="gelu")
+    for n in range(N):
+        for d in range(Dp):
+            for g in range(T):
+                acc = sum(x[n, c * T + h] * w[d, c, (g - h) % T] for c in range(Cp) for h in range(T)) + b[d]
+                want = 0.5 * acc * (1.0 + math.erf(acc / math.sqrt(2.0))) + r[n, d * T + g]
+                if abs(got[n, d * T + g] - want) > 1e-12 * max(1.0, abs(want)):
+                    return False
+    return True
+
+
+def pin_fused_equivariance(o, T=4, N=5, Cp=3, Dp=2):
+    """A shared per-channel bias and a pointwise activation commute with the group
+    action: shifting x and the residual along the group axis shifts y."""
+    x, w, b, r = rand(N, Cp * T), rand(Dp, Cp, T), rand(Dp), rand(N, Dp * T)
+    y = o.fwd_fused(x, w, bias=b, residual=r, act="gelu").reshape(N, Dp, T)
+    for s in range(1, T):
+        xs = np.roll(x.reshape(N, Cp, T), s, axis=2).reshape(N, Cp * T)
+        rs = np.roll(r.reshape(N, Dp, T), s, axis=2).reshape(N, Dp * T)
+        ys = o.fwd_fused(xs, w, bias=b, residual=rs, act="gelu").reshape(N, Dp, T)
+        if not np.allclose(ys, np.roll(y, s, axis=2), atol=1e-12):
+            return False
+    return True
+
+
+def pin_fused_reduces_to_fwd(o, T=4, N=4, Cp=3, Dp=2):
+    x, w = rand(N, Cp * T), rand(Dp, Cp, T)
+    return bool(np.array_equal(o.fwd_fused(x, w), o.fwd(x, w)))
+
+
 ALL_PINS = [pin_golden, pin_circulant, pin_torch_autograd, pin_fft, pin_adjoint,
-            pin_weight_gradient, pin_equivariance, pin_spectrum]
+            pin_weight_gradient, pin_equivariance, pin_spectrum, pin_gelu_table, pin_gelu_odd_part,
+            pin_fused_brute_force, pin_fused_equivariance, pin_fused_reduces_to_fwd]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
@@ -318,7 +371,34 @@ def _mut_spectrum_sign(v):
     return v @ np.exp(+2j * np.pi * t * k / T)                              # wrong sign
 
 
+def _mut_fused_bias_tiled(x, w, bias=None, residual=None, act="none"):
+    y = O.fwd(x, w)
+    T = np.asarray(w).shape[2]
+    if bias is not None:
+        y = y + np.tile(np.asarray(bias, np.float64), T)[None, :]          # b[(dT+g) mod D'], not b[d]
+    y = O.gelu(y) if act == "gelu" else y
+    return y + (0.0 if residual is None else np.asarray(residual, np.float64))
+
+
+def _mut_gelu_tanh(v):
+    v = np.asarray(v, dtype=np.float64)                                     # the tanh approximation
+    return 0.5 * v * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (v + 0.044715 * v ** 3)))
+
+
+def _mut_fused_residual_first(x, w, bias=None, residual=None, act="none"):
+    y = O.fwd(x, w)
+    T = np.asarray(w).shape[2]
+    if bias is not None:
+        y = y + np.repeat(np.asarray(bias, np.float64), T)[None, :]
+    if residual is not None:
+        y = y + np.asarray(residual, np.float64)                            # before the activation
+    return O.gelu(y) if act == "gelu" else y
+
+
 MUTANTS = {
+    "fused_bias_tiled_over_channels": dict(fwd_fused=_mut_fused_bias_tiled),
+    "gelu_tanh_approximation": dict(gelu=_mut_gelu_tanh),
+    "fused_residual_before_activation": dict(fwd_fused=_mut_fused_residual_first),
     "correlation_instead_of_convolution": dict(unroll=_mut_unroll_correlation,
                                                fwd=_mut_fwd_from(_mut_unroll_correlation)),
     "bwd_x_transposed_operand": dict(bwd_x=_mut_bwd_x_transposed),

@@ -27,7 +27,7 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 ROW_BLOCK = 1024
-_X, _W, _DY, _ROWS = 0, 1, 2, 3
+_X, _W, _DY, _ROWS, _BIAS, _RES = 0, 1, 2, 3, 4, 5
 
 
 @dataclasses.dataclass(frozen=True)
@@ -143,3 +143,17 @@ def make_w(wl: Workload) -> np.ndarray:
     a = rng.standard_normal((wl.Dp, wl.Cp, wl.T), dtype=np.float32)
     a *= np.float32(1.0 / np.sqrt(wl.C))
     return a.astype(wl.np_dtype)
+
+
+def make_bias(wl: Workload) -> np.ndarray:
+    """bias[D'] ~ N(0, 1) in the workload dtype: one value per output channel, shared
+    by its T group elements (the fused forward epilogue)."""
+    rng = np.random.default_rng([wl.seed, _BIAS])
+    return rng.standard_normal(wl.Dp, dtype=np.float32).astype(wl.np_dtype)
+
+
+def make_residual(wl: Workload, rows=None) -> np.ndarray:
+    """residual[rows, D'*T] ~ N(0, 1) in the workload dtype (the fused forward epilogue)."""
+    idx = _select(wl, rows)
+    return _rows_f32(wl, _RES, wl.D, idx).astype(wl.np_dtype)
+
