@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--workload", default="c5", choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip timing the unrolled dense GEMM comparator")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip timing the fused forward epilogue (bias, GELU, residual) against torch ops")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows of the CPU-oracle sample (0: sized to about 12 s of work)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -205,6 +207,14 @@ def main():
         total = dense["fwd_ms"] + dense["bwd_x_ms"] + dense["bwd_w_ms"]
         dense["speedup_fwd_bwd"] = round(total / (per["fwd"] + per["bwd_x"] + per["bwd_w"]), 3)
 
+    fused = None
+    if not args.no_fused:
+        b = torch.from_numpy(W.make_bias(wl)).to(dev)
+        fused = fused_epilogue(torch, eql, x, wp, b, dy, y, N, Cp, Dp, T, code, sptr,
+                               reps=max(5, min(args.steps, 20)))
+        fused["plain_fwd_ms"] = round(per["fwd"], 4)
+        del b
+
     cpu = None
     if not args.no_cpu_baseline:
         del x, dy, y, dx
@@ -233,9 +243,54 @@ def main():
         "mfma_frac_step": round(n_passes * actual / (ms_per_step * 1e-3) / 1e12 / MFMA_PEAK[wl.dtype], 4),
         "roofline": roofline,
         "dense_baseline": dense,
+        "fused_epilogue": fused,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
+
+
+def fused_epilogue(torch, eql, x, wp, b, r, y, N, Cp, Dp, T, code, sptr, reps):
+    """eqlinear_fwd_fused against the forward followed by the same epilogue as
+    separate torch ops, on the benchmark's workload: bias + GELU (the MLP expansion)
+    and bias + residual (the MLP projection back; dy's buffer serves as the residual)."""
+    F = torch.nn.functional
+    bb = b.repeat_interleave(T)
+
+    def timeit(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(e) / reps
+
+    def unfused(gelu, res):
+        eql.eqlinear_fwd(x, wp, y, N, Cp, Dp, T, code, sptr)
+        z = y + bb
+        if gelu:
+            z = F.gelu(z)
+        if res:
+            z = z + r
+        return z
+
+    res = {
+        "bias_gelu_ms": timeit(lambda: eql.eqlinear_fwd_fused(x, wp, b, None, y, N, Cp, Dp, T, code,
+                                                              eql.EQL_ACT_GELU, sptr)),
+        "bias_gelu_torch_ms": timeit(lambda: unfused(True, False)),
+        "bias_residual_ms": timeit(lambda: eql.eqlinear_fwd_fused(x, wp, b, r, y, N, Cp, Dp, T, code,
+                                                                  eql.EQL_ACT_NONE, sptr)),
+        "bias_residual_torch_ms": timeit(lambda: unfused(False, True)),
+    }
+    res = {k: round(v, 4) for k, v in res.items()}
+    res["speedup_bias_gelu"] = round(res["bias_gelu_torch_ms"] / res["bias_gelu_ms"], 3)
+    res["speedup_bias_residual"] = round(res["bias_residual_torch_ms"] / res["bias_residual_ms"], 3)
+    res["kind"] = "eqlinear_fwd_fused vs eqlinear_fwd + torch (y + b), F.gelu, + residual"
+    torch.cuda.empty_cache()
+    return res
 
 
 def dense_comparator(torch, x, w, dy, T, reps):
