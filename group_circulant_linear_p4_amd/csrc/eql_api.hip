@@ -53,6 +53,9 @@ int check_sizes(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? EQL_OK : EQL_EHIP; }
 
+// Fixed per-stage cost of a forward tile in units of one 32-column block's MFMAs.
+constexpr int64_t kFwdStageFixed = 5;
+
 // Compute units of the current device (cached per device; 256 on MI355X).  The
 // persistent kernels launch one workgroup per compute unit.
 int device_cus() {
@@ -83,8 +86,23 @@ int run_fwd(const void* x, const void* wp, void* y, int64_t N, int64_t Cin, int6
   const int nbm = fwd_nb_max(T);
   const int64_t rowTiles = ceil_div(N, kFwdRows);
   const bool rowsAligned = (Cin * T * elt_bytes(dtype)) % 16 == 0;
-  int nb = nbm;
-  if (!rowsAligned || (nbm > 1 && rowTiles * ceil_div(Dout, 32 * nbm) < kTargetWorkgroups)) nb = 1;
+  const int cus = device_cus();
+  // Tile width (32-column blocks): the persistent grid takes ceil(tiles / CUs) rounds,
+  // and a tile costs about kFwdStageFixed + nb block-units per K stage (the stage's
+  // barrier, x load and transform measure about five blocks' MFMA time).  Fewest
+  // estimated units wins; ties go to the wider tile, which moves fewer bytes per FLOP.
+  int nb = 1;
+  if (rowsAligned) {
+    int64_t best = -1;
+    for (int cand = nbm; cand >= 1; cand /= 2) {
+      const int64_t rounds = ceil_div(rowTiles * ceil_div(Dout, 32 * cand), (int64_t)cus);
+      const int64_t cost = rounds * (kFwdStageFixed + cand);
+      if (best < 0 || cost < best) {
+        best = cost;
+        nb = cand;
+      }
+    }
+  }
   const int64_t colTiles = ceil_div(Dout, 32 * nb);
   if (colTiles > kMaxGrid) return EQL_EINVAL;
 
@@ -103,7 +121,6 @@ int run_fwd(const void* x, const void* wp, void* y, int64_t N, int64_t Cin, int6
   a.bias = bias;
   a.act = act;
 
-  const int cus = device_cus();
   // Rows in pieces small enough for the tile indices.
   const int64_t maxRows = (kMaxGrid / colTiles) * kFwdRows;
   const size_t inRow = (size_t)Cin * T * elt_bytes(dtype), outRow = (size_t)Dout * T * elt_bytes(dtype);
@@ -279,7 +296,7 @@ int eqlinear_bwd_w(const void* x, const void* dy, void* dw, void* workspace, siz
     return EQL_EALIGN;
   const int64_t gdy = ceil_div(p.kgCount * 2 * p.Dpad, 256);
   const int64_t gx = ceil_div(p.kgCount * 2 * p.Cpad, 256);
-  const int64_t rgrid = ceil_div(Dp * Cp, 256);
+  const int64_t rgrid = ceil_div(Dp * Cp, kReduceOuts);
   if (p.real.items() > kMaxGrid || p.pair.items() > kMaxGrid || gdy > kMaxGrid || gx > kMaxGrid ||
       rgrid > kMaxGrid)
     return EQL_EINVAL;

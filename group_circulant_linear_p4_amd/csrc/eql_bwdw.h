@@ -25,7 +25,8 @@
 //      axes take 64-wide tiles instead of padding to 256.  Both operands stream
 //      into NS-deep LDS rings by buffer->LDS loads; the loop body is LDS reads and
 //      MFMAs.  Each item writes the fp32 partial spectrum of one row range.
-//   3. eql_bwdw_reduce: sums the partials in a fixed order (deterministic), applies
+//   3. eql_bwdw_reduce: sums the partials in a fixed order (deterministic; four waves
+//      share the splits of 64 outputs and are combined in order), applies
 //      the inverse group transform and rounds to the element type.
 #pragma once
 
@@ -302,29 +303,51 @@ __global__ void __launch_bounds__(256) eql_bwdw_gemm(const BwdwArgs a) {
 // Sum of the split partials, then the inverse group transform.  Both operands were
 // transformed without scaling, so the inverse is the plain one:
 //   dw[t] = (1/T) (G0 + (-1)^t G_{T/2} + 2 sum_k (cos Re G_k - sin Im G_k)).
+// Reduction of the partial spectra.  A workgroup covers 64 consecutive (d, c)
+// outputs; wave w sums splits w, w+4, w+8, ... of every plane for them (adjacent
+// lanes read adjacent outputs), and wave 0 adds the four partial sums in a fixed
+// order, so the result does not depend on timing.  Then the plain inverse
+// transform and one rounding to the element type.
+constexpr int kReduceOuts = 64;
+
 template <int T, typename Elt>
 __global__ void __launch_bounds__(256) eql_bwdw_reduce(const BwdwReduceArgs a) {
   constexpr int NR = n_real_planes(T);
   constexpr int NC = T - NR;  // planes of the complex pairs
-  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  __shared__ float part[3][T][kReduceOuts];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const size_t idx = (size_t)blockIdx.x * kReduceOuts + lane;
   const size_t plane = (size_t)a.Dp * a.Cp;
-  if (idx >= plane) return;
+  const bool live = idx < plane;
   float P[T];
 #pragma unroll
   for (int p = 0; p < T; ++p) P[p] = 0.0f;
-  for (int s = 0; s < a.SR; ++s) {
+  if (live) {
+    for (int s = wave; s < a.SR; s += 4) {
 #pragma unroll
-    for (int p = 0; p < NR; ++p) P[p] += a.wsR[((size_t)s * NR + p) * plane + idx];
-  }
-  if constexpr (NC > 0) {
-    for (int s = 0; s < a.SP; ++s) {
+      for (int p = 0; p < NR; ++p) P[p] += a.wsR[((size_t)s * NR + p) * plane + idx];
+    }
+    if constexpr (NC > 0) {
+      for (int s = wave; s < a.SP; s += 4) {
 #pragma unroll
-      for (int p = 0; p < NC; ++p) P[NR + p] += a.wsP[((size_t)s * NC + p) * plane + idx];
+        for (int p = 0; p < NC; ++p) P[NR + p] += a.wsP[((size_t)s * NC + p) * plane + idx];
+      }
     }
   }
-  float g[T];
-  Idft<T, true>::run(P, g, a.tw);
-  store_group<T, Elt>(static_cast<Elt*>(a.dw) + idx * T, g);
+  if (wave > 0) {
+#pragma unroll
+    for (int p = 0; p < T; ++p) part[wave - 1][p][lane] = P[p];
+  }
+  __syncthreads();
+  if (wave == 0 && live) {
+#pragma unroll
+    for (int w = 0; w < 3; ++w)
+#pragma unroll
+      for (int p = 0; p < T; ++p) P[p] += part[w][p][lane];
+    float g[T];
+    Idft<T, true>::run(P, g, a.tw);
+    store_group<T, Elt>(static_cast<Elt*>(a.dw) + idx * T, g);
+  }
 }
 
 }  // namespace eql

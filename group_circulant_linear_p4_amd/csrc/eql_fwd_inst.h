@@ -1,5 +1,6 @@
 // Forward-kernel instantiations for one element type and epilogue: T = 1..16, the
-// full-width and the one-column-block tile, and the three load modes (see
+// full-width tile (fwd_nb_max(T) column blocks), the two-block tile where the full
+// width is four blocks, the one-block tile, and the three load modes (see
 // eql_fwd.h).  Each of eql_fwd_{f16,f32}.hip (plain epilogue) and
 // eql_fwd_fused_{f16,f32}.hip (bias / activation / residual) instantiates one.
 #pragma once
@@ -23,6 +24,12 @@ struct FwdInst {
     if (NB == NBM) {
       return a.loadMode == kLoadFull ? launch<T, NBM, kLoadFull>(a, grid, s)
                                      : launch<T, NBM, kLoadAligned>(a, grid, s);
+    }
+    if constexpr (NBM == 4) {
+      if (NB == 2) {
+        return a.loadMode == kLoadFull ? launch<T, 2, kLoadFull>(a, grid, s)
+                                       : launch<T, 2, kLoadAligned>(a, grid, s);
+      }
     }
     if constexpr (NBM != 1) {
       if (NB == 1) {

@@ -171,6 +171,22 @@ def test_workload_full_size_sampled(key):
     assert np.isfinite(y).all() and np.isfinite(dx).all() and np.isfinite(dw).all()
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
+def test_two_block_tile(T, dtype):
+    """157 row tiles x 64 output channels: on a 256-CU device the tile-width model
+    picks the 64-column tile for the forward (D' = 64) and the input gradient
+    (C' = 40): one round of tiles where 32-column tiles would need two."""
+    N, Cp, Dp = 20000, 40, 64
+    print("case two-block tile T=%d %s" % (T, dtype), flush=True)
+    x, w, dy = inputs(T, N, Cp, Dp, dtype, seed=40 + T)
+    y, dx, dw = Lib(T, dtype).all_passes(x, w, dy)
+    tol = TOL[dtype]
+    assert rel_err(y, oracle.fwd(x, w)) <= tol
+    assert rel_err(dx, oracle.bwd_x(dy, w)) <= tol
+    assert rel_err(dw, oracle.bwd_w(x, dy, T)) <= tol
+
+
 # -------------------------------------------------------------- fused epilogue
 def fused_d(T, dtype, x_d, wp, b_d, r_d, y, N, Cp, Dp, act):
     eql.eqlinear_fwd_fused(x_d, wp, b_d, r_d, y, N, Cp, Dp, T, DT[dtype],
