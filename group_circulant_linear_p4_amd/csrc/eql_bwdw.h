@@ -300,14 +300,13 @@ __global__ void __launch_bounds__(256) eql_bwdw_gemm(const BwdwArgs a) {
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-// Sum of the split partials, then the inverse group transform.  Both operands were
-// transformed without scaling, so the inverse is the plain one:
-//   dw[t] = (1/T) (G0 + (-1)^t G_{T/2} + 2 sum_k (cos Re G_k - sin Im G_k)).
-// Reduction of the partial spectra.  A workgroup covers 64 consecutive (d, c)
-// outputs; wave w sums splits w, w+4, w+8, ... of every plane for them (adjacent
-// lanes read adjacent outputs), and wave 0 adds the four partial sums in a fixed
-// order, so the result does not depend on timing.  Then the plain inverse
-// transform and one rounding to the element type.
+// Sum of the split partials, then the inverse group transform.  A workgroup covers
+// 64 consecutive (d, c) outputs; wave w sums splits w, w+4, w+8, ... of every plane
+// for them (adjacent lanes read adjacent outputs), and wave 0 adds the four partial
+// sums in a fixed order, so the result does not depend on timing.  Both operands
+// were transformed without scaling, so the inverse is the plain one,
+//   dw[t] = (1/T) (G0 + (-1)^t G_{T/2} + 2 sum_k (cos Re G_k - sin Im G_k)),
+// followed by one rounding to the element type.
 constexpr int kReduceOuts = 64;
 
 template <int T, typename Elt>

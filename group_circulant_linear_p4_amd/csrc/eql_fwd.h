@@ -11,14 +11,16 @@
 //     of K stages, so loads run ahead across tile boundaries;
 //   * the K loop runs over "stages" of JC 16-byte channel groups (two groups per
 //     MFMA k-step);
-//   * x goes straight from HBM/L2 into registers in MFMA A-operand order: lane l
-//     takes row l%32 and channel group 2s + l/32 of k-step s (G channels x T group
-//     elements, 16*T contiguous bytes), via bounds-checked buffer loads (rows past
-//     N and channels past C' read as zero without branches).  The group DFT runs
-//     in fp32 registers and rounds once to the element type; the negated Im planes
-//     needed by the real part of each complex product are made by a sign flip;
+//   * x of a stage (the workgroup's 128 rows x JC groups) streams into its own
+//     LDS ring the same way as the weight (16-byte rows only; otherwise each lane
+//     loads its x straight into registers with narrower bounds-checked loads).
+//     Lane l takes row l%32 and channel group 2s + l/32 of k-step s (G channels x
+//     T group elements) in MFMA A-operand order; rows past N and channels past
+//     C' read as zero without branches.  The group DFT runs in fp32 registers and
+//     rounds once to the element type; the negated Im planes needed by the real
+//     part of each complex product are made by a sign flip;
 //   * the packed spectrum of w for the workgroup's BN channels streams into an
-//     NSTAGE-deep LDS ring with buffer loads that write LDS directly (no VGPR
+//     NS-deep LDS ring with buffer loads that write LDS directly (no VGPR
 //     staging).  A ring row holds the JC*T 16-byte units of one output channel,
 //     XOR-swizzled so that the 16-byte MFMA B-operand reads of 16 consecutive
 //     channels (one LDS cycle on the 64-bank LDS) touch 16 different 16-byte
@@ -26,8 +28,9 @@
 //   * per k-step and 32-column block: real planes take one MFMA, a complex pair
 //     four (Re += Xr Wr + (-Xi) Wi, Im += Xi Wr + Xr Wi);
 //   * the epilogue reads the T accumulators of one (row, channel) from the same
-//     register slot, applies the inverse DFT and stores T contiguous outputs;
-//     adjacent lanes write adjacent channels.
+//     register slot, applies the inverse DFT (its 1/T and 2/T are in the packed
+//     weight) and stores T contiguous outputs; adjacent lanes write adjacent
+//     channels.  EPI = 1 adds a per-channel bias, GELU and a residual first.
 #pragma once
 
 #include <type_traits>
