@@ -296,7 +296,8 @@ int eqlinear_bwd_w(const void* x, const void* dy, void* dw, void* workspace, siz
     return EQL_EALIGN;
   const int64_t gdy = ceil_div(p.kgCount * 2 * p.Dpad, 256);
   const int64_t gx = ceil_div(p.kgCount * 2 * p.Cpad, 256);
-  const int64_t rgrid = ceil_div(Dp * Cp, kReduceOuts);
+  const int rwaves = reduce_waves(p.real.S * n_real_planes(T) + p.pair.S * (T - n_real_planes(T)));
+  const int64_t rgrid = ceil_div(Dp * Cp, 256 / rwaves);
   if (p.real.items() > kMaxGrid || p.pair.items() > kMaxGrid || gdy > kMaxGrid || gx > kMaxGrid ||
       rgrid > kMaxGrid)
     return EQL_EINVAL;
@@ -360,8 +361,8 @@ int eqlinear_bwd_w(const void* x, const void* dy, void* dw, void* workspace, siz
   r.Dp = (int)Dp;
   r.Cp = (int)Cp;
   r.tw = tw;
-  return status_of(f16 ? launch_bwdw_reduce_f16(T, r, (unsigned)rgrid, s)
-                       : launch_bwdw_reduce_f32(T, r, (unsigned)rgrid, s));
+  return status_of(f16 ? launch_bwdw_reduce_f16(T, rwaves, r, (unsigned)rgrid, s)
+                       : launch_bwdw_reduce_f32(T, rwaves, r, (unsigned)rgrid, s));
 }
 
 }  // extern "C"

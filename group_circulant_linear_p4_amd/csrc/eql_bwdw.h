@@ -25,8 +25,8 @@
 //      axes take 64-wide tiles instead of padding to 256.  Both operands stream
 //      into NS-deep LDS rings by buffer->LDS loads; the loop body is LDS reads and
 //      MFMAs.  Each item writes the fp32 partial spectrum of one row range.
-//   3. eql_bwdw_reduce: sums the partials in a fixed order (deterministic; four waves
-//      share the splits of 64 outputs and are combined in order), applies
+//   3. eql_bwdw_reduce: sums the partials in a fixed order (deterministic; with long
+//      chains four waves share the splits of 64 outputs, combined in order), applies
 //      the inverse group transform and rounds to the element type.
 #pragma once
 
@@ -300,53 +300,63 @@ __global__ void __launch_bounds__(256) eql_bwdw_gemm(const BwdwArgs a) {
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-// Sum of the split partials, then the inverse group transform.  A workgroup covers
-// 64 consecutive (d, c) outputs; wave w sums splits w, w+4, w+8, ... of every plane
-// for them (adjacent lanes read adjacent outputs), and wave 0 adds the four partial
-// sums in a fixed order, so the result does not depend on timing.  Both operands
-// were transformed without scaling, so the inverse is the plain one,
+// Sum of the split partials, then the inverse group transform.  WAVES = 1: one
+// output per thread, all splits in one chain.  WAVES = 4 (for long chains): a
+// workgroup covers 64 consecutive (d, c) outputs and wave w sums splits w, w+4,
+// w+8, ... for them (adjacent lanes read adjacent outputs); wave 0 adds the four
+// partial sums in a fixed order.  Either way the order depends only on the shape,
+// so the result does not depend on timing.  Both operands were transformed
+// without scaling, so the inverse is the plain one,
 //   dw[t] = (1/T) (G0 + (-1)^t G_{T/2} + 2 sum_k (cos Re G_k - sin Im G_k)),
 // followed by one rounding to the element type.
-constexpr int kReduceOuts = 64;
-
-template <int T, typename Elt>
+template <int T, typename Elt, int WAVES>
 __global__ void __launch_bounds__(256) eql_bwdw_reduce(const BwdwReduceArgs a) {
   constexpr int NR = n_real_planes(T);
   constexpr int NC = T - NR;  // planes of the complex pairs
-  __shared__ float part[3][T][kReduceOuts];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const size_t idx = (size_t)blockIdx.x * kReduceOuts + lane;
+  constexpr int OUTS = 256 / WAVES;
+  __shared__ float part[WAVES > 1 ? WAVES - 1 : 1][T][OUTS];
+  const int lane = threadIdx.x % OUTS, w = threadIdx.x / OUTS;
+  const size_t idx = (size_t)blockIdx.x * OUTS + lane;
   const size_t plane = (size_t)a.Dp * a.Cp;
   const bool live = idx < plane;
   float P[T];
 #pragma unroll
   for (int p = 0; p < T; ++p) P[p] = 0.0f;
   if (live) {
-    for (int s = wave; s < a.SR; s += 4) {
+    for (int s = w; s < a.SR; s += WAVES) {
 #pragma unroll
       for (int p = 0; p < NR; ++p) P[p] += a.wsR[((size_t)s * NR + p) * plane + idx];
     }
     if constexpr (NC > 0) {
-      for (int s = wave; s < a.SP; s += 4) {
+      for (int s = w; s < a.SP; s += WAVES) {
 #pragma unroll
         for (int p = 0; p < NC; ++p) P[NR + p] += a.wsP[((size_t)s * NC + p) * plane + idx];
       }
     }
   }
-  if (wave > 0) {
+  if constexpr (WAVES > 1) {
+    if (w > 0) {
 #pragma unroll
-    for (int p = 0; p < T; ++p) part[wave - 1][p][lane] = P[p];
+      for (int p = 0; p < T; ++p) part[w - 1][p][lane] = P[p];
+    }
+    __syncthreads();
+    if (w == 0 && live) {
+#pragma unroll
+      for (int v = 0; v < WAVES - 1; ++v)
+#pragma unroll
+        for (int p = 0; p < T; ++p) P[p] += part[v][p][lane];
+    }
   }
-  __syncthreads();
-  if (wave == 0 && live) {
-#pragma unroll
-    for (int w = 0; w < 3; ++w)
-#pragma unroll
-      for (int p = 0; p < T; ++p) P[p] += part[w][p][lane];
+  if (w == 0 && live) {
     float g[T];
     Idft<T, true>::run(P, g, a.tw);
     store_group<T, Elt>(static_cast<Elt*>(a.dw) + idx * T, g);
   }
 }
+
+// Waves per output group of the reduce, from the loads one thread would chain
+// (splits x planes): sharing them pays only for long chains (c5: 32 loads, one wave;
+// the small layers: 128 and more, four).
+__host__ __device__ constexpr int reduce_waves(int64_t chain) { return chain >= 64 ? 4 : 1; }
 
 }  // namespace eql

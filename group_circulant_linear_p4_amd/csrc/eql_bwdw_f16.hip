@@ -9,8 +9,9 @@ static hipError_t spec_one(const SpecArgs& a, unsigned grid, hipStream_t s) {
 }
 
 template <int T>
-static hipError_t reduce_one(const BwdwReduceArgs& a, unsigned grid, hipStream_t s) {
-  return launch_kernel((const void*)&eql_bwdw_reduce<T, _Float16>, grid, a, s);
+static hipError_t reduce_one(int waves, const BwdwReduceArgs& a, unsigned grid, hipStream_t s) {
+  return waves == 4 ? launch_kernel((const void*)&eql_bwdw_reduce<T, _Float16, 4>, grid, a, s)
+                    : launch_kernel((const void*)&eql_bwdw_reduce<T, _Float16, 1>, grid, a, s);
 }
 
 hipError_t launch_spec_f16(int T, const SpecArgs& a, unsigned grid, hipStream_t s) {
@@ -19,8 +20,8 @@ hipError_t launch_spec_f16(int T, const SpecArgs& a, unsigned grid, hipStream_t 
 #undef EQL_CASE
 }
 
-hipError_t launch_bwdw_reduce_f16(int T, const BwdwReduceArgs& a, unsigned grid, hipStream_t s) {
-#define EQL_CASE(t) return reduce_one<t>(a, grid, s);
+hipError_t launch_bwdw_reduce_f16(int T, int waves, const BwdwReduceArgs& a, unsigned grid, hipStream_t s) {
+#define EQL_CASE(t) return reduce_one<t>(waves, a, grid, s);
   EQL_FOR_EACH_T(T, EQL_CASE)
 #undef EQL_CASE
 }

@@ -34,8 +34,8 @@ hipError_t launch_bwdw_real_f16(int T, int DB, int CB, const BwdwArgs& a, unsign
 hipError_t launch_bwdw_real_f32(int T, int DB, int CB, const BwdwArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_bwdw_pair_f16(int T, int DB, int CB, const BwdwArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_bwdw_pair_f32(int T, int DB, int CB, const BwdwArgs& a, unsigned grid, hipStream_t s);
-hipError_t launch_bwdw_reduce_f16(int T, const BwdwReduceArgs& a, unsigned grid, hipStream_t s);
-hipError_t launch_bwdw_reduce_f32(int T, const BwdwReduceArgs& a, unsigned grid, hipStream_t s);
+hipError_t launch_bwdw_reduce_f16(int T, int waves, const BwdwReduceArgs& a, unsigned grid, hipStream_t s);
+hipError_t launch_bwdw_reduce_f32(int T, int waves, const BwdwReduceArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_pack_f16(int T, const PackArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_pack_f32(int T, const PackArgs& a, unsigned grid, hipStream_t s);
 
