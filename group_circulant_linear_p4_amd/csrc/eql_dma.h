@@ -123,12 +123,6 @@ constexpr uint32_t kOob = 0x80000000u;
 struct BufDesc {
   u32x4 w;
 };
-__device__ __forceinline__ BufDesc make_desc(const void* base, uint32_t bytes) {
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  BufDesc d;
-  d.w = (u32x4){(uint32_t)b, (uint32_t)(b >> 32) & 0xFFFFu, bytes, 0x00020000u};
-  return d;
-}
 
 // 16 bytes per lane from buffer offset `voff` straight into LDS at
 // lds_base + 16 * lane (no VGPR destination).  Written as an asm statement so that

@@ -13,8 +13,9 @@ import math
 
 import torch
 
-from . import (EQL_PACK_BWDX, EQL_PACK_FWD, eqlinear_bwd_w, eqlinear_bwd_w_workspace_bytes, eqlinear_bwd_x,
-               eqlinear_fwd, eqlinear_pack_weight, eqlinear_packed_weight_bytes)
+from . import (EQL_ACT_GELU, EQL_ACT_NONE, EQL_PACK_BWDX, EQL_PACK_FWD, eqlinear_bwd_w,
+               eqlinear_bwd_w_workspace_bytes, eqlinear_bwd_x, eqlinear_fwd, eqlinear_fwd_fused,
+               eqlinear_pack_weight, eqlinear_packed_weight_bytes)
 
 
 def _packed(w: torch.Tensor, mode: int) -> torch.Tensor:
@@ -65,6 +66,30 @@ class EQLinearFunction(torch.autograd.Function):
 
 def eqlinear(x: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
     return EQLinearFunction.apply(x, w)
+
+
+def eqlinear_fused(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None = None,
+                   residual: torch.Tensor | None = None, act: str = "none") -> torch.Tensor:
+    """Forward only: act(x W^T + bias) + residual in one kernel (eqlinear_fwd_fused), the
+    MLP-block epilogue of the networks the layer is built into ("Nivel de Rede").  bias
+    has one value per output channel (shared by its T group elements); act is "none"
+    or "gelu"; residual has the output's shape.  There is no backward: it raises when
+    autograd would need one."""
+    if torch.is_grad_enabled() and any(t is not None and t.requires_grad for t in (x, w, bias, residual)):
+        raise RuntimeError("eqlinear_fused is forward-only; use eqlinear for training")
+    if act not in ("none", "gelu"):
+        raise ValueError("act must be 'none' or 'gelu'")
+    Dp, Cp, T = w.shape
+    if x.shape[-1] != Cp * T:
+        raise ValueError("x has %d features, the weight expects C'*T = %d" % (x.shape[-1], Cp * T))
+    x2 = x.reshape(-1, Cp * T).contiguous()
+    N = x2.shape[0]
+    b = bias.contiguous() if bias is not None else None
+    r = residual.reshape(N, Dp * T).contiguous() if residual is not None else None
+    y = torch.empty((N, Dp * T), dtype=x.dtype, device=x.device)
+    eqlinear_fwd_fused(x2, _packed(w.contiguous(), EQL_PACK_FWD), b, r, y, N, Cp, Dp, T, x.dtype,
+                       EQL_ACT_GELU if act == "gelu" else EQL_ACT_NONE)
+    return y.reshape(*x.shape[:-1], Dp * T)
 
 
 class EQLinear(torch.nn.Module):

@@ -375,6 +375,20 @@ def test_misaligned_buffer_is_rejected():
     assert ei.value.status == eql.EQL_EALIGN
 
 
+def test_layer_fused_forward_matches_oracle():
+    from group_circulant_linear_p4_amd.layer import eqlinear_fused
+    T, N, Cp, Dp = 4, 3 * 37, 24, 40
+    print("case layer fused", flush=True)
+    wl = W.Workload("t", "test", T, N, Cp, Dp, "f32", ("fwd",), seed=17)
+    x, w, b, r = W.make_x(wl), W.make_w(wl), W.make_bias(wl), W.make_residual(wl)
+    y = eqlinear_fused(dev(x).reshape(3, 37, Cp * T), dev(w), dev(b), dev(r), act="gelu")
+    assert tuple(y.shape) == (3, 37, Dp * T)
+    ref = oracle.fwd_fused(x, w, bias=b, residual=r, act="gelu")
+    assert rel_err(host(y).reshape(N, Dp * T), ref) <= TOL["f32"]
+    with pytest.raises(RuntimeError):
+        eqlinear_fused(dev(x).requires_grad_(), dev(w), act="gelu")
+
+
 def test_layer_autograd_matches_oracle():
     from group_circulant_linear_p4_amd.layer import EQLinear
     T, N, Cp, Dp = 4, 200, 6, 10
