@@ -43,3 +43,16 @@ def test_hot_rows():
     x = W.make_x(wl).astype(np.float32)
     cold = np.setdiff1d(np.arange(wl.N), hr)
     assert np.abs(x[hr]).max() > 16 * 2.0 and np.abs(x[cold]).max() < 8.0
+
+
+def test_bias_and_residual_streams():
+    """The fused epilogue's inputs: deterministic, own streams (independent of dy, whose
+    shape the residual shares), row subsets regenerate exactly."""
+    wl = small()
+    b, r = W.make_bias(wl), W.make_residual(wl)
+    assert b.shape == (wl.Dp,) and b.dtype == wl.np_dtype
+    assert r.shape == (wl.N, wl.Dp * wl.T) and r.dtype == wl.np_dtype
+    assert np.array_equal(b, W.make_bias(wl)) and np.array_equal(r, W.make_residual(wl))
+    assert not np.array_equal(r, W.make_dy(wl))
+    rows = np.array([5, 1024, 2999])
+    assert np.array_equal(W.make_residual(wl, rows), r[rows])
