@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--workload", default="c5", choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip timing the unrolled dense GEMM comparator")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip timing the same step captured once in a HIP graph and replayed")
     ap.add_argument("--no-fused", action="store_true",
                     help="skip timing the fused forward epilogue (bias, GELU, residual) against torch ops")
     ap.add_argument("--cpu-rows", type=int, default=0,
@@ -113,13 +115,16 @@ def main():
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
 
-    calls = {
-        "pack": lambda: (eql.eqlinear_pack_weight(w, wp, Dp, Cp, T, code, eql.EQL_PACK_FWD, sptr),
-                         eql.eqlinear_pack_weight(w, wpb, Dp, Cp, T, code, eql.EQL_PACK_BWDX, sptr)),
-        "fwd": lambda: eql.eqlinear_fwd(x, wp, y, N, Cp, Dp, T, code, sptr),
-        "bwd_x": lambda: eql.eqlinear_bwd_x(dy, wpb, dx, N, Cp, Dp, T, code, sptr),
-        "bwd_w": lambda: eql.eqlinear_bwd_w(x, dy, dw, ws, ws_bytes, N, Cp, Dp, T, code, sptr),
-    }
+    def make_calls(sp):
+        return {
+            "pack": lambda: (eql.eqlinear_pack_weight(w, wp, Dp, Cp, T, code, eql.EQL_PACK_FWD, sp),
+                             eql.eqlinear_pack_weight(w, wpb, Dp, Cp, T, code, eql.EQL_PACK_BWDX, sp)),
+            "fwd": lambda: eql.eqlinear_fwd(x, wp, y, N, Cp, Dp, T, code, sp),
+            "bwd_x": lambda: eql.eqlinear_bwd_x(dy, wpb, dx, N, Cp, Dp, T, code, sp),
+            "bwd_w": lambda: eql.eqlinear_bwd_w(x, dy, dw, ws, ws_bytes, N, Cp, Dp, T, code, sp),
+        }
+
+    calls = make_calls(sptr)
     order = ["pack", "fwd", "bwd_x", "bwd_w"]
 
     def step(events=None):
@@ -189,6 +194,32 @@ def main():
     roofline["algorithmic"] = ("%.4g FLOP (%s real GEMMs of N x D' x C') and %.4g bytes (x, y, weight) per launch"
                                % (actual, (2 * T - 2) if T % 2 == 0 else (2 * T - 1), bytes_pass[dom]))
 
+    # The same step captured once in a HIP graph and replayed (the library records only
+    # kernel launches on the caller's stream).  Reported beside the eager figure.
+    graph = None
+    if not args.no_graph:
+        try:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                cap = make_calls(torch.cuda.current_stream().cuda_stream)  # the capturing stream
+                for k in order:
+                    cap[k]()
+            for _ in range(3):
+                g.replay()
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(args.steps):
+                g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            gms = a.elapsed_time(b) / args.steps
+            graph = {"ms_per_step": round(gms, 4),
+                     "value": round(n_passes * dense_eq / (gms * 1e-3) / 1e12, 2), "unit": "TFLOP/s"}
+            del g
+        except Exception as e:  # reported, never fatal: the eager line above is the result
+            graph = {"error": "%s: %s" % (type(e).__name__, e)}
+
     if args.copy_probe_mib > 0:
         nbytes = args.copy_probe_mib << 20
         src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
@@ -242,6 +273,7 @@ def main():
         "pack_ms": round(per["pack"], 4),
         "mfma_frac_step": round(n_passes * actual / (ms_per_step * 1e-3) / 1e12 / MFMA_PEAK[wl.dtype], 4),
         "roofline": roofline,
+        "graph_step": graph,
         "dense_baseline": dense,
         "fused_epilogue": fused,
         "cpu_baseline": cpu,

@@ -375,6 +375,59 @@ def test_misaligned_buffer_is_rejected():
     assert ei.value.status == eql.EQL_EALIGN
 
 
+def test_graph_replay_matches_eager():
+    """One training step (pack, forward, input gradient, weight gradient) captured in a
+    HIP graph and replayed three times.  Between replays the inputs are rewritten in
+    place and other eager work runs; every replay must equal the eager result for the
+    same inputs bit for bit (the library allocates nothing and records no memset, so the
+    captured step is the eager one)."""
+    T, N, Cp, Dp, dtype = 4, 700, 72, 96, "f16"
+    print("case graph replay", flush=True)
+    L = Lib(T, dtype)
+    code = DT[dtype]
+    bufs = [inputs(T, N, Cp, Dp, dtype, seed=60 + i) for i in range(4)]
+    x_d, w_d, dy_d = (dev(a) for a in bufs[0])
+    wp = torch.empty(eql.eqlinear_packed_weight_bytes(Dp, Cp, T, code), dtype=torch.uint8, device=DEV)
+    wpb = torch.empty(eql.eqlinear_packed_weight_bytes(Cp, Dp, T, code), dtype=torch.uint8, device=DEV)
+    y = torch.empty((N, Dp * T), dtype=x_d.dtype, device=DEV)
+    dx = torch.empty((N, Cp * T), dtype=x_d.dtype, device=DEV)
+    dw = torch.empty_like(w_d)
+    nbytes = eql.eqlinear_bwd_w_workspace_bytes(N, Cp, Dp, T, code)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=DEV)
+
+    def step():
+        eql.eqlinear_pack_weight(w_d, wp, Dp, Cp, T, code, eql.EQL_PACK_FWD)
+        eql.eqlinear_pack_weight(w_d, wpb, Dp, Cp, T, code, eql.EQL_PACK_BWDX)
+        eql.eqlinear_fwd(x_d, wp, y, N, Cp, Dp, T, code)
+        eql.eqlinear_bwd_x(dy_d, wpb, dx, N, Cp, Dp, T, code)
+        eql.eqlinear_bwd_w(x_d, dy_d, dw, ws, nbytes, N, Cp, Dp, T, code)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for i in range(1, 4):
+        xh, wh, dyh = bufs[i]
+        x_d.copy_(dev(xh)); w_d.copy_(dev(wh)); dy_d.copy_(dev(dyh))
+        junk = torch.randn(1 << 20, device=DEV).sum()          # other eager work in between
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (y.clone(), dx.clone(), dw.clone())
+        step()                                                  # eager, same inputs
+        torch.cuda.synchronize()
+        for a, b in zip(got, (y, dx, dw)):
+            assert torch.equal(a, b)
+        assert rel_err(host(got[0]), oracle.fwd(xh, wh)) <= TOL[dtype]
+        assert bool(torch.isfinite(junk))
+
+
 def test_layer_fused_forward_matches_oracle():
     from group_circulant_linear_p4_amd.layer import eqlinear_fused
     T, N, Cp, Dp = 4, 3 * 37, 24, 40
