@@ -375,6 +375,46 @@ def test_misaligned_buffer_is_rejected():
     assert ei.value.status == eql.EQL_EALIGN
 
 
+def _sweep_cases(n=30, seed=2024):
+    """Seeded shapes over every T and both dtypes (oracle work <= ~5e8 MACs each), plus
+    large-N / few-channel shapes for which the tile-width model picks two-block tiles."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        T = int(rng.integers(1, 17))
+        dtype = ["f32", "f16"][int(rng.integers(0, 2))]
+        N = int(rng.integers(1, 1500))
+        Cp = int(rng.integers(1, 90))
+        Dp = int(rng.integers(1, 90))
+        if N * Cp * Dp * T * T <= 5e8:
+            cases.append((T, dtype, N, Cp, Dp))
+    cases += [(4, "f16", 14000, 24, 80), (2, "f32", 20000, 16, 60), (1, "f16", 30000, 40, 48),
+              (3, "f16", 17000, 20, 96), (4, "f32", 12800, 96, 40), (4, "f16", 16500, 70, 33)]
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_cases(), ids=lambda c: "T%d_%s_N%d_C%d_D%d" % c)
+def test_random_shape_sweep(case):
+    T, dtype, N, Cp, Dp = case
+    print("case sweep T=%d %s N=%d C'=%d D'=%d" % case, flush=True)
+    x, w, dy = inputs(T, N, Cp, Dp, dtype, seed=N % 97 + T)
+    y, dx, dw = Lib(T, dtype).all_passes(x, w, dy)
+    tol = TOL[dtype]
+    assert rel_err(y, oracle.fwd(x, w)) <= tol
+    assert rel_err(dx, oracle.bwd_x(dy, w)) <= tol
+    assert rel_err(dw, oracle.bwd_w(x, dy, T)) <= tol
+    # The fused epilogue on the same shape (bias + GELU + residual).
+    wl = W.Workload("t", "test", T, N, Cp, Dp, dtype, ("fwd",), seed=3)
+    b, r = W.make_bias(wl), W.make_residual(wl)
+    L = Lib(T, dtype)
+    x_d = dev(x)
+    wp = L.pack(dev(w), Dp, Cp, eql.EQL_PACK_FWD)
+    yf = torch.empty((N, Dp * T), dtype=x_d.dtype, device=DEV)
+    fused_d(T, dtype, x_d, wp, dev(b), dev(r), yf, N, Cp, Dp, "gelu")
+    torch.cuda.synchronize()
+    assert rel_err(host(yf), oracle.fwd_fused(x, w, bias=b, residual=r, act="gelu")) <= tol
+
+
 def test_graph_replay_matches_eager():
     """One training step (pack, forward, input gradient, weight gradient) captured in a
     HIP graph and replayed three times.  Between replays the inputs are rewritten in
