@@ -148,10 +148,14 @@ struct EltT<_Float16> {
   // Clear a 32x32 tile with one MFMA of zero operands (exact +0).  The zero operand
   // comes from a volatile move, so separate tiles get separate MFMAs: a constant
   // would be rematerialised as 16 register writes per tile (and, as generated,
-  // twice).
+  // twice).  An MFMA that reads a VGPR written by a VALU instruction needs wait
+  // states in between, and the compiler's hazard check does not see a VALU write
+  // inside an asm statement (it then emitted a single wait state, and the MFMA
+  // could read the register's previous contents), so the statement carries its
+  // own: five, a margin over the two the hazard requires.
   static __device__ __forceinline__ void zero(f32x16& acc) {
     uint32_t z0;
-    asm volatile("v_mov_b32 %0, 0" : "=v"(z0));
+    asm volatile("v_mov_b32 %0, 0\n\ts_nop 4" : "=v"(z0));
     const f16x8 z = __builtin_bit_cast(f16x8, (u32x4){z0, z0, z0, z0});
     acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(z, z, (f32x16){}, 0, 0, 0);
   }
@@ -178,7 +182,7 @@ struct EltT<float> {
   }
   static __device__ __forceinline__ void zero(f32x16& acc) {  // see EltT<_Float16>::zero
     float z0;
-    asm volatile("v_mov_b32 %0, 0" : "=v"(z0));
+    asm volatile("v_mov_b32 %0, 0\n\ts_nop 4" : "=v"(z0));
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(z0, z0, (f32x16){}, 0, 0, 0);
   }
 };
