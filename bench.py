@@ -310,10 +310,10 @@ def fused_epilogue(torch, eql, x, wp, b, r, y, N, Cp, Dp, T, code, sptr, reps):
         return z
 
     res = {
-        "bias_gelu_ms": timeit(lambda: eql.eqlinear_fwd_fused(x, wp, b, None, y, N, Cp, Dp, T, code,
+        "bias_gelu_ms": timeit(lambda: eql.eqlinear_fwd_fused(x, wp, b, None, y, None, N, Cp, Dp, T, code,
                                                               eql.EQL_ACT_GELU, sptr)),
         "bias_gelu_torch_ms": timeit(lambda: unfused(True, False)),
-        "bias_residual_ms": timeit(lambda: eql.eqlinear_fwd_fused(x, wp, b, r, y, N, Cp, Dp, T, code,
+        "bias_residual_ms": timeit(lambda: eql.eqlinear_fwd_fused(x, wp, b, r, y, None, N, Cp, Dp, T, code,
                                                                   eql.EQL_ACT_NONE, sptr)),
         "bias_residual_torch_ms": timeit(lambda: unfused(False, True)),
     }

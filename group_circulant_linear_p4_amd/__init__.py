@@ -23,6 +23,7 @@ __all__ = [
     "EqlError",
     "lib", "library_path", "eqlinear_abi_version", "eqlinear_status_string",
     "eqlinear_packed_weight_bytes", "eqlinear_pack_weight", "eqlinear_fwd", "eqlinear_fwd_fused", "eqlinear_bwd_x",
+    "eqlinear_fused_epilogue_bwd_workspace_bytes", "eqlinear_fused_epilogue_bwd",
     "eqlinear_bwd_w_workspace_bytes", "eqlinear_bwd_w",
 ]
 
@@ -64,8 +65,12 @@ def lib() -> ctypes.CDLL:
         L.eqlinear_pack_weight.restype = i32
         L.eqlinear_fwd.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, vp]
         L.eqlinear_fwd.restype = i32
-        L.eqlinear_fwd_fused.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp]
+        L.eqlinear_fwd_fused.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp]
         L.eqlinear_fwd_fused.restype = i32
+        L.eqlinear_fused_epilogue_bwd_workspace_bytes.argtypes = [i64, i64, i32, i32]
+        L.eqlinear_fused_epilogue_bwd_workspace_bytes.restype = sz
+        L.eqlinear_fused_epilogue_bwd.argtypes = [vp, vp, vp, vp, vp, sz, i64, i64, i32, i32, i32, vp]
+        L.eqlinear_fused_epilogue_bwd.restype = i32
         L.eqlinear_bwd_x.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, vp]
         L.eqlinear_bwd_x.restype = i32
         L.eqlinear_bwd_w_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
@@ -138,11 +143,23 @@ def eqlinear_fwd(x, w_packed, y, N: int, Cp: int, Dp: int, T: int, dtype, stream
            "eqlinear_fwd")
 
 
-def eqlinear_fwd_fused(x, w_packed, bias, residual, y, N: int, Cp: int, Dp: int, T: int, dtype, act: int,
-                       stream=None) -> None:
-    """bias / residual may be None; residual may be y itself."""
-    _check(lib().eqlinear_fwd_fused(_ptr(x), _ptr(w_packed), _ptr(bias), _ptr(residual), _ptr(y), N, Cp, Dp, T,
-                                    _dtype(dtype), int(act), _stream(stream)), "eqlinear_fwd_fused")
+def eqlinear_fwd_fused(x, w_packed, bias, residual, y, pre_out, N: int, Cp: int, Dp: int, T: int, dtype,
+                       act: int, stream=None) -> None:
+    """bias / residual / pre_out may be None; residual may be y itself."""
+    _check(lib().eqlinear_fwd_fused(_ptr(x), _ptr(w_packed), _ptr(bias), _ptr(residual), _ptr(y), _ptr(pre_out),
+                                    N, Cp, Dp, T, _dtype(dtype), int(act), _stream(stream)), "eqlinear_fwd_fused")
+
+
+def eqlinear_fused_epilogue_bwd_workspace_bytes(N: int, Dp: int, T: int, dtype) -> int:
+    return lib().eqlinear_fused_epilogue_bwd_workspace_bytes(N, Dp, T, _dtype(dtype))
+
+
+def eqlinear_fused_epilogue_bwd(dy, pre, dpre, dbias, workspace, ws_bytes: int, N: int, Dp: int, T: int, dtype,
+                                act: int, stream=None) -> None:
+    """pre may be None without an activation, dbias may be None, dpre may be dy."""
+    _check(lib().eqlinear_fused_epilogue_bwd(_ptr(dy), _ptr(pre), _ptr(dpre), _ptr(dbias), _ptr(workspace),
+                                             int(ws_bytes), N, Dp, T, _dtype(dtype), int(act), _stream(stream)),
+           "eqlinear_fused_epilogue_bwd")
 
 
 def eqlinear_bwd_x(dy, w_packed_bwdx, dx, N: int, Cp: int, Dp: int, T: int, dtype, stream=None) -> None:

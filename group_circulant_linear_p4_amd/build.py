@@ -34,6 +34,7 @@ SOURCES = [
     "eql_bwdw_real_f32.hip",
     "eql_bwdw_pair_f16.hip",
     "eql_bwdw_pair_f32.hip",
+    "eql_epi.hip",
 ]
 
 CFLAGS = [

@@ -76,7 +76,7 @@ int device_cus() {
 // epi: the fused epilogue (bias, act, res); otherwise those are ignored.
 int run_fwd(const void* x, const void* wp, void* y, int64_t N, int64_t Cin, int64_t Dout, int T,
             int dtype, void* stream, bool epi = false, const void* bias = nullptr, const void* res = nullptr,
-            int act = 0) {
+            int act = 0, void* pre = nullptr) {
   int st = check_sizes(N, Cin, Dout, T, dtype);
   if (st != EQL_OK) return st;
   if (N == 0) return EQL_OK;
@@ -130,6 +130,7 @@ int run_fwd(const void* x, const void* wp, void* y, int64_t N, int64_t Cin, int6
     a.x = static_cast<const char*>(x) + (size_t)r0 * inRow;
     a.y = static_cast<char*>(y) + (size_t)r0 * outRow;
     a.res = res ? static_cast<const char*>(res) + (size_t)r0 * outRow : nullptr;
+    a.pre = pre ? static_cast<char*>(pre) + (size_t)r0 * outRow : nullptr;
     a.N = (int)rows;
     a.numTiles = (int)(ceil_div(rows, kFwdRows) * colTiles);
     const unsigned grid = (unsigned)std::min<int64_t>(a.numTiles, cus);
@@ -261,14 +262,57 @@ int eqlinear_fwd(const void* x, const void* w_packed, void* y, int64_t N, int64_
 }
 
 int eqlinear_fwd_fused(const void* x, const void* w_packed, const void* bias, const void* residual,
-                       void* y, int64_t N, int64_t Cp, int64_t Dp, int T, int dtype, int act, void* stream) {
+                       void* y, void* pre_out, int64_t N, int64_t Cp, int64_t Dp, int T, int dtype, int act,
+                       void* stream) {
   if (act != EQL_ACT_NONE && act != EQL_ACT_GELU) return EQL_EINVAL;
   int st = check_sizes(N, Cp, Dp, T, dtype);
   if (st != EQL_OK) return st;
   if (N == 0) return EQL_OK;
   if (bias && (reinterpret_cast<uintptr_t>(bias) % (uintptr_t)elt_bytes(dtype)) != 0) return EQL_EALIGN;
-  if (residual && !aligned16(residual)) return EQL_EALIGN;
-  return run_fwd(x, w_packed, y, N, Cp, Dp, T, dtype, stream, true, bias, residual, act);
+  if ((residual && !aligned16(residual)) || (pre_out && !aligned16(pre_out))) return EQL_EALIGN;
+  return run_fwd(x, w_packed, y, N, Cp, Dp, T, dtype, stream, true, bias, residual, act, pre_out);
+}
+
+size_t eqlinear_fused_epilogue_bwd_workspace_bytes(int64_t N, int64_t Dp, int T, int dtype) {
+  if (check_sizes(N, 1, Dp, T, dtype) != EQL_OK || N == 0) return 0;
+  return (size_t)ceil_div(N, kEpiRows) * (size_t)Dp * sizeof(float);
+}
+
+int eqlinear_fused_epilogue_bwd(const void* dy, const void* pre, void* dpre, void* dbias, void* workspace,
+                                size_t ws_bytes, int64_t N, int64_t Dp, int T, int dtype, int act,
+                                void* stream) {
+  if (act != EQL_ACT_NONE && act != EQL_ACT_GELU) return EQL_EINVAL;
+  int st = check_sizes(N, 1, Dp, T, dtype);
+  if (st != EQL_OK) return st;
+  const int64_t rowBlocks = ceil_div(N, kEpiRows), chBlocks = ceil_div(Dp, kEpiCh);
+  if (rowBlocks * chBlocks > kMaxGrid) return EQL_EINVAL;
+  if (N > 0 && (!dy || !dpre || (act == EQL_ACT_GELU && !pre))) return EQL_EINVAL;
+  if (dbias && N > 0 && (!workspace || ws_bytes < eqlinear_fused_epilogue_bwd_workspace_bytes(N, Dp, T, dtype)))
+    return EQL_EINVAL;
+  if ((dy && !aligned16(dy)) || (pre && !aligned16(pre)) || (dpre && !aligned16(dpre)) ||
+      (workspace && !aligned16(workspace)) ||
+      (dbias && (reinterpret_cast<uintptr_t>(dbias) % (uintptr_t)elt_bytes(dtype)) != 0))
+    return EQL_EALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool f16 = dtype == EQL_F16;
+  EpiBwdArgs a{};
+  a.dy = dy;
+  a.pre = pre;
+  a.dpre = dpre;
+  a.part = dbias && N > 0 ? static_cast<float*>(workspace) : nullptr;
+  a.dbias = dbias;
+  a.N = (int)N;
+  a.Dp = (int)Dp;
+  a.act = act;
+  a.chBlocks = (int)chBlocks;
+  a.rowBlocks = (int)rowBlocks;
+  if (N > 0) {
+    const hipError_t e = launch_epi_bwd(T, f16, a, (unsigned)(rowBlocks * chBlocks), s);
+    if (e != hipSuccess) return EQL_EHIP;
+  }
+  // dbias (zeros when N == 0: no partials to add).
+  if (dbias) return status_of(launch_epi_bias(f16, a, (unsigned)ceil_div(Dp, 256), s));
+  return EQL_OK;
 }
 
 int eqlinear_bwd_x(const void* dy, const void* w_packed_bwdx, void* dx, int64_t N, int64_t Cp,

@@ -50,6 +50,7 @@ struct FwdArgs {
   // Fused epilogue (EPI = 1 instantiations only): y = act(x W^T + bias) + res.
   const void* bias;  // [Dout] or null
   const void* res;   // [N][Dout*T] or null (may equal y)
+  void* pre;         // [N][Dout*T] or null: receives x W^T + bias (the activation's input)
   int act;           // 0 none, 1 GELU
 };
 
@@ -443,6 +444,9 @@ __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
     const __amdgpu_buffer_rsrc_t rr =
         make_rsrc(EPI && a.res ? static_cast<const char*>(a.res) + (size_t)row0 * outRow : nullptr,
                   EPI && a.res ? rows * outRow : 0u);
+    const __amdgpu_buffer_rsrc_t pr =
+        make_rsrc(EPI && a.pre ? static_cast<char*>(a.pre) + (size_t)row0 * outRow : nullptr,
+                  EPI && a.pre ? rows * outRow : 0u);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int col = col0 + nb * 32 + (ln & 31);
@@ -481,9 +485,11 @@ __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
             float rv[T];
             group_from_raw<T, Elt>(rw[j], rv);
 #pragma unroll
+            for (int g = 0; g < T; ++g) yv[g] += bv;
+            if (a.pre) store_group_buf<T, Elt>(pr, off, yv);
+#pragma unroll
             for (int g = 0; g < T; ++g) {
-              float v = yv[g] + bv;
-              if (a.act == 1) v = gelu_erf(v);
+              const float v = a.act == 1 ? gelu_erf(yv[g]) : yv[g];
               yv[g] = v + rv[g];
             }
           }

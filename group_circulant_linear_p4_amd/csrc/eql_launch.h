@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include "eql_bwdw.h"
+#include "eql_epi.h"
 #include "eql_fwd.h"
 #include "eql_pack.h"
 
@@ -37,6 +38,9 @@ hipError_t launch_bwdw_pair_f32(int T, int DB, int CB, const BwdwArgs& a, unsign
 hipError_t launch_bwdw_reduce_f16(int T, int waves, const BwdwReduceArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_bwdw_reduce_f32(int T, int waves, const BwdwReduceArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_pack_f16(int T, const PackArgs& a, unsigned grid, hipStream_t s);
+// Fused-epilogue backward: dpre and the bias partials, then the bias sum.
+hipError_t launch_epi_bwd(int T, bool f16, const EpiBwdArgs& a, unsigned grid, hipStream_t s);
+hipError_t launch_epi_bias(bool f16, const EpiBwdArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_pack_f32(int T, const PackArgs& a, unsigned grid, hipStream_t s);
 
 template <typename A>

@@ -14,7 +14,8 @@ import math
 import torch
 
 from . import (EQL_ACT_GELU, EQL_ACT_NONE, EQL_PACK_BWDX, EQL_PACK_FWD, eqlinear_bwd_w,
-               eqlinear_bwd_w_workspace_bytes, eqlinear_bwd_x, eqlinear_fwd, eqlinear_fwd_fused,
+               eqlinear_bwd_w_workspace_bytes, eqlinear_bwd_x, eqlinear_fused_epilogue_bwd,
+               eqlinear_fused_epilogue_bwd_workspace_bytes, eqlinear_fwd, eqlinear_fwd_fused,
                eqlinear_pack_weight, eqlinear_packed_weight_bytes)
 
 
@@ -68,6 +69,63 @@ def eqlinear(x: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
     return EQLinearFunction.apply(x, w)
 
 
+def _act_code(act):
+    if act in (None, "none"):
+        return EQL_ACT_NONE
+    if act == "gelu":
+        return EQL_ACT_GELU
+    raise ValueError("activation must be None, 'none' or 'gelu'")
+
+
+class EQLinearFusedFunction(torch.autograd.Function):
+    """y = act(x W^T + b), b[D'] shared by the T group elements of each output channel.
+
+    Forward: one eqlinear_fwd_fused launch, which also keeps the activation's input
+    when a gradient will be needed.  Backward: eqlinear_fused_epilogue_bwd (dpre and
+    the bias gradient), then eqlinear_bwd_x and eqlinear_bwd_w on dpre."""
+
+    @staticmethod
+    def forward(ctx, x: torch.Tensor, w: torch.Tensor, b, act):
+        Dp, Cp, T = w.shape
+        if x.shape[-1] != Cp * T:
+            raise ValueError("x has %d features, the weight expects C'*T = %d" % (x.shape[-1], Cp * T))
+        code = _act_code(act)
+        w = w.contiguous()
+        x2 = x.reshape(-1, Cp * T).contiguous()
+        N = x2.shape[0]
+        y = torch.empty((N, Dp * T), dtype=x.dtype, device=x.device)
+        keep = code == EQL_ACT_GELU and any(ctx.needs_input_grad[:3])
+        pre = torch.empty_like(y) if keep else None
+        eqlinear_fwd_fused(x2, _packed(w, EQL_PACK_FWD), b.contiguous() if b is not None else None, None, y, pre,
+                           N, Cp, Dp, T, x.dtype, code)
+        ctx.save_for_backward(x2, w, pre)
+        ctx.code, ctx.has_bias, ctx.lead_shape = code, b is not None, x.shape[:-1]
+        return y.reshape(*x.shape[:-1], Dp * T)
+
+    @staticmethod
+    def backward(ctx, dy: torch.Tensor):
+        x2, w, pre = ctx.saved_tensors
+        Dp, Cp, T = w.shape
+        N = x2.shape[0]
+        dy2 = dy.reshape(-1, Dp * T).to(x2.dtype).contiguous()
+        dpre = torch.empty_like(dy2)
+        db = torch.empty(Dp, dtype=x2.dtype, device=x2.device) if ctx.has_bias and ctx.needs_input_grad[2] else None
+        ws_bytes = eqlinear_fused_epilogue_bwd_workspace_bytes(N, Dp, T, x2.dtype)
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=x2.device)
+        eqlinear_fused_epilogue_bwd(dy2, pre, dpre, db, ws, ws_bytes, N, Dp, T, x2.dtype, ctx.code)
+        dx = dw = None
+        if ctx.needs_input_grad[0]:
+            dx = torch.empty((N, Cp * T), dtype=x2.dtype, device=x2.device)
+            eqlinear_bwd_x(dpre, _packed(w, EQL_PACK_BWDX), dx, N, Cp, Dp, T, x2.dtype)
+            dx = dx.reshape(*ctx.lead_shape, Cp * T)
+        if ctx.needs_input_grad[1]:
+            wsw = eqlinear_bwd_w_workspace_bytes(N, Cp, Dp, T, x2.dtype)
+            wsb = torch.empty(max(wsw, 16), dtype=torch.uint8, device=x2.device)
+            dw = torch.empty_like(w)
+            eqlinear_bwd_w(x2, dpre, dw, wsb, wsw, N, Cp, Dp, T, x2.dtype)
+        return dx, dw, db, None
+
+
 def eqlinear_fused(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None = None,
                    residual: torch.Tensor | None = None, act: str = "none") -> torch.Tensor:
     """Forward only: act(x W^T + bias) + residual in one kernel (eqlinear_fwd_fused), the
@@ -87,7 +145,7 @@ def eqlinear_fused(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None =
     b = bias.contiguous() if bias is not None else None
     r = residual.reshape(N, Dp * T).contiguous() if residual is not None else None
     y = torch.empty((N, Dp * T), dtype=x.dtype, device=x.device)
-    eqlinear_fwd_fused(x2, _packed(w.contiguous(), EQL_PACK_FWD), b, r, y, N, Cp, Dp, T, x.dtype,
+    eqlinear_fwd_fused(x2, _packed(w.contiguous(), EQL_PACK_FWD), b, r, y, None, N, Cp, Dp, T, x.dtype,
                        EQL_ACT_GELU if act == "gelu" else EQL_ACT_NONE)
     return y.reshape(*x.shape[:-1], Dp * T)
 
@@ -95,17 +153,24 @@ def eqlinear_fused(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None =
 class EQLinear(torch.nn.Module):
     """Equivariant linear layer over C_T: in_channels*T -> out_channels*T features."""
 
-    def __init__(self, in_channels: int, out_channels: int, group_order: int = 4, device=None, dtype=None):
+    def __init__(self, in_channels: int, out_channels: int, group_order: int = 4, bias: bool = False,
+                 activation: str | None = None, device=None, dtype=None):
         super().__init__()
         self.in_channels, self.out_channels, self.group_order = in_channels, out_channels, group_order
+        _act_code(activation)
+        self.activation = activation
         self.weight = torch.nn.Parameter(torch.empty(out_channels, in_channels, group_order, device=device,
                                                      dtype=dtype))
+        # One bias per output channel, shared by its group elements (equivariant).
+        self.bias = torch.nn.Parameter(torch.zeros(out_channels, device=device, dtype=dtype)) if bias else None
         with torch.no_grad():
             self.weight.normal_(0.0, 1.0 / math.sqrt(in_channels * group_order))
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
-        return EQLinearFunction.apply(x, self.weight)
+        if self.bias is None and self.activation in (None, "none"):
+            return EQLinearFunction.apply(x, self.weight)
+        return EQLinearFusedFunction.apply(x, self.weight, self.bias, self.activation)
 
     def extra_repr(self) -> str:
-        return "in_channels=%d, out_channels=%d, group_order=%d" % (self.in_channels, self.out_channels,
-                                                                    self.group_order)
+        return "in_channels=%d, out_channels=%d, group_order=%d, bias=%s, activation=%s" % (
+            self.in_channels, self.out_channels, self.group_order, self.bias is not None, self.activation)

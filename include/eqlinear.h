@@ -135,13 +135,44 @@ int eqlinear_fwd(const void* x, const void* w_packed, void* y, int64_t N, int64_
  * residual: [N][Dp*T] elements of `dtype`, or NULL; 16-byte aligned.  It may be
  *   the same buffer as y (an in-place residual add); any other overlap with y is
  *   undefined.
+ * pre_out: [N][Dp*T] elements of `dtype`, or NULL; 16-byte aligned.  When given it
+ *   receives x W^T + bias (the activation's input, rounded once), which
+ *   eqlinear_fused_epilogue_bwd needs for training.
  * The bias, the activation and the residual are applied in fp32 to the fp32
  * result of the inverse transform; y is rounded once.  bias = residual = NULL
  * with EQL_ACT_NONE gives exactly eqlinear_fwd's result.
  */
 int eqlinear_fwd_fused(const void* x, const void* w_packed, const void* bias,
-                       const void* residual, void* y, int64_t N, int64_t Cp, int64_t Dp,
-                       int T, int dtype, int act, void* stream);
+                       const void* residual, void* y, void* pre_out, int64_t N, int64_t Cp,
+                       int64_t Dp, int T, int dtype, int act, void* stream);
+
+/*
+ * Scratch bytes eqlinear_fused_epilogue_bwd needs for the bias gradient: fp32 partial
+ * sums, one row of Dp per block of 256 rows (0 when N == 0 or the arguments are
+ * invalid).
+ */
+size_t eqlinear_fused_epilogue_bwd_workspace_bytes(int64_t N, int64_t Dp, int T, int dtype);
+
+/*
+ * Backward of eqlinear_fwd_fused's epilogue (the training side of "Nivel de Rede"):
+ *     dpre[n][d*T+g] = dy[n][d*T+g] * act'(pre[n][d*T+g])     (act' = 1 for EQL_ACT_NONE)
+ *     dbias[d]       = sum_n sum_g dpre[n][d*T+g]
+ * GELU'(v) = Phi(v) + v phi(v), phi the standard normal density.  dx and dw of the
+ * layer then come from eqlinear_bwd_x and eqlinear_bwd_w applied to dpre; the
+ * residual's gradient is dy itself.
+ * dy, pre: [N][Dp*T] read (pre only with EQL_ACT_GELU, else it may be NULL);
+ * dpre: [N][Dp*T] written, may be the same buffer as dy; dbias: [Dp] written, or NULL
+ * (no bias gradient; zeros when N == 0); workspace: at least
+ * eqlinear_fused_epilogue_bwd_workspace_bytes bytes when dbias is given.  All in
+ * `dtype`, 16-byte aligned (dbias: element-aligned).  dpre is computed in fp32 and
+ * rounded once; dbias adds the unrounded fp32 values, per block of rows and then over
+ * the blocks in a fixed order (deterministic).  Errors as the other entry points;
+ * EQL_EINVAL also for an unknown act, a missing pre with EQL_ACT_GELU or a short
+ * workspace.
+ */
+int eqlinear_fused_epilogue_bwd(const void* dy, const void* pre, void* dpre, void* dbias,
+                                void* workspace, size_t ws_bytes, int64_t N, int64_t Dp, int T,
+                                int dtype, int act, void* stream);
 
 /*
  * Input gradient: dx = dy W.  dy: [N][Dp*T] read; w_packed_bwdx: the

@@ -11,6 +11,8 @@ from .eqlinear_oracle import (  # noqa: F401
     half_spectrum,
     gelu,
     fwd_fused,
+    gelu_grad,
+    fused_epilogue_bwd,
     real_gemm_count,
     actual_flops,
     dense_equivalent_flops,

@@ -29,6 +29,9 @@ Functions:
   gelu(v)              v * Phi(v), the exact (erf) form
   fwd_fused(x, w, bias, residual, act)
                        y = act(x W^T + bias broadcast over g) + residual
+  gelu_grad(v)         Phi(v) + v phi(v)
+  fused_epilogue_bwd(dy, pre, T, act)
+                       dpre = dy * act'(pre), dbias = sum of dpre over rows and g
   real_gemm_count(T)   per-frequency real products after conjugate symmetry
 """
 from __future__ import annotations
@@ -135,6 +138,30 @@ def fwd_fused(x, w, bias=None, residual=None, act: str = "none") -> np.ndarray:
     if residual is not None:
         y = y + _f64(residual)
     return y
+
+
+def gelu_grad(v) -> np.ndarray:
+    """Derivative of v * Phi(v): Phi(v) + v * phi(v), phi the standard normal density."""
+    from scipy.special import erf
+    v = _f64(v)
+    return 0.5 * (1.0 + erf(v / np.sqrt(2.0))) + v * np.exp(-0.5 * v * v) / np.sqrt(2.0 * np.pi)
+
+
+def fused_epilogue_bwd(dy, pre, T: int, act: str = "none"):
+    """Chain rule through y = act(pre) + r with pre = x W^T + b (b shared over g):
+    dpre = dy * act'(pre) and dbias[d] = sum over rows n and group elements g of
+    dpre[n, d*T+g].  The input and weight gradients are bwd_x / bwd_w applied to dpre;
+    the residual's gradient is dy."""
+    dy = _f64(dy)
+    if act == "gelu":
+        dpre = dy * gelu_grad(pre)
+    elif act == "none":
+        dpre = dy.copy()
+    else:
+        raise ValueError("act must be 'none' or 'gelu'")
+    N, DT = dpre.shape
+    dbias = dpre.reshape(N, DT // T, T).sum(axis=(0, 2))
+    return dpre, dbias
 
 
 def half_spectrum(v) -> np.ndarray:

@@ -26,7 +26,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_function():
     L = eql.lib()
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 11
     for n in names:
         assert hasattr(L, n), "missing export %s" % n
         assert hasattr(eql, n), "binding lacks %s" % n
@@ -106,16 +106,37 @@ def test_fwd_fused_validation():
     GELU = eql.EQL_ACT_GELU
     x, wp, y = A16, A16B, A16 + 0x1000
     fn = "eqlinear_fwd_fused"
-    assert raw(fn, x, wp, None, None, y, 8, 4, 4, 4, F16, 2, None) == eql.EQL_EINVAL        # act
-    assert raw(fn, x, wp, None, None, y, 8, 4, 4, 4, F16, -1, None) == eql.EQL_EINVAL       # act
-    assert raw(fn, x, wp, None, None, y, 8, 4, 4, 4, 5, GELU, None) == eql.EQL_EINVAL       # dtype
-    assert raw(fn, x, wp, None, None, y, 8, 4, 4, 17, F16, GELU, None) == eql.EQL_EUNSUPPORTED
-    assert raw(fn, None, wp, None, None, y, 8, 4, 4, 4, F16, GELU, None) == eql.EQL_EINVAL
-    assert raw(fn, x, wp, A16 + 1, None, y, 8, 4, 4, 4, F16, GELU, None) == eql.EQL_EALIGN  # bias, fp16
-    assert raw(fn, x, wp, A16 + 2, None, y, 8, 4, 4, 4, F32, GELU, None) == eql.EQL_EALIGN  # bias, fp32
-    assert raw(fn, x, wp, None, MIS, y, 8, 4, 4, 4, F16, GELU, None) == eql.EQL_EALIGN      # residual
-    assert raw(fn, MIS, wp, None, None, y, 8, 4, 4, 4, F16, GELU, None) == eql.EQL_EALIGN
-    assert raw(fn, None, None, None, None, None, 0, 4, 4, 4, F16, GELU, None) == eql.EQL_OK
+    assert raw(fn, x, wp, None, None, y, None, 8, 4, 4, 4, F16, 2, None) == eql.EQL_EINVAL       # act
+    assert raw(fn, x, wp, None, None, y, None, 8, 4, 4, 4, F16, -1, None) == eql.EQL_EINVAL      # act
+    assert raw(fn, x, wp, None, None, y, None, 8, 4, 4, 4, 5, GELU, None) == eql.EQL_EINVAL      # dtype
+    assert raw(fn, x, wp, None, None, y, None, 8, 4, 4, 17, F16, GELU, None) == eql.EQL_EUNSUPPORTED
+    assert raw(fn, None, wp, None, None, y, None, 8, 4, 4, 4, F16, GELU, None) == eql.EQL_EINVAL
+    assert raw(fn, x, wp, A16 + 1, None, y, None, 8, 4, 4, 4, F16, GELU, None) == eql.EQL_EALIGN  # bias
+    assert raw(fn, x, wp, A16 + 2, None, y, None, 8, 4, 4, 4, F32, GELU, None) == eql.EQL_EALIGN  # bias
+    assert raw(fn, x, wp, None, MIS, y, None, 8, 4, 4, 4, F16, GELU, None) == eql.EQL_EALIGN     # residual
+    assert raw(fn, x, wp, None, None, y, MIS, 8, 4, 4, 4, F16, GELU, None) == eql.EQL_EALIGN     # pre_out
+    assert raw(fn, MIS, wp, None, None, y, None, 8, 4, 4, 4, F16, GELU, None) == eql.EQL_EALIGN
+    assert raw(fn, None, None, None, None, None, None, 0, 4, 4, 4, F16, GELU, None) == eql.EQL_OK
+
+
+def test_fused_epilogue_bwd_validation():
+    F16, F32 = eql.EQL_F16, eql.EQL_F32
+    GELU, NONE = eql.EQL_ACT_GELU, eql.EQL_ACT_NONE
+    fn = "eqlinear_fused_epilogue_bwd"
+    dy, pre, dpre, db, ws = A16, A16B, A16 + 0x1000, A16 + 0x2000, A16 + 0x3000
+    need = eql.eqlinear_fused_epilogue_bwd_workspace_bytes(300, 5, 4, F16)
+    assert need == 2 * 5 * 4                                                                  # 2 row blocks
+    assert eql.eqlinear_fused_epilogue_bwd_workspace_bytes(0, 5, 4, F16) == 0
+    assert raw(fn, dy, pre, dpre, db, ws, need, 300, 5, 4, F16, 3, None) == eql.EQL_EINVAL      # act
+    assert raw(fn, dy, None, dpre, db, ws, need, 300, 5, 4, F16, GELU, None) == eql.EQL_EINVAL  # pre needed
+    assert raw(fn, dy, pre, dpre, db, ws, need - 1, 300, 5, 4, F16, GELU, None) == eql.EQL_EINVAL   # short ws
+    assert raw(fn, dy, pre, dpre, db, None, need, 300, 5, 4, F16, GELU, None) == eql.EQL_EINVAL  # no ws
+    assert raw(fn, None, pre, dpre, db, ws, need, 300, 5, 4, F16, GELU, None) == eql.EQL_EINVAL
+    assert raw(fn, dy, pre, None, db, ws, need, 300, 5, 4, F16, GELU, None) == eql.EQL_EINVAL
+    assert raw(fn, dy, pre, dpre, db, ws, need, 300, 5, 17, F16, GELU, None) == eql.EQL_EUNSUPPORTED
+    assert raw(fn, MIS, pre, dpre, db, ws, need, 300, 5, 4, F16, GELU, None) == eql.EQL_EALIGN
+    assert raw(fn, dy, pre, dpre, A16 + 2, ws, need, 300, 5, 4, F32, NONE, None) == eql.EQL_EALIGN
+    assert raw(fn, dy, pre, dpre, db, ws, need, 300, 0, 4, F16, GELU, None) == eql.EQL_EINVAL   # D' < 1
 
 
 def test_pack_validation():

@@ -189,7 +189,7 @@ def test_two_block_tile(T, dtype):
 
 # -------------------------------------------------------------- fused epilogue
 def fused_d(T, dtype, x_d, wp, b_d, r_d, y, N, Cp, Dp, act):
-    eql.eqlinear_fwd_fused(x_d, wp, b_d, r_d, y, N, Cp, Dp, T, DT[dtype],
+    eql.eqlinear_fwd_fused(x_d, wp, b_d, r_d, y, None, N, Cp, Dp, T, DT[dtype],
                            eql.EQL_ACT_GELU if act == "gelu" else eql.EQL_ACT_NONE)
     return y
 
@@ -415,6 +415,58 @@ def test_random_shape_sweep(case):
     assert rel_err(host(yf), oracle.fwd_fused(x, w, bias=b, residual=r, act="gelu")) <= tol
 
 
+def epi_bwd_d(T, dtype, dy_d, pre_d, dpre, with_bias, N, Dp, act):
+    code = DT[dtype]
+    nbytes = eql.eqlinear_fused_epilogue_bwd_workspace_bytes(N, Dp, T, code)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=DEV)
+    db = torch.empty(Dp, dtype=dy_d.dtype, device=DEV) if with_bias else None
+    eql.eqlinear_fused_epilogue_bwd(dy_d, pre_d, dpre, db, ws, nbytes, N, Dp, T, code,
+                                    eql.EQL_ACT_GELU if act == "gelu" else eql.EQL_ACT_NONE)
+    return db
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("T", [3, 4, 8])
+@pytest.mark.parametrize("act", ["gelu", "none"])
+def test_fused_epilogue_bwd_matches_oracle(T, dtype, act):
+    N, Dp = 700, 70                               # 3 row blocks x 2 channel blocks, ragged
+    print("case epilogue bwd T=%d %s %s" % (T, dtype, act), flush=True)
+    wl = W.Workload("t", "test", T, N, 8, Dp, dtype, ("fwd",), seed=31 + T)
+    dy, pre = W.make_dy(wl), W.make_residual(wl)
+    dy_d, pre_d = dev(dy), dev(pre)
+    dpre = torch.empty_like(dy_d)
+    db = epi_bwd_d(T, dtype, dy_d, pre_d if act == "gelu" else None, dpre, True, N, Dp, act)
+    torch.cuda.synchronize()
+    ref_dpre, ref_db = oracle.fused_epilogue_bwd(dy, pre, T, act=act)
+    assert rel_err(host(dpre), ref_dpre) <= TOL[dtype]
+    assert rel_err(host(db), ref_db) <= TOL[dtype]
+    # In place (dpre = dy) gives the same result.
+    dyi = dy_d.clone()
+    epi_bwd_d(T, dtype, dyi, pre_d if act == "gelu" else None, dyi, False, N, Dp, act)
+    torch.cuda.synchronize()
+    assert torch.equal(dyi, dpre)
+
+
+def test_fused_epilogue_bwd_empty_and_pre_out():
+    """N = 0 writes a zero bias gradient; pre_out of the fused forward is x W^T + b."""
+    dy_d = torch.empty((0, 40), dtype=torch.float32, device=DEV)
+    db = epi_bwd_d(4, "f32", dy_d, None, dy_d, True, 0, 10, "none")
+    torch.cuda.synchronize()
+    assert torch.equal(db, torch.zeros(10, device=DEV))
+    T, N, Cp, Dp, dtype = 4, 333, 24, 50, "f16"
+    wl = W.Workload("t", "test", T, N, Cp, Dp, dtype, ("fwd",), seed=12)
+    x, w, b = W.make_x(wl), W.make_w(wl), W.make_bias(wl)
+    L = Lib(T, dtype)
+    x_d = dev(x)
+    wp = L.pack(dev(w), Dp, Cp, eql.EQL_PACK_FWD)
+    y = torch.empty((N, Dp * T), dtype=x_d.dtype, device=DEV)
+    pre = torch.empty_like(y)
+    eql.eqlinear_fwd_fused(x_d, wp, dev(b), None, y, pre, N, Cp, Dp, T, DT[dtype], eql.EQL_ACT_GELU)
+    torch.cuda.synchronize()
+    assert rel_err(host(pre), oracle.fwd_fused(x, w, bias=b)) <= TOL[dtype]
+    assert rel_err(host(y), oracle.fwd_fused(x, w, bias=b, act="gelu")) <= TOL[dtype]
+
+
 def test_graph_replay_matches_eager():
     """One training step (pack, forward, input gradient, weight gradient) captured in a
     HIP graph and replayed three times.  Between replays the inputs are rewritten in
@@ -480,6 +532,30 @@ def test_layer_fused_forward_matches_oracle():
     assert rel_err(host(y).reshape(N, Dp * T), ref) <= TOL["f32"]
     with pytest.raises(RuntimeError):
         eqlinear_fused(dev(x).requires_grad_(), dev(w), act="gelu")
+
+
+def test_layer_bias_gelu_training_matches_oracle():
+    """EQLinear(bias=True, activation='gelu'): the fused forward and the epilogue
+    backward + input and weight gradients against the oracle's chain rule."""
+    from group_circulant_linear_p4_amd.layer import EQLinear
+    T, N, Cp, Dp = 4, 260, 20, 36
+    print("case layer bias+gelu training", flush=True)
+    layer = EQLinear(Cp, Dp, T, bias=True, activation="gelu", device=DEV, dtype=torch.float32)
+    wl = W.Workload("t", "test", T, N, Cp, Dp, "f32", ("fwd",), seed=44)
+    with torch.no_grad():
+        layer.bias.copy_(dev(W.make_bias(wl)))
+    xn, dyn = W.make_x(wl), W.make_dy(wl)
+    x = dev(xn).requires_grad_()
+    y = layer(x)
+    y.backward(dev(dyn))
+    torch.cuda.synchronize()
+    w, b = host(layer.weight.detach()), host(layer.bias.detach())
+    assert rel_err(host(y.detach()), oracle.fwd_fused(xn, w, bias=b, act="gelu")) <= 1e-5
+    pre = oracle.fwd_fused(xn, w, bias=b)
+    dpre, db = oracle.fused_epilogue_bwd(dyn, pre, T, act="gelu")
+    assert rel_err(host(layer.bias.grad), db) <= 1e-5
+    assert rel_err(host(x.grad), oracle.bwd_x(dpre, w)) <= 1e-5
+    assert rel_err(host(layer.weight.grad), oracle.bwd_w(xn, dpre, T)) <= 1e-5
 
 
 def test_layer_autograd_matches_oracle():

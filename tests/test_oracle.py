@@ -28,7 +28,8 @@ def rand(*shape):
 
 def _ns(**over):
     base = dict(unroll=O.unroll, fwd=O.fwd, bwd_x=O.bwd_x, bwd_w=O.bwd_w, half_spectrum=O.half_spectrum,
-                gelu=O.gelu, fwd_fused=O.fwd_fused)
+                gelu=O.gelu, fwd_fused=O.fwd_fused, gelu_grad=O.gelu_grad,
+                fused_epilogue_bwd=O.fused_epilogue_bwd)
     base.update(over)
     return types.SimpleNamespace(**base)
 
@@ -175,9 +176,60 @@ def pin_fused_reduces_to_fwd(o, T=4, N=4, Cp=3, Dp=2):
     return bool(np.array_equal(o.fwd_fused(x, w), o.fwd(x, w)))
 
 
+def pin_gelu_grad_finite_difference(o):
+    """GELU' against central differences of GELU itself (error O(h^2) ~ 1e-10)."""
+    v = np.linspace(-5.0, 5.0, 81)
+    h = 1e-5
+    fd = (o.gelu(v + h) - o.gelu(v - h)) / (2 * h)
+    return bool(np.allclose(o.gelu_grad(v), fd, atol=1e-8))
+
+
+def pin_gelu_grad_identities(o):
+    """GELU'(v) + GELU'(-v) = 1 (Phi(v) + Phi(-v) = 1, phi even) and GELU'(0) = 1/2."""
+    v = np.linspace(-6.0, 6.0, 61)
+    return bool(np.allclose(o.gelu_grad(v) + o.gelu_grad(-v), 1.0, atol=1e-12) and
+                abs(o.gelu_grad(np.array([0.0]))[0] - 0.5) < 1e-15)
+
+
+def pin_epilogue_bwd_loops(o, T=3, N=4, Dp=2):
+    """dbias by plain loops, dpre elementwise."""
+    dy, pre = rand(N, Dp * T), rand(N, Dp * T)
+    dpre, db = o.fused_epilogue_bwd(dy, pre, T, act="gelu")
+    g = o.gelu_grad(pre)
+    for d in range(Dp):
+        want = sum(dy[n, d * T + k] * g[n, d * T + k] for n in range(N) for k in range(T))
+        if abs(db[d] - want) > 1e-12 * max(1.0, abs(want)):
+            return False
+    return bool(np.allclose(dpre, dy * g, atol=1e-14))
+
+
+def pin_fused_layer_autograd(o, T=4, N=5, Cp=3, Dp=2):
+    """The whole training step of y = gelu(x W^T + b) + r through torch autograd in
+    fp64: conv1d layer, F.gelu (exact form), bias broadcast over g."""
+    x = torch.tensor(rand(N, Cp * T), requires_grad=True)
+    w = torch.tensor(rand(Dp, Cp, T), requires_grad=True)
+    b = torch.tensor(rand(Dp), requires_grad=True)
+    r = torch.tensor(rand(N, Dp * T), requires_grad=True)
+    dy = torch.tensor(rand(N, Dp * T))
+    pre_t = _torch_layer(x, w, T) + b.repeat_interleave(T)
+    y = torch.nn.functional.gelu(pre_t) + r
+    y.backward(dy)
+    xn, wn, bn, rn = (t.detach().numpy() for t in (x, w, b, r))
+    ok = np.allclose(o.fwd_fused(xn, wn, bias=bn, residual=rn, act="gelu"), y.detach().numpy(), atol=1e-12)
+    pre = o.fwd_fused(xn, wn, bias=bn)
+    dpre, db = o.fused_epilogue_bwd(dy.numpy(), pre, T, act="gelu")
+    ok &= np.allclose(db, b.grad.numpy(), atol=1e-10)
+    ok &= np.allclose(o.bwd_x(dpre, wn), x.grad.numpy(), atol=1e-10)
+    ok &= np.allclose(o.bwd_w(xn, dpre, T), w.grad.numpy(), atol=1e-10)
+    ok &= np.allclose(dy.numpy(), r.grad.numpy())
+    return bool(ok)
+
+
 ALL_PINS = [pin_golden, pin_circulant, pin_torch_autograd, pin_fft, pin_adjoint,
             pin_weight_gradient, pin_equivariance, pin_spectrum, pin_gelu_table, pin_gelu_odd_part,
-            pin_fused_brute_force, pin_fused_equivariance, pin_fused_reduces_to_fwd]
+            pin_fused_brute_force, pin_fused_equivariance, pin_fused_reduces_to_fwd,
+            pin_gelu_grad_finite_difference, pin_gelu_grad_identities, pin_epilogue_bwd_loops,
+            pin_fused_layer_autograd]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
@@ -395,7 +447,21 @@ def _mut_fused_residual_first(x, w, bias=None, residual=None, act="none"):
     return O.gelu(y) if act == "gelu" else y
 
 
+def _mut_gelu_grad_no_density(v):
+    from scipy.special import erf
+    v = np.asarray(v, dtype=np.float64)
+    return 0.5 * (1.0 + erf(v / np.sqrt(2.0)))                             # Phi only, v*phi dropped
+
+
+def _mut_epilogue_bwd_bias_over_channels(dy, pre, T, act="none"):
+    dpre, _ = O.fused_epilogue_bwd(dy, pre, T, act)
+    N, DT = dpre.shape
+    return dpre, dpre.reshape(N, T, DT // T).sum(axis=(0, 1))              # wrong grouping of d, g
+
+
 MUTANTS = {
+    "gelu_grad_without_density_term": dict(gelu_grad=_mut_gelu_grad_no_density),
+    "epilogue_bwd_bias_wrong_grouping": dict(fused_epilogue_bwd=_mut_epilogue_bwd_bias_over_channels),
     "fused_bias_tiled_over_channels": dict(fwd_fused=_mut_fused_bias_tiled),
     "gelu_tanh_approximation": dict(gelu=_mut_gelu_tanh),
     "fused_residual_before_activation": dict(fwd_fused=_mut_fused_residual_first),
