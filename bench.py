@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--no-graph", action="store_true",
                     help="skip timing the same step captured once in a HIP graph and replayed")
     ap.add_argument("--no-fused", action="store_true",
-                    help="skip timing the fused forward epilogue (bias, GELU, residual) against torch ops")
+                    help="skip timing the fused epilogue (bias, GELU, residual; and its backward) against torch ops")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows of the CPU-oracle sample (0: sized to about 12 s of work)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -317,10 +317,34 @@ def fused_epilogue(torch, eql, x, wp, b, r, y, N, Cp, Dp, T, code, sptr, reps):
                                                                   eql.EQL_ACT_NONE, sptr)),
         "bias_residual_torch_ms": timeit(lambda: unfused(False, True)),
     }
+    # Training: the forward also keeps the activation's input, and the backward of the
+    # epilogue (dpre = dy * GELU'(pre), dbias) runs before the layer's input and weight
+    # gradients.  Torch's counterpart: its GELU backward and a channel sum.
+    pre = torch.empty_like(y)
+    dpre = torch.empty_like(y)
+    db = torch.empty_like(b)
+    ws_bytes = eql.eqlinear_fused_epilogue_bwd_workspace_bytes(N, Dp, T, code)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=y.device)
+    res["bias_gelu_pre_out_ms"] = timeit(lambda: eql.eqlinear_fwd_fused(x, wp, b, None, y, pre, N, Cp, Dp, T, code,
+                                                                        eql.EQL_ACT_GELU, sptr))
+
+    def torch_epi_bwd():
+        g = torch.ops.aten.gelu_backward(r, pre)
+        return g, g.view(N, Dp, T).sum(dim=(0, 2))
+
+    res["epilogue_bwd_ms"] = timeit(lambda: eql.eqlinear_fused_epilogue_bwd(r, pre, dpre, db, ws, ws_bytes, N, Dp, T,
+                                                                            code, eql.EQL_ACT_GELU, sptr))
+    res["epilogue_bwd_torch_ms"] = timeit(torch_epi_bwd)
+    # dy and pre read, dpre written once each (the bias partials are 1/64 of that).
+    epi_bytes = 3 * N * Dp * T * y.element_size()
+    del pre, dpre, db, ws
     res = {k: round(v, 4) for k, v in res.items()}
     res["speedup_bias_gelu"] = round(res["bias_gelu_torch_ms"] / res["bias_gelu_ms"], 3)
     res["speedup_bias_residual"] = round(res["bias_residual_torch_ms"] / res["bias_residual_ms"], 3)
-    res["kind"] = "eqlinear_fwd_fused vs eqlinear_fwd + torch (y + b), F.gelu, + residual"
+    res["speedup_epilogue_bwd"] = round(res["epilogue_bwd_torch_ms"] / res["epilogue_bwd_ms"], 3)
+    res["epilogue_bwd_GBps"] = round(epi_bytes / (res["epilogue_bwd_ms"] * 1e-3) / 1e9, 1)
+    res["kind"] = ("eqlinear_fwd_fused vs eqlinear_fwd + torch (y + b), F.gelu, + residual; "
+                   "eqlinear_fused_epilogue_bwd vs torch gelu_backward + channel sum")
     torch.cuda.empty_cache()
     return res
 
