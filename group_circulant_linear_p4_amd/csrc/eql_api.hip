@@ -273,9 +273,32 @@ int eqlinear_fwd_fused(const void* x, const void* w_packed, const void* bias, co
   return run_fwd(x, w_packed, y, N, Cp, Dp, T, dtype, stream, true, bias, residual, act, pre_out);
 }
 
+// Launch shape of the epilogue backward: chunk width W (the widest power of two, up
+// to 16 bytes, dividing a row), 64 chunks across per workgroup, and rows per
+// workgroup halved from 1024 (down to 16) until the grid has 2048 workgroups (eight
+// per compute unit) or more.  The bias partials take one fp32 per row block and
+// element position.
+struct EpiPlan {
+  int W;
+  int64_t rowsPerBlock, rowBlocks, chunkBlocks;
+  size_t partBytes;
+};
+
+EpiPlan plan_epi(int64_t N, int64_t Dp, int T, int dtype) {
+  EpiPlan p{};
+  const int64_t rowBytes = Dp * T * elt_bytes(dtype);
+  p.W = pow2_part((int)(rowBytes % 16 == 0 ? 16 : rowBytes % 16));
+  p.chunkBlocks = ceil_div(rowBytes / p.W, 64);
+  p.rowsPerBlock = 1024;
+  while (p.rowsPerBlock > 16 && ceil_div(N, p.rowsPerBlock) * p.chunkBlocks < 2048) p.rowsPerBlock /= 2;
+  p.rowBlocks = ceil_div(N, p.rowsPerBlock);
+  p.partBytes = (size_t)p.rowBlocks * (size_t)(Dp * T) * sizeof(float);
+  return p;
+}
+
 size_t eqlinear_fused_epilogue_bwd_workspace_bytes(int64_t N, int64_t Dp, int T, int dtype) {
   if (check_sizes(N, 1, Dp, T, dtype) != EQL_OK || N == 0) return 0;
-  return (size_t)ceil_div(N, kEpiRows) * (size_t)Dp * sizeof(float);
+  return plan_epi(N, Dp, T, dtype).partBytes;
 }
 
 int eqlinear_fused_epilogue_bwd(const void* dy, const void* pre, void* dpre, void* dbias, void* workspace,
@@ -284,11 +307,10 @@ int eqlinear_fused_epilogue_bwd(const void* dy, const void* pre, void* dpre, voi
   if (act != EQL_ACT_NONE && act != EQL_ACT_GELU) return EQL_EINVAL;
   int st = check_sizes(N, 1, Dp, T, dtype);
   if (st != EQL_OK) return st;
-  const int64_t rowBlocks = ceil_div(N, kEpiRows), chBlocks = ceil_div(Dp, kEpiCh);
-  if (rowBlocks * chBlocks > kMaxGrid) return EQL_EINVAL;
+  const EpiPlan p = plan_epi(N, Dp, T, dtype);
+  if (p.rowBlocks * p.chunkBlocks > kMaxGrid) return EQL_EINVAL;
   if (N > 0 && (!dy || !dpre || (act == EQL_ACT_GELU && !pre))) return EQL_EINVAL;
-  if (dbias && N > 0 && (!workspace || ws_bytes < eqlinear_fused_epilogue_bwd_workspace_bytes(N, Dp, T, dtype)))
-    return EQL_EINVAL;
+  if (dbias && N > 0 && (!workspace || ws_bytes < p.partBytes)) return EQL_EINVAL;
   if ((dy && !aligned16(dy)) || (pre && !aligned16(pre)) || (dpre && !aligned16(dpre)) ||
       (workspace && !aligned16(workspace)) ||
       (dbias && (reinterpret_cast<uintptr_t>(dbias) % (uintptr_t)elt_bytes(dtype)) != 0))
@@ -303,11 +325,14 @@ int eqlinear_fused_epilogue_bwd(const void* dy, const void* pre, void* dpre, voi
   a.dbias = dbias;
   a.N = (int)N;
   a.Dp = (int)Dp;
+  a.T = T;
   a.act = act;
-  a.chBlocks = (int)chBlocks;
-  a.rowBlocks = (int)rowBlocks;
+  a.rowElems = (int)(Dp * T);
+  a.rowsPerBlock = (int)p.rowsPerBlock;
+  a.chunkBlocks = (int)p.chunkBlocks;
+  a.rowBlocks = N > 0 ? (int)p.rowBlocks : 0;
   if (N > 0) {
-    const hipError_t e = launch_epi_bwd(T, f16, a, (unsigned)(rowBlocks * chBlocks), s);
+    const hipError_t e = launch_epi_bwd(f16, p.W, a, (unsigned)(p.rowBlocks * p.chunkBlocks), s);
     if (e != hipSuccess) return EQL_EHIP;
   }
   // dbias (zeros when N == 0: no partials to add).

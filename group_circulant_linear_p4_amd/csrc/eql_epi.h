@@ -5,6 +5,12 @@
 //   dbias[d]       = sum over n and g of dpre[n][d*T+g]
 // The input and weight gradients of the layer then follow from the input-gradient and
 // weight-gradient kernels applied to dpre; the residual's gradient is dy itself.
+//
+// The first part is elementwise, so the kernel streams each row as a flat array in
+// chunks of W bytes (the widest power of two, up to 16, dividing the row), with no
+// regard to group boundaries.  The bias sum is kept per element position: each
+// workgroup writes the column sums of its row block, and the bias kernel adds, for
+// channel d, the T positions d*T .. d*T+T-1 of every row block in a fixed order.
 #pragma once
 
 #include "eql_device.h"
@@ -16,67 +22,168 @@ struct EpiBwdArgs {
   const void* dy;    // [N][Dp*T]
   const void* pre;   // [N][Dp*T] (read only with an activation)
   void* dpre;        // [N][Dp*T] (may be dy)
-  float* part;       // [rowBlocks][Dp] fp32 bias partials, or null (no bias gradient)
+  float* part;       // [rowBlocks][Dp*T] fp32 column sums, or null (no bias gradient)
   void* dbias;       // [Dp]
-  int N, Dp, act, chBlocks, rowBlocks;
+  int N, Dp, T, act;
+  int rowElems;      // Dp*T
+  int rowsPerBlock;  // rows of one workgroup (a multiple of 4)
+  int chunkBlocks;   // workgroups across a row (64 chunks each)
+  int rowBlocks;
 };
 
-constexpr int kEpiRows = 256;  // rows per workgroup
-constexpr int kEpiCh = 64;     // output channels per workgroup
-
-// GELU'(v) = Phi(v) + v phi(v), phi the standard normal density, in fp32 (erf as in
-// the forward; exp(-v^2/2) through the hardware exp2).
+// GELU'(v) = Phi(v) + v phi(v), phi the standard normal density, in fp32.  exp(-v^2/2)
+// serves both phi and the erf of Phi (erf(v/sqrt 2) needs exp(-(v/sqrt 2)^2)).
 __device__ __forceinline__ float gelu_grad(float v) {
-  const float cdf = 0.5f * (1.0f + erf_as(v * 0.7071067811865475f));
-  const float pdf = 0.3989422804014327f * __builtin_amdgcn_exp2f((-0.7213475204444817f * v) * v);
-  return __builtin_fmaf(v, pdf, cdf);
+  const float e = __builtin_amdgcn_exp2f((-0.7213475204444817f * v) * v);  // exp(-v^2/2)
+  const float cdf = __builtin_fmaf(0.5f, erf_as_e(v * 0.7071067811865475f, e), 0.5f);
+  return __builtin_fmaf(v, 0.3989422804014327f * e, cdf);
 }
 
-// Workgroup (channel block, row block): 64 channels x 4 row lanes; lane (c, l) takes
-// channel c's T group elements in rows l, l+4, ... of the block.  The four lanes'
-// bias sums are added in a fixed order.
-template <int T, typename Elt>
+// W bytes at p as 32-bit words (W = 2: the low half of one word).
+template <int W>
+__device__ __forceinline__ void load_chunk(const char* p, uint32_t (&w)[W >= 4 ? W / 4 : 1]) {
+  if constexpr (W == 16) {
+    const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    w[0] = q[0]; w[1] = q[1]; w[2] = q[2]; w[3] = q[3];
+  } else if constexpr (W == 8) {
+    const u32x2 q = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    w[0] = q[0]; w[1] = q[1];
+  } else if constexpr (W == 4) {
+    w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+  } else {
+    w[0] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
+  }
+}
+
+template <int W>
+__device__ __forceinline__ void store_chunk(char* p, const uint32_t (&w)[W >= 4 ? W / 4 : 1]) {
+  if constexpr (W == 16) {
+    __builtin_nontemporal_store((u32x4){w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4*>(p));
+  } else if constexpr (W == 8) {
+    __builtin_nontemporal_store((u32x2){w[0], w[1]}, reinterpret_cast<u32x2*>(p));
+  } else if constexpr (W == 4) {
+    __builtin_nontemporal_store(w[0], reinterpret_cast<uint32_t*>(p));
+  } else {
+    __builtin_nontemporal_store((uint16_t)w[0], reinterpret_cast<uint16_t*>(p));
+  }
+}
+
+template <typename Elt, int W>
+__device__ __forceinline__ float chunk_elt(const uint32_t (&w)[W >= 4 ? W / 4 : 1], int e) {
+  if constexpr (sizeof(Elt) == 4) return __builtin_bit_cast(float, w[e]);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w[e / 2] >> ((e & 1) * 16)));
+}
+
+// V values rounded to Elt into the chunk's words (fp16 pairs in one packed
+// round-to-nearest-even conversion).
+template <typename Elt, int W>
+__device__ __forceinline__ void pack_chunk(const float (&d)[W / sizeof(Elt)], uint32_t (&w)[W >= 4 ? W / 4 : 1]) {
+  constexpr int V = W / (int)sizeof(Elt);
+  if constexpr (sizeof(Elt) == 4) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) w[v] = __builtin_bit_cast(uint32_t, d[v]);
+  } else if constexpr (V == 1) {
+    w[0] = __builtin_bit_cast(uint16_t, (_Float16)d[0]);
+  } else {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int i = 0; i < V / 2; ++i) {
+      const h2 pr = {(_Float16)d[2 * i], (_Float16)d[2 * i + 1]};
+      w[i] = __builtin_bit_cast(uint32_t, pr);
+    }
+  }
+}
+
+// Workgroup (chunk block cb, row block rb): lane c of each wave takes chunk
+// cb*64 + c of the rows; wave l takes rows l, l+4, ... of the block, four at a
+// time so that eight loads are in flight per lane.  The four waves' column sums
+// are added in a fixed order.
+template <typename Elt, int W>
 __global__ void __launch_bounds__(256) eql_epi_bwd_kernel(const EpiBwdArgs a) {
-  __shared__ float red[4][kEpiCh];
-  const int ch = threadIdx.x % kEpiCh, rl = threadIdx.x / kEpiCh;
-  const int cb = blockIdx.x % a.chBlocks, rb = blockIdx.x / a.chBlocks;
-  const int d = cb * kEpiCh + ch;
-  const int r0 = rb * kEpiRows, r1 = min(a.N, r0 + kEpiRows);
-  const size_t rowElems = (size_t)a.Dp * T;
-  float s = 0.0f;
-  if (d < a.Dp) {
-    for (int r = r0 + rl; r < r1; r += 4) {
-      const size_t at = (size_t)r * rowElems + (size_t)d * T;
-      float g[T], o[T];
-      load_group<T, Elt>(static_cast<const Elt*>(a.dy) + at, g);
-      if (a.act == 1) {
-        float p[T];
-        load_group<T, Elt>(static_cast<const Elt*>(a.pre) + at, p);
+  constexpr int V = W / (int)sizeof(Elt);  // elements per chunk
+  constexpr int NWD = W >= 4 ? W / 4 : 1;  // words per chunk
+  constexpr int U = 4;                     // rows per iteration and wave
+  __shared__ float red[3][V][64];
+  const int lane = (int)threadIdx.x & 63, wv = (int)threadIdx.x >> 6;
+  const int cb = (int)blockIdx.x % a.chunkBlocks, rb = (int)blockIdx.x / a.chunkBlocks;
+  const int chunk = cb * 64 + lane;
+  const bool live = chunk < a.rowElems / V;
+  const int r0 = rb * a.rowsPerBlock, r1 = min(a.N, r0 + a.rowsPerBlock);
+  const size_t rowBytes = (size_t)a.rowElems * sizeof(Elt);
+  const size_t colOff = (size_t)chunk * W;
+  const bool gelu = a.act == 1;
+  float s[V];
 #pragma unroll
-        for (int e = 0; e < T; ++e) o[e] = g[e] * gelu_grad(p[e]);
-      } else {
+  for (int v = 0; v < V; ++v) s[v] = 0.0f;
+
+  // dpre in fp32, rounded once when stored; the bias sums take the fp32 values.
+  auto row_step = [&](const uint32_t (&g)[NWD], const uint32_t (&p)[NWD], size_t off) __attribute__((always_inline)) {
+    float d[V];
 #pragma unroll
-        for (int e = 0; e < T; ++e) o[e] = g[e];
+    for (int v = 0; v < V; ++v) {
+      d[v] = chunk_elt<Elt, W>(g, v);
+      if (gelu) d[v] *= gelu_grad(chunk_elt<Elt, W>(p, v));
+      s[v] += d[v];
+    }
+    uint32_t o[NWD];
+    pack_chunk<Elt, W>(d, o);
+    store_chunk<W>(static_cast<char*>(a.dpre) + off, o);
+  };
+
+  if (live) {
+    const char* dy = static_cast<const char*>(a.dy);
+    const char* pre = static_cast<const char*>(a.pre);
+    int r = r0 + wv;
+    for (; r + 4 * (U - 1) < r1; r += 4 * U) {
+      uint32_t g[U][NWD], p[U][NWD];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const size_t off = (size_t)(r + 4 * u) * rowBytes + colOff;
+        load_chunk<W>(dy + off, g[u]);
+        if (gelu) load_chunk<W>(pre + off, p[u]);
+        else
+#pragma unroll
+          for (int i = 0; i < NWD; ++i) p[u][i] = 0;
       }
-      store_group<T, Elt>(static_cast<Elt*>(a.dpre) + at, o);
 #pragma unroll
-      for (int e = 0; e < T; ++e) s += o[e];
+      for (int u = 0; u < U; ++u) row_step(g[u], p[u], (size_t)(r + 4 * u) * rowBytes + colOff);
+    }
+    for (; r < r1; r += 4) {
+      const size_t off = (size_t)r * rowBytes + colOff;
+      uint32_t g[NWD], p[NWD];
+      load_chunk<W>(dy + off, g);
+      if (gelu) load_chunk<W>(pre + off, p);
+      else
+#pragma unroll
+        for (int i = 0; i < NWD; ++i) p[i] = 0;
+      row_step(g, p, off);
     }
   }
   if (a.part) {
-    red[rl][ch] = s;
+    if (wv > 0) {
+#pragma unroll
+      for (int v = 0; v < V; ++v) red[wv - 1][v][lane] = s[v];
+    }
     __syncthreads();
-    if (rl == 0 && d < a.Dp) a.part[(size_t)rb * a.Dp + d] = ((red[0][ch] + red[1][ch]) + red[2][ch]) + red[3][ch];
+    if (wv == 0 && live) {
+      float* out = a.part + (size_t)rb * a.rowElems + (size_t)chunk * V;
+#pragma unroll
+      for (int v = 0; v < V; ++v) out[v] = ((s[v] + red[0][v][lane]) + red[1][v][lane]) + red[2][v][lane];
+    }
   }
 }
 
-// dbias[d]: the row blocks' partials added in order, rounded once.
+// dbias[d]: for each row block in order, the partial sums of positions d*T .. d*T+T-1
+// in order; rounded once to Elt.
 template <typename Elt>
 __global__ void __launch_bounds__(256) eql_epi_bias_kernel(const EpiBwdArgs a) {
-  const int d = blockIdx.x * 256 + threadIdx.x;
+  const int d = (int)blockIdx.x * 256 + (int)threadIdx.x;
   if (d >= a.Dp) return;
   float s = 0.0f;
-  for (int rb = 0; rb < a.rowBlocks; ++rb) s += a.part[(size_t)rb * a.Dp + d];
+  for (int rb = 0; rb < a.rowBlocks; ++rb) {
+    const float* p = a.part + (size_t)rb * a.rowElems + (size_t)d * a.T;
+    for (int g = 0; g < a.T; ++g) s += p[g];
+  }
   static_cast<Elt*>(a.dbias)[d] = (Elt)s;
 }
 

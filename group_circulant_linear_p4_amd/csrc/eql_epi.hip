@@ -1,23 +1,21 @@
-// Fused-epilogue backward instantiations, both element types, T = 1..16.
+// Fused-epilogue backward instantiations: both element types, every chunk width.
 #include "eql_epi.h"
 #include "eql_launch.h"
 
 namespace eql {
 
-template <int T, typename Elt>
+template <typename Elt, int W>
 static hipError_t epi_one(const EpiBwdArgs& a, unsigned grid, hipStream_t s) {
-  return launch_kernel((const void*)&eql_epi_bwd_kernel<T, Elt>, grid, a, s);
+  return launch_kernel((const void*)&eql_epi_bwd_kernel<Elt, W>, grid, a, s);
 }
 
-hipError_t launch_epi_bwd(int T, bool f16, const EpiBwdArgs& a, unsigned grid, hipStream_t s) {
-  if (f16) {
-#define EQL_CASE(t) return epi_one<t, _Float16>(a, grid, s);
-    EQL_FOR_EACH_T(T, EQL_CASE)
-#undef EQL_CASE
-  } else {
-#define EQL_CASE(t) return epi_one<t, float>(a, grid, s);
-    EQL_FOR_EACH_T(T, EQL_CASE)
-#undef EQL_CASE
+hipError_t launch_epi_bwd(bool f16, int W, const EpiBwdArgs& a, unsigned grid, hipStream_t s) {
+  switch (W) {
+    case 16: return f16 ? epi_one<_Float16, 16>(a, grid, s) : epi_one<float, 16>(a, grid, s);
+    case 8: return f16 ? epi_one<_Float16, 8>(a, grid, s) : epi_one<float, 8>(a, grid, s);
+    case 4: return f16 ? epi_one<_Float16, 4>(a, grid, s) : epi_one<float, 4>(a, grid, s);
+    case 2: return f16 ? epi_one<_Float16, 2>(a, grid, s) : hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
   }
 }
 

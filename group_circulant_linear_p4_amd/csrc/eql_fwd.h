@@ -123,15 +123,20 @@ constexpr int floor_pow2(int v) { return v >= 16 ? 16 : v >= 8 ? 8 : v >= 4 ? 4 
 //   erf(a) = 1 - t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-a^2),
 //   t = 1 / (1 + p a), a = |u|, extended as an odd function.
 // The reciprocal and exp2 are the hardware approximations (about 1 ulp).
-__device__ __forceinline__ float erf_as(float u) {
+// erf_as_e takes exp(-u^2) from the caller (GELU's derivative needs it as well).
+__device__ __forceinline__ float erf_as_e(float u, float e) {
   const float a = __builtin_fabsf(u);
   const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, a, 1.0f));
   float q = __builtin_fmaf(1.061405429f, t, -1.453152027f);
   q = __builtin_fmaf(q, t, 1.421413741f);
   q = __builtin_fmaf(q, t, -0.284496736f);
   q = __builtin_fmaf(q, t, 0.254829592f);
-  const float e = __builtin_amdgcn_exp2f((-1.4426950408889634f * a) * a);  // exp(-a^2)
   return __builtin_copysignf(__builtin_fmaf(-q * t, e, 1.0f), u);
+}
+
+__device__ __forceinline__ float erf_as(float u) {
+  const float a = __builtin_fabsf(u);
+  return erf_as_e(u, __builtin_amdgcn_exp2f((-1.4426950408889634f * a) * a));  // exp(-a^2)
 }
 
 // GELU in its exact form, v * Phi(v) = v/2 (1 + erf(v / sqrt 2)), in fp32.

@@ -39,7 +39,7 @@ hipError_t launch_bwdw_reduce_f16(int T, int waves, const BwdwReduceArgs& a, uns
 hipError_t launch_bwdw_reduce_f32(int T, int waves, const BwdwReduceArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_pack_f16(int T, const PackArgs& a, unsigned grid, hipStream_t s);
 // Fused-epilogue backward: dpre and the bias partials, then the bias sum.
-hipError_t launch_epi_bwd(int T, bool f16, const EpiBwdArgs& a, unsigned grid, hipStream_t s);
+hipError_t launch_epi_bwd(bool f16, int W, const EpiBwdArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_epi_bias(bool f16, const EpiBwdArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_pack_f32(int T, const PackArgs& a, unsigned grid, hipStream_t s);
 

@@ -147,9 +147,10 @@ int eqlinear_fwd_fused(const void* x, const void* w_packed, const void* bias,
                        int64_t Dp, int T, int dtype, int act, void* stream);
 
 /*
- * Scratch bytes eqlinear_fused_epilogue_bwd needs for the bias gradient: fp32 partial
- * sums, one row of Dp per block of 256 rows (0 when N == 0 or the arguments are
- * invalid).
+ * Scratch bytes eqlinear_fused_epilogue_bwd needs for the bias gradient: fp32 column
+ * sums of dpre, one row of Dp*T per block of rows (16 to 1024 rows, fewer rows per
+ * block for small N); depends only on the arguments (0 when N == 0 or the arguments
+ * are invalid).
  */
 size_t eqlinear_fused_epilogue_bwd_workspace_bytes(int64_t N, int64_t Dp, int T, int dtype);
 
@@ -165,8 +166,9 @@ size_t eqlinear_fused_epilogue_bwd_workspace_bytes(int64_t N, int64_t Dp, int T,
  * (no bias gradient; zeros when N == 0); workspace: at least
  * eqlinear_fused_epilogue_bwd_workspace_bytes bytes when dbias is given.  All in
  * `dtype`, 16-byte aligned (dbias: element-aligned).  dpre is computed in fp32 and
- * rounded once; dbias adds the unrounded fp32 values, per block of rows and then over
- * the blocks in a fixed order (deterministic).  Errors as the other entry points;
+ * rounded once; dbias adds the unrounded fp32 values: column sums per block of rows,
+ * then, for each channel, the blocks in order and the T positions d*T .. d*T+T-1 in
+ * order (deterministic).  Errors as the other entry points;
  * EQL_EINVAL also for an unknown act, a missing pre with EQL_ACT_GELU or a short
  * workspace.
  */

@@ -125,7 +125,12 @@ def test_fused_epilogue_bwd_validation():
     fn = "eqlinear_fused_epilogue_bwd"
     dy, pre, dpre, db, ws = A16, A16B, A16 + 0x1000, A16 + 0x2000, A16 + 0x3000
     need = eql.eqlinear_fused_epilogue_bwd_workspace_bytes(300, 5, 4, F16)
-    assert need == 2 * 5 * 4                                                                  # 2 row blocks
+    # fp32 column sums of each block of rows: 300 rows of D'T = 20 elements (one 64-chunk
+    # block across) take the smallest row block, 16 rows: 19 blocks.
+    assert need == 19 * 20 * 4
+    # Large enough for 2048 workgroups at 1024 rows a block: 65536 rows of 16384 fp16
+    # elements (32 blocks of 64 16-byte chunks across) give 64 row blocks.
+    assert eql.eqlinear_fused_epilogue_bwd_workspace_bytes(65536, 4096, 4, F16) == 64 * 16384 * 4
     assert eql.eqlinear_fused_epilogue_bwd_workspace_bytes(0, 5, 4, F16) == 0
     assert raw(fn, dy, pre, dpre, db, ws, need, 300, 5, 4, F16, 3, None) == eql.EQL_EINVAL      # act
     assert raw(fn, dy, None, dpre, db, ws, need, 300, 5, 4, F16, GELU, None) == eql.EQL_EINVAL  # pre needed

@@ -425,12 +425,16 @@ def epi_bwd_d(T, dtype, dy_d, pre_d, dpre, with_bias, N, Dp, act):
     return db
 
 
+# Rows of (D'T) elements stream in chunks of 16, 8, 4 or 2 bytes (the widest power of
+# two dividing the row); between them these shapes take every chunk width, and
+# dozens of ragged row blocks.
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
 @pytest.mark.parametrize("T", [3, 4, 8])
 @pytest.mark.parametrize("act", ["gelu", "none"])
-def test_fused_epilogue_bwd_matches_oracle(T, dtype, act):
-    N, Dp = 700, 70                               # 3 row blocks x 2 channel blocks, ragged
-    print("case epilogue bwd T=%d %s %s" % (T, dtype, act), flush=True)
+@pytest.mark.parametrize("shape", [(700, 70), (1301, 7)], ids=lambda s: "N%d_D%d" % s)
+def test_fused_epilogue_bwd_matches_oracle(T, dtype, act, shape):
+    N, Dp = shape
+    print("case epilogue bwd T=%d %s %s N=%d D'=%d" % (T, dtype, act, N, Dp), flush=True)
     wl = W.Workload("t", "test", T, N, 8, Dp, dtype, ("fwd",), seed=31 + T)
     dy, pre = W.make_dy(wl), W.make_residual(wl)
     dy_d, pre_d = dev(dy), dev(pre)
@@ -445,6 +449,31 @@ def test_fused_epilogue_bwd_matches_oracle(T, dtype, act):
     epi_bwd_d(T, dtype, dyi, pre_d if act == "gelu" else None, dyi, False, N, Dp, act)
     torch.cuda.synchronize()
     assert torch.equal(dyi, dpre)
+
+
+def test_fused_epilogue_bwd_full_size_sampled():
+    """The epilogue backward at the benchmark's size (p4 fp16, N=65536, D'T=4096: 8
+    blocks of 64 16-byte chunks across, 256 row blocks of 256 rows): sampled rows of
+    dpre against the oracle, and the bias gradient against an fp64 sum of the kernel's
+    own dpre over every row."""
+    wl = W.WORKLOADS["c5"]
+    T, N, Dp = wl.T, wl.N, wl.Dp
+    print("case epilogue bwd full size %s" % wl.name, flush=True)
+    dy, pre = W.make_dy(wl), W.make_residual(wl)
+    dy_d, pre_d = dev(dy), dev(pre)
+    dpre = torch.empty_like(dy_d)
+    db = epi_bwd_d(T, wl.dtype, dy_d, pre_d, dpre, True, N, Dp, "gelu")
+    torch.cuda.synchronize()
+    rows = _sample_rows(N)
+    ref_dpre, _ = oracle.fused_epilogue_bwd(dy[rows], pre[rows], T, act="gelu")
+    got = host(dpre[torch.from_numpy(rows).to(DEV)])
+    assert rel_err(got, ref_dpre) <= TOL[wl.dtype]
+    total = torch.zeros(Dp, dtype=torch.float64, device=DEV)
+    for r0 in range(0, N, 8192):
+        total += dpre[r0:r0 + 8192].view(-1, Dp, T).double().sum(dim=(0, 2))
+    torch.cuda.synchronize()
+    assert np.isfinite(host(dpre[:4096])).all()
+    assert rel_err(host(db), host(total)) <= TOL[wl.dtype]
 
 
 def test_fused_epilogue_bwd_empty_and_pre_out():
