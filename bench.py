@@ -244,6 +244,8 @@ def main():
         fused = fused_epilogue(torch, eql, x, wp, b, dy, y, N, Cp, Dp, T, code, sptr,
                                reps=max(5, min(args.steps, 20)))
         fused["plain_fwd_ms"] = round(per["fwd"], 4)
+        fused["mlp_train_step"] = mlp_train_step(torch, eql, x, w, wp, wpb, b, dy, y, dx, dw, ws, ws_bytes,
+                                                 N, Cp, Dp, T, code, sptr, reps=max(5, min(args.steps, 20)))
         del b
 
     cpu = None
@@ -345,6 +347,66 @@ def fused_epilogue(torch, eql, x, wp, b, r, y, N, Cp, Dp, T, code, sptr, reps):
     res["epilogue_bwd_GBps"] = round(epi_bytes / (res["epilogue_bwd_ms"] * 1e-3) / 1e9, 1)
     res["kind"] = ("eqlinear_fwd_fused vs eqlinear_fwd + torch (y + b), F.gelu, + residual; "
                    "eqlinear_fused_epilogue_bwd vs torch gelu_backward + channel sum")
+    torch.cuda.empty_cache()
+    return res
+
+
+def mlp_train_step(torch, eql, x, w, wp, wpb, b, dy, y, dx, dw, ws, ws_bytes, N, Cp, Dp, T, code, sptr, reps):
+    """One training step of the layer as an MLP expansion, y = GELU(x W^T + b): the
+    library's pack (both forms), fused forward keeping pre, epilogue backward (dpre,
+    dbias), input and weight gradients on dpre; against the unrolled dense layer in
+    torch (F.linear with the repeated bias, F.gelu, gelu_backward, the bias sum, the two
+    gradient matmuls, and the fold of the dense weight gradient onto the T tied entries
+    of each (d, c)).  Both produce y, dx, dw and db."""
+    F = torch.nn.functional
+    g = torch.arange(T, device=w.device)
+    idx = (g.view(T, 1) - g.view(1, T)) % T          # idx[g][h] = (g - h) mod T
+    Wd = w[:, :, idx].permute(0, 2, 1, 3).reshape(Dp * T, Cp * T).contiguous()
+    bb = b.repeat_interleave(T)
+    # dw[d, c, t] = sum_g dWd[(d, g), (c, (g - t) mod T)]: gather along the last axis
+    # with idx[g][t] = (g - t) mod T, then sum over g.
+    fold = idx.view(1, T, 1, T).expand(Dp, T, Cp, T)
+    pre, dpre = torch.empty_like(y), torch.empty_like(y)
+    db = torch.empty_like(b)
+    ebytes = eql.eqlinear_fused_epilogue_bwd_workspace_bytes(N, Dp, T, code)
+    ews = torch.empty(max(ebytes, 16), dtype=torch.uint8, device=y.device)
+
+    def lib_step():
+        eql.eqlinear_pack_weight(w, wp, Dp, Cp, T, code, eql.EQL_PACK_FWD, sptr)
+        eql.eqlinear_pack_weight(w, wpb, Dp, Cp, T, code, eql.EQL_PACK_BWDX, sptr)
+        eql.eqlinear_fwd_fused(x, wp, b, None, y, pre, N, Cp, Dp, T, code, eql.EQL_ACT_GELU, sptr)
+        eql.eqlinear_fused_epilogue_bwd(dy, pre, dpre, db, ews, ebytes, N, Dp, T, code, eql.EQL_ACT_GELU, sptr)
+        eql.eqlinear_bwd_x(dpre, wpb, dx, N, Cp, Dp, T, code, sptr)
+        eql.eqlinear_bwd_w(x, dpre, dw, ws, ws_bytes, N, Cp, Dp, T, code, sptr)
+
+    def torch_step():
+        pre_t = F.linear(x, Wd, bb)
+        y_t = F.gelu(pre_t)
+        gr = torch.ops.aten.gelu_backward(dy, pre_t)
+        db_t = gr.view(N, Dp, T).sum(dim=(0, 2))
+        dx_t = torch.mm(gr, Wd)
+        dWd = torch.mm(gr.t(), x)
+        dw_t = torch.gather(dWd.view(Dp, T, Cp, T), 3, fold).sum(dim=1)
+        return y_t, db_t, dx_t, dw_t
+
+    def timeit(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(e) / reps
+
+    res = {"lib_ms": round(timeit(lib_step), 4), "torch_dense_ms": round(timeit(torch_step), 4)}
+    res["speedup"] = round(res["torch_dense_ms"] / res["lib_ms"], 3)
+    res["kind"] = ("pack x2 + eqlinear_fwd_fused(bias, GELU, pre) + eqlinear_fused_epilogue_bwd + bwd_x + bwd_w, "
+                   "vs torch on the unrolled dense weight (F.linear, F.gelu, gelu_backward, bias sum, mm x2, "
+                   "weight-gradient fold)")
+    del Wd, pre, dpre, ews
     torch.cuda.empty_cache()
     return res
 

@@ -496,33 +496,47 @@ def test_fused_epilogue_bwd_empty_and_pre_out():
     assert rel_err(host(y), oracle.fwd_fused(x, w, bias=b, act="gelu")) <= TOL[dtype]
 
 
-def test_graph_replay_matches_eager():
-    """One training step (pack, forward, input gradient, weight gradient) captured in a
-    HIP graph and replayed three times.  Between replays the inputs are rewritten in
-    place and other eager work runs; every replay must equal the eager result for the
-    same inputs bit for bit (the library allocates nothing and records no memset, so the
-    captured step is the eager one)."""
+@pytest.mark.parametrize("fused", [False, True], ids=["plain", "fused_bias_gelu"])
+def test_graph_replay_matches_eager(fused):
+    """One training step captured in a HIP graph and replayed three times: pack, forward,
+    input gradient and weight gradient; with `fused`, the forward with bias + GELU that
+    keeps pre, the epilogue's backward (dpre, dbias), and both gradients on dpre.
+    Between replays the inputs are rewritten in place and other eager work runs; every
+    replay must equal the eager result for the same inputs bit for bit (the library
+    allocates nothing and records no memset, so the captured step is the eager one)."""
     T, N, Cp, Dp, dtype = 4, 700, 72, 96, "f16"
-    print("case graph replay", flush=True)
-    L = Lib(T, dtype)
+    print("case graph replay fused=%d" % fused, flush=True)
     code = DT[dtype]
     bufs = [inputs(T, N, Cp, Dp, dtype, seed=60 + i) for i in range(4)]
+    biases = [W.make_bias(W.Workload("t", "test", T, N, Cp, Dp, dtype, ("fwd",), seed=70 + i)) for i in range(4)]
     x_d, w_d, dy_d = (dev(a) for a in bufs[0])
+    b_d = dev(biases[0])
     wp = torch.empty(eql.eqlinear_packed_weight_bytes(Dp, Cp, T, code), dtype=torch.uint8, device=DEV)
     wpb = torch.empty(eql.eqlinear_packed_weight_bytes(Cp, Dp, T, code), dtype=torch.uint8, device=DEV)
     y = torch.empty((N, Dp * T), dtype=x_d.dtype, device=DEV)
+    pre, dpre = torch.empty_like(y), torch.empty_like(y)
+    db = torch.empty_like(b_d)
     dx = torch.empty((N, Cp * T), dtype=x_d.dtype, device=DEV)
     dw = torch.empty_like(w_d)
     nbytes = eql.eqlinear_bwd_w_workspace_bytes(N, Cp, Dp, T, code)
     ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=DEV)
+    ebytes = eql.eqlinear_fused_epilogue_bwd_workspace_bytes(N, Dp, T, code)
+    ews = torch.empty(max(ebytes, 16), dtype=torch.uint8, device=DEV)
 
     def step():
         eql.eqlinear_pack_weight(w_d, wp, Dp, Cp, T, code, eql.EQL_PACK_FWD)
         eql.eqlinear_pack_weight(w_d, wpb, Dp, Cp, T, code, eql.EQL_PACK_BWDX)
-        eql.eqlinear_fwd(x_d, wp, y, N, Cp, Dp, T, code)
-        eql.eqlinear_bwd_x(dy_d, wpb, dx, N, Cp, Dp, T, code)
-        eql.eqlinear_bwd_w(x_d, dy_d, dw, ws, nbytes, N, Cp, Dp, T, code)
+        if fused:
+            eql.eqlinear_fwd_fused(x_d, wp, b_d, None, y, pre, N, Cp, Dp, T, code, eql.EQL_ACT_GELU)
+            eql.eqlinear_fused_epilogue_bwd(dy_d, pre, dpre, db, ews, ebytes, N, Dp, T, code, eql.EQL_ACT_GELU)
+            g_out = dpre
+        else:
+            eql.eqlinear_fwd(x_d, wp, y, N, Cp, Dp, T, code)
+            g_out = dy_d
+        eql.eqlinear_bwd_x(g_out, wpb, dx, N, Cp, Dp, T, code)
+        eql.eqlinear_bwd_w(x_d, g_out, dw, ws, nbytes, N, Cp, Dp, T, code)
 
+    outs = (y, dx, dw) + ((pre, dpre, db) if fused else ())
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -535,17 +549,20 @@ def test_graph_replay_matches_eager():
     torch.cuda.synchronize()
     for i in range(1, 4):
         xh, wh, dyh = bufs[i]
-        x_d.copy_(dev(xh)); w_d.copy_(dev(wh)); dy_d.copy_(dev(dyh))
+        x_d.copy_(dev(xh)); w_d.copy_(dev(wh)); dy_d.copy_(dev(dyh)); b_d.copy_(dev(biases[i]))
         junk = torch.randn(1 << 20, device=DEV).sum()          # other eager work in between
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        got = (y.clone(), dx.clone(), dw.clone())
+        got = tuple(t.clone() for t in outs)
         step()                                                  # eager, same inputs
         torch.cuda.synchronize()
-        for a, b in zip(got, (y, dx, dw)):
+        for a, b in zip(got, outs):
             assert torch.equal(a, b)
-        assert rel_err(host(got[0]), oracle.fwd(xh, wh)) <= TOL[dtype]
+        if fused:
+            assert rel_err(host(got[0]), oracle.fwd_fused(xh, wh, bias=biases[i], act="gelu")) <= TOL[dtype]
+        else:
+            assert rel_err(host(got[0]), oracle.fwd(xh, wh)) <= TOL[dtype]
         assert bool(torch.isfinite(junk))
 
 
