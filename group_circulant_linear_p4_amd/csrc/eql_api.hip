@@ -336,7 +336,7 @@ int eqlinear_fused_epilogue_bwd(const void* dy, const void* pre, void* dpre, voi
     if (e != hipSuccess) return EQL_EHIP;
   }
   // dbias (zeros when N == 0: no partials to add).
-  if (dbias) return status_of(launch_epi_bias(f16, a, (unsigned)ceil_div(Dp, 256), s));
+  if (dbias) return status_of(launch_epi_bias(f16, a, (unsigned)ceil_div(Dp, 16), s));
   return EQL_OK;
 }
 

@@ -173,18 +173,43 @@ __global__ void __launch_bounds__(256) eql_epi_bwd_kernel(const EpiBwdArgs a) {
   }
 }
 
-// dbias[d]: for each row block in order, the partial sums of positions d*T .. d*T+T-1
-// in order; rounded once to Elt.
-template <typename Elt>
+// dbias[d] from the row blocks' column sums.  A workgroup takes 16 channels x 16
+// slices of the row blocks: slice l adds blocks l, l+16, l+32, ... in that order
+// (each block's T positions in order, four blocks' loads in flight), and the 16
+// slice sums of a channel are then added in slice order; rounded once to Elt.
+template <int T, typename Elt>
 __global__ void __launch_bounds__(256) eql_epi_bias_kernel(const EpiBwdArgs a) {
-  const int d = (int)blockIdx.x * 256 + (int)threadIdx.x;
-  if (d >= a.Dp) return;
+  __shared__ float red[16][16];
+  const int c = (int)threadIdx.x & 15, sl = (int)threadIdx.x >> 4;
+  const int d = (int)blockIdx.x * 16 + c;
   float s = 0.0f;
-  for (int rb = 0; rb < a.rowBlocks; ++rb) {
-    const float* p = a.part + (size_t)rb * a.rowElems + (size_t)d * a.T;
-    for (int g = 0; g < a.T; ++g) s += p[g];
+  if (d < a.Dp) {
+    const float* p = a.part + (size_t)d * T;
+    const size_t stride = (size_t)a.rowElems;
+    auto block_sum = [&](int rb) __attribute__((always_inline)) {
+      float v[T];
+#pragma unroll
+      for (int g = 0; g < T; ++g) v[g] = p[(size_t)rb * stride + g];
+      float t = v[0];
+#pragma unroll
+      for (int g = 1; g < T; ++g) t += v[g];
+      return t;
+    };
+    int rb = sl;
+    for (; rb + 48 < a.rowBlocks; rb += 64) {
+      const float t0 = block_sum(rb), t1 = block_sum(rb + 16), t2 = block_sum(rb + 32), t3 = block_sum(rb + 48);
+      s = (((s + t0) + t1) + t2) + t3;
+    }
+    for (; rb < a.rowBlocks; rb += 16) s += block_sum(rb);
   }
-  static_cast<Elt*>(a.dbias)[d] = (Elt)s;
+  red[sl][c] = s;
+  __syncthreads();
+  if (sl == 0 && d < a.Dp) {
+    float tot = red[0][c];
+#pragma unroll
+    for (int l = 1; l < 16; ++l) tot += red[l][c];
+    static_cast<Elt*>(a.dbias)[d] = (Elt)tot;
+  }
 }
 
 }  // namespace eql

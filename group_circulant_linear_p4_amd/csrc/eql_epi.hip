@@ -1,4 +1,5 @@
-// Fused-epilogue backward instantiations: both element types, every chunk width.
+// Fused-epilogue backward instantiations: both element types, every chunk width
+// (and, for the bias reduction, every T).
 #include "eql_epi.h"
 #include "eql_launch.h"
 
@@ -19,9 +20,16 @@ hipError_t launch_epi_bwd(bool f16, int W, const EpiBwdArgs& a, unsigned grid, h
   }
 }
 
+template <int T>
+static hipError_t bias_one(bool f16, const EpiBwdArgs& a, unsigned grid, hipStream_t s) {
+  return f16 ? launch_kernel((const void*)&eql_epi_bias_kernel<T, _Float16>, grid, a, s)
+             : launch_kernel((const void*)&eql_epi_bias_kernel<T, float>, grid, a, s);
+}
+
 hipError_t launch_epi_bias(bool f16, const EpiBwdArgs& a, unsigned grid, hipStream_t s) {
-  return f16 ? launch_kernel((const void*)&eql_epi_bias_kernel<_Float16>, grid, a, s)
-             : launch_kernel((const void*)&eql_epi_bias_kernel<float>, grid, a, s);
+#define EQL_CASE(t) return bias_one<t>(f16, a, grid, s);
+  EQL_FOR_EACH_T(a.T, EQL_CASE)
+#undef EQL_CASE
 }
 
 }  // namespace eql

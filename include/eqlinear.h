@@ -167,8 +167,9 @@ size_t eqlinear_fused_epilogue_bwd_workspace_bytes(int64_t N, int64_t Dp, int T,
  * eqlinear_fused_epilogue_bwd_workspace_bytes bytes when dbias is given.  All in
  * `dtype`, 16-byte aligned (dbias: element-aligned).  dpre is computed in fp32 and
  * rounded once; dbias adds the unrounded fp32 values: column sums per block of rows,
- * then, for each channel, the blocks in order and the T positions d*T .. d*T+T-1 in
- * order (deterministic).  Errors as the other entry points;
+ * then, for each channel, its T positions in every block, in a fixed order (16
+ * interleaved slices of the blocks, each in block order, then the slices in order),
+ * so the result is deterministic.  Errors as the other entry points;
  * EQL_EINVAL also for an unknown act, a missing pre with EQL_ACT_GELU or a short
  * workspace.
  */
