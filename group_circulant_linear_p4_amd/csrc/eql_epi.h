@@ -112,6 +112,8 @@ __global__ void __launch_bounds__(256) eql_epi_bwd_kernel(const EpiBwdArgs a) {
   const size_t rowBytes = (size_t)a.rowElems * sizeof(Elt);
   const size_t colOff = (size_t)chunk * W;
   const bool gelu = a.act == 1;
+  // Without an activation, dpre written over dy would rewrite the same values: skip it.
+  const bool store = gelu || a.dpre != a.dy;
   float s[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) s[v] = 0.0f;
@@ -125,9 +127,11 @@ __global__ void __launch_bounds__(256) eql_epi_bwd_kernel(const EpiBwdArgs a) {
       if (gelu) d[v] *= gelu_grad(chunk_elt<Elt, W>(p, v));
       s[v] += d[v];
     }
-    uint32_t o[NWD];
-    pack_chunk<Elt, W>(d, o);
-    store_chunk<W>(static_cast<char*>(a.dpre) + off, o);
+    if (store) {
+      uint32_t o[NWD];
+      pack_chunk<Elt, W>(d, o);
+      store_chunk<W>(static_cast<char*>(a.dpre) + off, o);
+    }
   };
 
   if (live) {

@@ -4,8 +4,10 @@ weight can be used as is ("Implementacao" in "Resumo Tecnico: Flash EQ-Linear":
 training-free, plug-and-play replacement).
 
 Forward packs the half spectrum of w and runs eqlinear_fwd; backward runs
-eqlinear_bwd_x on the conjugate-transposed packing and eqlinear_bwd_w.  Torch only
-allocates the buffers; every arithmetic step runs in the HIP library.
+eqlinear_bwd_x on the conjugate-transposed packing and eqlinear_bwd_w.  With a bias,
+GELU or a residual, the forward is eqlinear_fwd_fused and the backward starts with
+eqlinear_fused_epilogue_bwd.  Torch only allocates the buffers; every arithmetic step
+runs in the HIP library.
 """
 from __future__ import annotations
 
@@ -78,28 +80,38 @@ def _act_code(act):
 
 
 class EQLinearFusedFunction(torch.autograd.Function):
-    """y = act(x W^T + b), b[D'] shared by the T group elements of each output channel.
+    """y = act(x W^T + b) + r: b[D'] shared by the T group elements of each output
+    channel, act none or GELU, r a residual of the output's shape (each optional).
 
     Forward: one eqlinear_fwd_fused launch, which also keeps the activation's input
     when a gradient will be needed.  Backward: eqlinear_fused_epilogue_bwd (dpre and
-    the bias gradient), then eqlinear_bwd_x and eqlinear_bwd_w on dpre."""
+    the bias gradient; without an activation dpre is dy itself), then eqlinear_bwd_x
+    and eqlinear_bwd_w on dpre; the residual's gradient is dy."""
 
     @staticmethod
-    def forward(ctx, x: torch.Tensor, w: torch.Tensor, b, act):
+    def forward(ctx, x: torch.Tensor, w: torch.Tensor, b, r, act, grad_mode: bool):
         Dp, Cp, T = w.shape
         if x.shape[-1] != Cp * T:
             raise ValueError("x has %d features, the weight expects C'*T = %d" % (x.shape[-1], Cp * T))
+        if x.dtype != w.dtype or (b is not None and b.dtype != x.dtype) or (r is not None and r.dtype != x.dtype):
+            raise ValueError("x, w, bias and residual must share a dtype (fp16 or fp32)")
         code = _act_code(act)
         w = w.contiguous()
         x2 = x.reshape(-1, Cp * T).contiguous()
         N = x2.shape[0]
+        if r is not None and r.numel() != N * Dp * T:
+            raise ValueError("residual must have the output's shape")
+        r2 = r.reshape(N, Dp * T).contiguous() if r is not None else None
         y = torch.empty((N, Dp * T), dtype=x.dtype, device=x.device)
-        keep = code == EQL_ACT_GELU and any(ctx.needs_input_grad[:3])
+        # grad_mode is the caller's grad mode (autograd runs this body with grad disabled):
+        # pre is kept only when a backward can follow.
+        keep = code == EQL_ACT_GELU and grad_mode and any(ctx.needs_input_grad[:3])
         pre = torch.empty_like(y) if keep else None
-        eqlinear_fwd_fused(x2, _packed(w, EQL_PACK_FWD), b.contiguous() if b is not None else None, None, y, pre,
+        eqlinear_fwd_fused(x2, _packed(w, EQL_PACK_FWD), b.contiguous() if b is not None else None, r2, y, pre,
                            N, Cp, Dp, T, x.dtype, code)
         ctx.save_for_backward(x2, w, pre)
         ctx.code, ctx.has_bias, ctx.lead_shape = code, b is not None, x.shape[:-1]
+        ctx.res_shape = r.shape if r is not None else None
         return y.reshape(*x.shape[:-1], Dp * T)
 
     @staticmethod
@@ -108,12 +120,18 @@ class EQLinearFusedFunction(torch.autograd.Function):
         Dp, Cp, T = w.shape
         N = x2.shape[0]
         dy2 = dy.reshape(-1, Dp * T).to(x2.dtype).contiguous()
-        dpre = torch.empty_like(dy2)
-        db = torch.empty(Dp, dtype=x2.dtype, device=x2.device) if ctx.has_bias and ctx.needs_input_grad[2] else None
-        ws_bytes = eqlinear_fused_epilogue_bwd_workspace_bytes(N, Dp, T, x2.dtype)
-        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=x2.device)
-        eqlinear_fused_epilogue_bwd(dy2, pre, dpre, db, ws, ws_bytes, N, Dp, T, x2.dtype, ctx.code)
-        dx = dw = None
+        dr = dy2.reshape(ctx.res_shape) if ctx.res_shape is not None and ctx.needs_input_grad[3] else None
+        dx = dw = db = None
+        if not any(ctx.needs_input_grad[:3]):
+            return dx, dw, db, dr, None, None
+        # Without an activation dpre = dy: the call then only sums the bias gradient.
+        dpre = torch.empty_like(dy2) if ctx.code == EQL_ACT_GELU else dy2
+        if ctx.has_bias and ctx.needs_input_grad[2]:
+            db = torch.empty(Dp, dtype=x2.dtype, device=x2.device)
+        if ctx.code == EQL_ACT_GELU or db is not None:
+            ws_bytes = eqlinear_fused_epilogue_bwd_workspace_bytes(N, Dp, T, x2.dtype)
+            ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=x2.device)
+            eqlinear_fused_epilogue_bwd(dy2, pre, dpre, db, ws, ws_bytes, N, Dp, T, x2.dtype, ctx.code)
         if ctx.needs_input_grad[0]:
             dx = torch.empty((N, Cp * T), dtype=x2.dtype, device=x2.device)
             eqlinear_bwd_x(dpre, _packed(w, EQL_PACK_BWDX), dx, N, Cp, Dp, T, x2.dtype)
@@ -123,31 +141,17 @@ class EQLinearFusedFunction(torch.autograd.Function):
             wsb = torch.empty(max(wsw, 16), dtype=torch.uint8, device=x2.device)
             dw = torch.empty_like(w)
             eqlinear_bwd_w(x2, dpre, dw, wsb, wsw, N, Cp, Dp, T, x2.dtype)
-        return dx, dw, db, None
+        return dx, dw, db, dr, None, None
 
 
 def eqlinear_fused(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None = None,
                    residual: torch.Tensor | None = None, act: str = "none") -> torch.Tensor:
-    """Forward only: act(x W^T + bias) + residual in one kernel (eqlinear_fwd_fused), the
-    MLP-block epilogue of the networks the layer is built into ("Nivel de Rede").  bias
-    has one value per output channel (shared by its T group elements); act is "none"
-    or "gelu"; residual has the output's shape.  There is no backward: it raises when
-    autograd would need one."""
-    if torch.is_grad_enabled() and any(t is not None and t.requires_grad for t in (x, w, bias, residual)):
-        raise RuntimeError("eqlinear_fused is forward-only; use eqlinear for training")
-    if act not in ("none", "gelu"):
-        raise ValueError("act must be 'none' or 'gelu'")
-    Dp, Cp, T = w.shape
-    if x.shape[-1] != Cp * T:
-        raise ValueError("x has %d features, the weight expects C'*T = %d" % (x.shape[-1], Cp * T))
-    x2 = x.reshape(-1, Cp * T).contiguous()
-    N = x2.shape[0]
-    b = bias.contiguous() if bias is not None else None
-    r = residual.reshape(N, Dp * T).contiguous() if residual is not None else None
-    y = torch.empty((N, Dp * T), dtype=x.dtype, device=x.device)
-    eqlinear_fwd_fused(x2, _packed(w.contiguous(), EQL_PACK_FWD), b, r, y, None, N, Cp, Dp, T, x.dtype,
-                       EQL_ACT_GELU if act == "gelu" else EQL_ACT_NONE)
-    return y.reshape(*x.shape[:-1], Dp * T)
+    """act(x W^T + bias) + residual with the epilogue fused into the forward kernel
+    (eqlinear_fwd_fused), the MLP-block epilogue of the networks the layer is built into
+    ("Nivel de Rede").  bias has one value per output channel (shared by its T group
+    elements); act is "none" or "gelu"; residual has the output's shape.  Differentiable
+    in x, w, bias and residual."""
+    return EQLinearFusedFunction.apply(x, w, bias, residual, act, torch.is_grad_enabled())
 
 
 class EQLinear(torch.nn.Module):
@@ -166,10 +170,12 @@ class EQLinear(torch.nn.Module):
         with torch.no_grad():
             self.weight.normal_(0.0, 1.0 / math.sqrt(in_channels * group_order))
 
-    def forward(self, x: torch.Tensor) -> torch.Tensor:
-        if self.bias is None and self.activation in (None, "none"):
+    def forward(self, x: torch.Tensor, residual: torch.Tensor | None = None) -> torch.Tensor:
+        """y = act(x W^T + bias) + residual (the parts not configured are skipped)."""
+        if self.bias is None and self.activation in (None, "none") and residual is None:
             return EQLinearFunction.apply(x, self.weight)
-        return EQLinearFusedFunction.apply(x, self.weight, self.bias, self.activation)
+        return EQLinearFusedFunction.apply(x, self.weight, self.bias, residual, self.activation,
+                                           torch.is_grad_enabled())
 
     def extra_repr(self) -> str:
         return "in_channels=%d, out_channels=%d, group_order=%d, bias=%s, activation=%s" % (

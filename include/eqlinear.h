@@ -162,7 +162,8 @@ size_t eqlinear_fused_epilogue_bwd_workspace_bytes(int64_t N, int64_t Dp, int T,
  * layer then come from eqlinear_bwd_x and eqlinear_bwd_w applied to dpre; the
  * residual's gradient is dy itself.
  * dy, pre: [N][Dp*T] read (pre only with EQL_ACT_GELU, else it may be NULL);
- * dpre: [N][Dp*T] written, may be the same buffer as dy; dbias: [Dp] written, or NULL
+ * dpre: [N][Dp*T] written, may be the same buffer as dy (with EQL_ACT_NONE it then already
+ * holds the result and only dbias is computed); dbias: [Dp] written, or NULL
  * (no bias gradient; zeros when N == 0); workspace: at least
  * eqlinear_fused_epilogue_bwd_workspace_bytes bytes when dbias is given.  All in
  * `dtype`, 16-byte aligned (dbias: element-aligned).  dpre is computed in fp32 and

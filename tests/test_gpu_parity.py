@@ -444,11 +444,13 @@ def test_fused_epilogue_bwd_matches_oracle(T, dtype, act, shape):
     ref_dpre, ref_db = oracle.fused_epilogue_bwd(dy, pre, T, act=act)
     assert rel_err(host(dpre), ref_dpre) <= TOL[dtype]
     assert rel_err(host(db), ref_db) <= TOL[dtype]
-    # In place (dpre = dy) gives the same result.
+    # In place (dpre = dy) gives the same result, bias gradient included (without an
+    # activation the kernel then stores nothing and only sums).
     dyi = dy_d.clone()
-    epi_bwd_d(T, dtype, dyi, pre_d if act == "gelu" else None, dyi, False, N, Dp, act)
+    dbi = epi_bwd_d(T, dtype, dyi, pre_d if act == "gelu" else None, dyi, True, N, Dp, act)
     torch.cuda.synchronize()
     assert torch.equal(dyi, dpre)
+    assert torch.equal(dbi, db)
 
 
 def test_fused_epilogue_bwd_full_size_sampled():
@@ -576,8 +578,27 @@ def test_layer_fused_forward_matches_oracle():
     assert tuple(y.shape) == (3, 37, Dp * T)
     ref = oracle.fwd_fused(x, w, bias=b, residual=r, act="gelu")
     assert rel_err(host(y).reshape(N, Dp * T), ref) <= TOL["f32"]
-    with pytest.raises(RuntimeError):
-        eqlinear_fused(dev(x).requires_grad_(), dev(w), act="gelu")
+
+
+@pytest.mark.parametrize("act", ["gelu", "none"])
+def test_layer_fused_training_with_residual(act):
+    """eqlinear_fused(x, w, b, r, act) trains: gradients of x, w, b and r against the
+    oracle's chain rule (dr = dy; without an activation dpre is dy itself)."""
+    from group_circulant_linear_p4_amd.layer import eqlinear_fused
+    T, N, Cp, Dp = 4, 2 * 65, 20, 28
+    print("case layer fused training act=%s" % act, flush=True)
+    wl = W.Workload("t", "test", T, N, Cp, Dp, "f32", ("fwd",), seed=23)
+    x, w, b, r, dy = W.make_x(wl), W.make_w(wl), W.make_bias(wl), W.make_residual(wl), W.make_dy(wl)
+    xt, wt, bt, rt = (dev(a).requires_grad_() for a in (x, w, b, r))
+    y = eqlinear_fused(xt.reshape(2, 65, Cp * T), wt, bt, rt, act=act)
+    y.backward(dev(dy).reshape(2, 65, Dp * T))
+    torch.cuda.synchronize()
+    assert rel_err(host(y.detach()).reshape(N, Dp * T), oracle.fwd_fused(x, w, bias=b, residual=r, act=act)) <= 1e-5
+    dpre, db = oracle.fused_epilogue_bwd(dy, oracle.fwd_fused(x, w, bias=b), T, act=act)
+    assert rel_err(host(bt.grad), db) <= 1e-5
+    assert rel_err(host(xt.grad), oracle.bwd_x(dpre, w)) <= 1e-5
+    assert rel_err(host(wt.grad), oracle.bwd_w(x, dpre, T)) <= 1e-5
+    assert np.array_equal(host(rt.grad), dy)
 
 
 def test_layer_bias_gelu_training_matches_oracle():
@@ -602,6 +623,10 @@ def test_layer_bias_gelu_training_matches_oracle():
     assert rel_err(host(layer.bias.grad), db) <= 1e-5
     assert rel_err(host(x.grad), oracle.bwd_x(dpre, w)) <= 1e-5
     assert rel_err(host(layer.weight.grad), oracle.bwd_w(xn, dpre, T)) <= 1e-5
+    with torch.no_grad():                     # inference: no pre kept, same output
+        y2 = layer(dev(xn))
+    torch.cuda.synchronize()
+    assert torch.equal(y2, y.detach())
 
 
 def test_layer_autograd_matches_oracle():
