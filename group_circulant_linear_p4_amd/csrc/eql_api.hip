@@ -42,11 +42,14 @@ Twiddles make_twiddles(int T) {
   return tw;
 }
 
+// Rows: a row index plus any kernel's row-block size (at most 1024) stays below 2^31.
+constexpr int64_t kMaxN = (1LL << 31) - (1LL << 20);
+
 int check_sizes(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype) {
   if (!dtype_ok(dtype) || T < 1) return EQL_EINVAL;
   if (T > EQL_MAX_T) return EQL_EUNSUPPORTED;
   if (N < 0 || Cp < 1 || Dp < 1) return EQL_EINVAL;
-  if (N >= (1LL << 31) || Cp * T * elt_bytes(dtype) > kMaxRowBytes || Dp * T * elt_bytes(dtype) > kMaxRowBytes)
+  if (N > kMaxN || Cp * T * elt_bytes(dtype) > kMaxRowBytes || Dp * T * elt_bytes(dtype) > kMaxRowBytes)
     return EQL_EINVAL;
   return EQL_OK;
 }

@@ -108,7 +108,8 @@ __global__ void __launch_bounds__(256) eql_epi_bwd_kernel(const EpiBwdArgs a) {
   const int cb = (int)blockIdx.x % a.chunkBlocks, rb = (int)blockIdx.x / a.chunkBlocks;
   const int chunk = cb * 64 + lane;
   const bool live = chunk < a.rowElems / V;
-  const int r0 = rb * a.rowsPerBlock, r1 = min(a.N, r0 + a.rowsPerBlock);
+  // Row indices in 64 bits: N may come within a block of 2^31.
+  const int64_t r0 = (int64_t)rb * a.rowsPerBlock, r1 = min((int64_t)a.N, r0 + a.rowsPerBlock);
   const size_t rowBytes = (size_t)a.rowElems * sizeof(Elt);
   const size_t colOff = (size_t)chunk * W;
   const bool gelu = a.act == 1;
@@ -137,7 +138,7 @@ __global__ void __launch_bounds__(256) eql_epi_bwd_kernel(const EpiBwdArgs a) {
   if (live) {
     const char* dy = static_cast<const char*>(a.dy);
     const char* pre = static_cast<const char*>(a.pre);
-    int r = r0 + wv;
+    int64_t r = r0 + wv;
     for (; r + 4 * (U - 1) < r1; r += 4 * U) {
       uint32_t g[U][NWD], p[U][NWD];
 #pragma unroll

@@ -34,7 +34,8 @@
  *  - Return value: an eql_status.  Arguments are validated before anything is
  *    launched; on any error nothing is launched and no memory is touched.
  *    N == 0 is valid and launches nothing.
- *  - Sizes: 1 <= T <= EQL_MAX_T, C' >= 1, D' >= 1, 0 <= N < 2^31, and one
+ *  - Sizes: 1 <= T <= EQL_MAX_T, C' >= 1, D' >= 1, 0 <= N <= 2^31 - 2^20 (room
+ *    for the kernels' 32-bit row arithmetic), and one
  *    activation row (C'*T or D'*T elements) at most 2^23 bytes; EQL_EINVAL
  *    otherwise, also when a launch would need more than 2^24 - 1 workgroups.
  */

@@ -91,6 +91,7 @@ def test_fwd_validation(fn):
     assert raw(fn, *ok, 8, 4, 0, 4, F32, None) == eql.EQL_EINVAL          # D' < 1
     assert raw(fn, *ok, 8, 1 << 22, 4, 4, F32, None) == eql.EQL_EINVAL    # C'T >= 2^24
     assert raw(fn, *ok, 1 << 31, 4, 4, 4, F32, None) == eql.EQL_EINVAL   # N >= 2^31
+    assert raw(fn, *ok, (1 << 31) - (1 << 20) + 1, 4, 4, 4, F32, None) == eql.EQL_EINVAL  # N > 2^31 - 2^20
     assert raw(fn, None, A16B, A16, 8, 4, 4, 4, F16, None) == eql.EQL_EINVAL
     assert raw(fn, A16, None, A16B, 8, 4, 4, 4, F16, None) == eql.EQL_EINVAL
     assert raw(fn, A16, A16B, None, 8, 4, 4, 4, F16, None) == eql.EQL_EINVAL
