@@ -413,6 +413,14 @@ def test_random_shape_sweep(case):
     fused_d(T, dtype, x_d, wp, dev(b), dev(r), yf, N, Cp, Dp, "gelu")
     torch.cuda.synchronize()
     assert rel_err(host(yf), oracle.fwd_fused(x, w, bias=b, residual=r, act="gelu")) <= tol
+    # The epilogue's backward on the same shape (GELU, bias gradient), r standing in for pre.
+    dy_d, r_d = dev(dy), dev(r)
+    dpre = torch.empty_like(dy_d)
+    db = epi_bwd_d(T, dtype, dy_d, r_d, dpre, True, N, Dp, "gelu")
+    torch.cuda.synchronize()
+    ref_dpre, ref_db = oracle.fused_epilogue_bwd(dy, r, T, act="gelu")
+    assert rel_err(host(dpre), ref_dpre) <= tol
+    assert rel_err(host(db), ref_db) <= tol
 
 
 def epi_bwd_d(T, dtype, dy_d, pre_d, dpre, with_bias, N, Dp, act):
