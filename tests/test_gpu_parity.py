@@ -588,24 +588,26 @@ def test_layer_fused_forward_matches_oracle():
     assert rel_err(host(y).reshape(N, Dp * T), ref) <= TOL["f32"]
 
 
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
 @pytest.mark.parametrize("act", ["gelu", "none"])
-def test_layer_fused_training_with_residual(act):
+def test_layer_fused_training_with_residual(act, dtype):
     """eqlinear_fused(x, w, b, r, act) trains: gradients of x, w, b and r against the
     oracle's chain rule (dr = dy; without an activation dpre is dy itself)."""
     from group_circulant_linear_p4_amd.layer import eqlinear_fused
     T, N, Cp, Dp = 4, 2 * 65, 20, 28
-    print("case layer fused training act=%s" % act, flush=True)
-    wl = W.Workload("t", "test", T, N, Cp, Dp, "f32", ("fwd",), seed=23)
+    print("case layer fused training act=%s %s" % (act, dtype), flush=True)
+    wl = W.Workload("t", "test", T, N, Cp, Dp, dtype, ("fwd",), seed=23)
     x, w, b, r, dy = W.make_x(wl), W.make_w(wl), W.make_bias(wl), W.make_residual(wl), W.make_dy(wl)
     xt, wt, bt, rt = (dev(a).requires_grad_() for a in (x, w, b, r))
     y = eqlinear_fused(xt.reshape(2, 65, Cp * T), wt, bt, rt, act=act)
     y.backward(dev(dy).reshape(2, 65, Dp * T))
     torch.cuda.synchronize()
-    assert rel_err(host(y.detach()).reshape(N, Dp * T), oracle.fwd_fused(x, w, bias=b, residual=r, act=act)) <= 1e-5
+    tol = TOL[dtype]
+    assert rel_err(host(y.detach()).reshape(N, Dp * T), oracle.fwd_fused(x, w, bias=b, residual=r, act=act)) <= tol
     dpre, db = oracle.fused_epilogue_bwd(dy, oracle.fwd_fused(x, w, bias=b), T, act=act)
-    assert rel_err(host(bt.grad), db) <= 1e-5
-    assert rel_err(host(xt.grad), oracle.bwd_x(dpre, w)) <= 1e-5
-    assert rel_err(host(wt.grad), oracle.bwd_w(x, dpre, T)) <= 1e-5
+    assert rel_err(host(bt.grad), db) <= tol
+    assert rel_err(host(xt.grad), oracle.bwd_x(dpre, w)) <= tol
+    assert rel_err(host(wt.grad), oracle.bwd_w(x, dpre, T)) <= tol
     assert np.array_equal(host(rt.grad), dy)
 
 
