@@ -49,6 +49,9 @@ def parse():
                     help="skip timing the fused epilogue (bias, GELU, residual; and its backward) against torch ops")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows of the CPU-oracle sample (0: sized to about 12 s of work)")
+    ap.add_argument("--rotate-mib", type=int, default=512,
+                    help="rotate through enough copies of every buffer that one round of steps touches at "
+                         "least this many MiB (above the 256 MiB Infinity Cache); 0: one resident set")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this size (a reference for "
                          "profiler traffic counters)")
@@ -102,61 +105,79 @@ def main():
     print("bench: generating %s" % wl.name, file=sys.stderr, flush=True)
 
     x_h, w_h, dy_h = W.make_x(wl), W.make_w(wl), W.make_dy(wl)
-    x = torch.from_numpy(x_h).to(dev)
-    w = torch.from_numpy(w_h).to(dev)
-    dy = torch.from_numpy(dy_h).to(dev)
-    y = torch.empty((N, Dp * T), dtype=tdt, device=dev)
-    dx = torch.empty((N, Cp * T), dtype=tdt, device=dev)
-    dw = torch.empty((Dp, Cp, T), dtype=tdt, device=dev)
-    wp = torch.empty(eql.eqlinear_packed_weight_bytes(Dp, Cp, T, code), dtype=torch.uint8, device=dev)
-    wpb = torch.empty(eql.eqlinear_packed_weight_bytes(Cp, Dp, T, code), dtype=torch.uint8, device=dev)
+    elt = 2 if wl.dtype == "f16" else 4
     ws_bytes = eql.eqlinear_bwd_w_workspace_bytes(N, Cp, Dp, T, code)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    # Rotating buffer sets: every step reads and writes its own copy of every buffer,
+    # so that the working set of consecutive steps exceeds the 256 MiB Infinity Cache
+    # (twice over) and each step starts cold, as the large workloads do by their size.
+    set_bytes = (elt * (2 * N * Cp * T + 2 * N * Dp * T + 2 * Dp * Cp * T) + ws_bytes
+                 + eql.eqlinear_packed_weight_bytes(Dp, Cp, T, code)
+                 + eql.eqlinear_packed_weight_bytes(Cp, Dp, T, code))
+    n_sets = max(1, -(-(args.rotate_mib << 20) // set_bytes)) if args.rotate_mib > 0 else 1
+    sets = []
+    for i in range(n_sets):
+        b = {"x": torch.from_numpy(x_h).to(dev), "w": torch.from_numpy(w_h).to(dev),
+             "dy": torch.from_numpy(dy_h).to(dev),
+             "y": torch.empty((N, Dp * T), dtype=tdt, device=dev), "dx": torch.empty((N, Cp * T), dtype=tdt, device=dev),
+             "dw": torch.empty((Dp, Cp, T), dtype=tdt, device=dev),
+             "wp": torch.empty(eql.eqlinear_packed_weight_bytes(Dp, Cp, T, code), dtype=torch.uint8, device=dev),
+             "wpb": torch.empty(eql.eqlinear_packed_weight_bytes(Cp, Dp, T, code), dtype=torch.uint8, device=dev),
+             "ws": torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)}
+        sets.append(b)
+    s0 = sets[0]
+    x, w, dy, y, dx, dw, wp, wpb, ws = (s0[k] for k in ("x", "w", "dy", "y", "dx", "dw", "wp", "wpb", "ws"))
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
 
-    def make_calls(sp):
+    def make_calls(sp, b=s0):
         return {
-            "pack": lambda: (eql.eqlinear_pack_weight(w, wp, Dp, Cp, T, code, eql.EQL_PACK_FWD, sp),
-                             eql.eqlinear_pack_weight(w, wpb, Dp, Cp, T, code, eql.EQL_PACK_BWDX, sp)),
-            "fwd": lambda: eql.eqlinear_fwd(x, wp, y, N, Cp, Dp, T, code, sp),
-            "bwd_x": lambda: eql.eqlinear_bwd_x(dy, wpb, dx, N, Cp, Dp, T, code, sp),
-            "bwd_w": lambda: eql.eqlinear_bwd_w(x, dy, dw, ws, ws_bytes, N, Cp, Dp, T, code, sp),
+            "pack": lambda: (eql.eqlinear_pack_weight(b["w"], b["wp"], Dp, Cp, T, code, eql.EQL_PACK_FWD, sp),
+                             eql.eqlinear_pack_weight(b["w"], b["wpb"], Dp, Cp, T, code, eql.EQL_PACK_BWDX, sp)),
+            "fwd": lambda: eql.eqlinear_fwd(b["x"], b["wp"], b["y"], N, Cp, Dp, T, code, sp),
+            "bwd_x": lambda: eql.eqlinear_bwd_x(b["dy"], b["wpb"], b["dx"], N, Cp, Dp, T, code, sp),
+            "bwd_w": lambda: eql.eqlinear_bwd_w(b["x"], b["dy"], b["dw"], b["ws"], ws_bytes, N, Cp, Dp, T, code, sp),
         }
 
-    calls = make_calls(sptr)
+    set_calls = [make_calls(sptr, b) for b in sets]
     order = ["pack", "fwd", "bwd_x", "bwd_w"]
 
-    def step(events=None):
-        for i, k in enumerate(order):
+    def step(i, calls, events=None):
+        for k in order:
             if events is not None:
                 events[k][0].record(stream)
             calls[k]()
             if events is not None:
                 events[k][1].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    def timed(calls_of):
+        """args.warmup untimed steps, then args.steps timed ones; step i runs calls_of(i)."""
+        for i in range(args.warmup):
+            step(i, calls_of(i))
+        torch.cuda.synchronize()
+        evs = [{k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for k in order}
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(i, calls_of(args.warmup + i), evs[i])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        per = {k: float(np.mean([e[k][0].elapsed_time(e[k][1]) for e in evs])) for k in order}
+        # Device time of each step (the sum of its passes' event windows): spread across steps.
+        step_dev = [sum(e[k][0].elapsed_time(e[k][1]) for k in order) for e in evs]
+        return wall * 1e3 / args.steps, per, step_dev
 
-    evs = [{k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for k in order}
-           for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    per = {k: float(np.mean([e[k][0].elapsed_time(e[k][1]) for e in evs])) for k in order}
-    # Device time of each step (the sum of its passes' event windows): spread across steps.
-    step_dev = [sum(e[k][0].elapsed_time(e[k][1]) for k in order) for e in evs]
+    ms_per_step, per, step_dev = timed(lambda i: set_calls[i % n_sets])
+    warm = None
+    if n_sets > 1:
+        wms, wper, _ = timed(lambda i: set_calls[0])
+        warm = {"ms_per_step": round(wms, 4), "passes_ms": {k: round(v, 4) for k, v in wper.items()},
+                "kind": "one resident buffer set (inputs partly served from the Infinity Cache)"}
 
     dense_eq = 2.0 * N * (Dp * T) * (Cp * T)
     actual = 2.0 * (2 * T - 2 if T % 2 == 0 else 2 * T - 1) * N * Dp * Cp if T > 1 else 2.0 * N * Dp * Cp
     n_passes = 3
     value = n_passes * dense_eq / (ms_per_step * 1e-3) / 1e12
-    elt = 2 if wl.dtype == "f16" else 4
     bytes_pass = {
         "fwd": elt * (N * Cp * T + N * Dp * T + Dp * Cp * T),
         "bwd_x": elt * (N * Dp * T + N * Cp * T + Dp * Cp * T),
@@ -199,21 +220,24 @@ def main():
     graph = None
     if not args.no_graph:
         try:
+            # One captured step per buffer set, in rotation order.
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                cap = make_calls(torch.cuda.current_stream().cuda_stream)  # the capturing stream
-                for k in order:
-                    cap[k]()
+                for b_set in sets:
+                    cap = make_calls(torch.cuda.current_stream().cuda_stream, b_set)  # the capturing stream
+                    for k in order:
+                        cap[k]()
             for _ in range(3):
                 g.replay()
             torch.cuda.synchronize()
+            replays = max(1, -(-args.steps // n_sets))
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
-            for _ in range(args.steps):
+            for _ in range(replays):
                 g.replay()
             b.record()
             torch.cuda.synchronize()
-            gms = a.elapsed_time(b) / args.steps
+            gms = a.elapsed_time(b) / (replays * n_sets)
             graph = {"ms_per_step": round(gms, 4),
                      "value": round(n_passes * dense_eq / (gms * 1e-3) / 1e12, 2), "unit": "TFLOP/s"}
             del g
@@ -231,7 +255,8 @@ def main():
 
     dense = None
     if not args.no_dense:
-        dense = dense_comparator(torch, x, w, dy, T, reps=max(5, min(args.steps, 20)))
+        dense = dense_comparator(torch, [b["x"] for b in sets], w, [b["dy"] for b in sets], T,
+                                 reps=max(5, min(args.steps, 20)))
         dense["speedup_fwd"] = round(dense["fwd_ms"] / per["fwd"], 3)
         dense["speedup_bwd_x"] = round(dense["bwd_x_ms"] / per["bwd_x"], 3)
         dense["speedup_bwd_w"] = round(dense["bwd_w_ms"] / per["bwd_w"], 3)
@@ -250,7 +275,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        del x, dy, y, dx
+        del x, dy, y, dx, sets, set_calls, s0
         torch.cuda.empty_cache()
         cpu = cpu_baseline(wl, x_h, w_h, dy_h, args.cpu_rows, n_passes)
 
@@ -270,7 +295,9 @@ def main():
         "data": "synthetic (seeded; x,dy ~ N(0,1), w ~ N(0,1/C)%s)" % (
             ", %g%% of rows x%g" % (100 * wl.hot_rows_frac, wl.hot_rows_scale) if wl.hot_rows_frac else ""),
         "config": {"workload": wl.name, "T": T, "N": N, "C": Cp * T, "D": Dp * T,
-                   "step": "pack(fwd)+pack(bwd_x)+fwd+bwd_x+bwd_w"},
+                   "step": "pack(fwd)+pack(bwd_x)+fwd+bwd_x+bwd_w", "buffer_sets": n_sets,
+                   "set_mib": round(set_bytes / 2**20, 1)},
+        "warm": warm,
         "passes": passes,
         "pack_ms": round(per["pack"], 4),
         "mfma_frac_step": round(n_passes * actual / (ms_per_step * 1e-3) / 1e12 / MFMA_PEAK[wl.dtype], 4),
@@ -411,38 +438,53 @@ def mlp_train_step(torch, eql, x, w, wp, wpb, b, dy, y, dx, dw, ws, ws_bytes, N,
     return res
 
 
-def dense_comparator(torch, x, w, dy, T, reps):
+def dense_comparator(torch, xs, w, dys, T, reps):
     """The unrolled ("replicate and multiply dense") layer on the same GPU: torch
     F.linear and matmuls on the dense (D'T) x (C'T) weight (built outside the timed
-    region)."""
+    region), rotating over the same buffer sets as the library's step (xs, dys)."""
     Dp, Cp, _ = w.shape
     g = torch.arange(T, device=w.device)
     idx = (g.view(T, 1) - g.view(1, T)) % T
     Wd = w[:, :, idx].permute(0, 2, 1, 3).reshape(Dp * T, Cp * T).contiguous()
     F = torch.nn.functional
+    n = len(xs)
 
     def timeit(fn):
-        for _ in range(3):
-            fn()
+        for i in range(3):
+            fn(i % n)
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        for _ in range(reps):
-            fn()
+        for i in range(reps):
+            fn(i % n)
         b.record()
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
 
-    dyT = dy.t().contiguous()
+    dyTs = [dy.t().contiguous() for dy in dys]
     res = {
-        "fwd_ms": timeit(lambda: F.linear(x, Wd)),
-        "bwd_x_ms": timeit(lambda: torch.matmul(dy, Wd)),
-        "bwd_w_ms": timeit(lambda: torch.matmul(dyT, x)),
+        "fwd_ms": timeit(lambda i: F.linear(xs[i], Wd)),
+        "bwd_x_ms": timeit(lambda i: torch.matmul(dys[i], Wd)),
+        "bwd_w_ms": timeit(lambda i: torch.matmul(dyTs[i], xs[i])),
     }
     res = {k: round(v, 4) for k, v in res.items()}
     res["kind"] = "torch F.linear / matmul on the unrolled dense weight (hipBLASLt)"
-    del Wd, dyT
+    res["buffer_sets"] = n
+    del Wd, dyTs
     return res
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), or the platform's description."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
 
 
 def cpu_baseline(wl, x_h, w_h, dy_h, rows, n_passes, target_s=12.0, min_s=10.0, max_reps=6):
@@ -481,7 +523,8 @@ def cpu_baseline(wl, x_h, w_h, dy_h, rows, n_passes, target_s=12.0, min_s=10.0, 
         reps += 1
     flops = n_passes * 2.0 * rows * wl.D * wl.C * reps
     what = "rows 0..%d" % (rows - 1) if rows < wl.N else "all %d rows" % rows
-    return {"value": round(flops / total / 1e12, 5), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+    return {"value": round(flops / total / 1e12, 5), "unit": "TFLOP/s", "cores": int(cores), "cpu": cpu_model(),
+            "kind": "oracle",
             "sample": "%s of the same workload x %d run(s), forward + input gradient + weight gradient, "
                       "fp64 dense unroll (%.1f s)" % (what, reps, total)}
 

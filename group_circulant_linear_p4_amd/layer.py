@@ -96,6 +96,15 @@ class EQLinearFusedFunction(torch.autograd.Function):
         if x.dtype != w.dtype or (b is not None and b.dtype != x.dtype) or (r is not None and r.dtype != x.dtype):
             raise ValueError("x, w, bias and residual must share a dtype (fp16 or fp32)")
         code = _act_code(act)
+        # The kernel reads exactly D' bias values (one per output channel, shared by its
+        # T group elements): a per-feature bias of D'*T values, or a short one, is refused.
+        if b is not None and (b.dim() != 1 or b.numel() != Dp):
+            raise ValueError("bias must be 1-D with D' = %d values (one per output channel, shared over the "
+                             "group), got shape %s" % (Dp, tuple(b.shape)))
+        if b is not None and b.device != x.device:
+            raise ValueError("bias must be on x's device (%s), got %s" % (x.device, b.device))
+        if r is not None and r.device != x.device:
+            raise ValueError("residual must be on x's device (%s), got %s" % (x.device, r.device))
         w = w.contiguous()
         x2 = x.reshape(-1, Cp * T).contiguous()
         N = x2.shape[0]

@@ -183,3 +183,17 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(eql, "_LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(ImportError):
         eql.lib()
+
+
+@pytest.mark.parametrize("shape", [(12,), (2,), (1, 3)], ids=["per_feature", "short", "two_dim"])
+def test_fused_layer_rejects_a_bias_of_the_wrong_shape(shape):
+    """The fused layer's bias holds one value per output channel (D' = 3 here); a
+    per-feature bias of D'*T values, a short one or a 2-D one is refused before any
+    buffer reaches the library (CPU tensors: nothing is launched)."""
+    import torch
+    from group_circulant_linear_p4_amd.layer import eqlinear_fused
+    x = torch.zeros(5, 2 * 4)
+    w = torch.zeros(3, 2, 4)
+    b = torch.zeros(*shape)
+    with pytest.raises(ValueError, match="bias"):
+        eqlinear_fused(x, w, bias=b, act="gelu")
