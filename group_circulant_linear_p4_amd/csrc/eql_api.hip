@@ -26,6 +26,8 @@ int64_t padded_groups(int64_t ch, int dtype) {
   const int64_t g = (ch + group_channels(dtype) - 1) / group_channels(dtype);
   return (g + kPackGroupAlign - 1) / kPackGroupAlign * kPackGroupAlign;
 }
+// Output channels of the packed weight, padded to whole 32-channel blocks.
+int64_t padded_out(int64_t ch) { return (ch + kPackBlock - 1) / kPackBlock * kPackBlock; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -114,7 +116,7 @@ int run_fwd(const void* x, const void* wp, void* y, int64_t N, int64_t Cin, int6
   a.Cin = (int)Cin;
   a.Dout = (int)Dout;
   a.Jpad = (int)padded_groups(Cin, dtype);
-  const int64_t wpBytes = Dout * a.Jpad * 16LL * T;
+  const int64_t wpBytes = padded_out(Dout) * a.Jpad * 16LL * T;
   if (wpBytes >= (1LL << 32)) return EQL_EINVAL;
   a.wpBytes = (uint32_t)wpBytes;
   a.colTiles = (int)colTiles;
@@ -231,7 +233,7 @@ const char* eqlinear_status_string(int status) {
 
 size_t eqlinear_packed_weight_bytes(int64_t out_ch, int64_t in_ch, int T, int dtype) {
   if (check_sizes(0, in_ch, out_ch, T, dtype) != EQL_OK) return 0;
-  return (size_t)out_ch * (size_t)padded_groups(in_ch, dtype) * 16 * T;
+  return (size_t)padded_out(out_ch) * (size_t)padded_groups(in_ch, dtype) * 16 * T;
 }
 
 int eqlinear_pack_weight(const void* w, void* w_packed, int64_t Dp, int64_t Cp, int T, int dtype,
@@ -251,7 +253,7 @@ int eqlinear_pack_weight(const void* w, void* w_packed, int64_t Dp, int64_t Cp, 
   a.inCh = (int)(a.transposed ? Dp : Cp);
   a.Jin = (int)padded_groups(a.inCh, dtype);
   a.tw = make_twiddles(T);
-  const int64_t threads = (int64_t)a.outCh * a.Jin * group_channels(dtype);
+  const int64_t threads = padded_out(a.outCh) * a.Jin * group_channels(dtype);
   const int64_t grid = ceil_div(threads, 256);
   if (grid > kMaxGrid) return EQL_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -178,6 +178,80 @@ __device__ __forceinline__ void dma16_batch(const BufDesc& d, const uint32_t (&v
 }
 #undef EQL_DMA_ONE
 
+// Descriptor words of `bytes` bytes at `base`, forced into scalar registers.  The
+// address is below 2^48, so the stride field above it stays zero.
+__device__ __forceinline__ u32x4 desc_words(uint64_t base, uint32_t bytes) {
+  return (u32x4){(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base),
+                 (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32)),
+                 (uint32_t)__builtin_amdgcn_readfirstlane(bytes), 0x00020000u};
+}
+
+// N consecutive 1 KB loads (16 bytes per lane) from buffer offsets voff + 1024 i into
+// LDS at ldsBase + OFF + 1024 i + 16 lane.  The instruction offset applies to both the
+// buffer and the LDS address, so one M0 write serves a run of up to four loads; M0 is
+// formed inside the statement (base register plus immediate), so the compiler keeps no
+// per-slot copy of it live.  Wait states as dma16.
+#define EQL_DMAO(v, i) "buffer_load_dwordx4 %[" #v "], %[desc], 0 offen offset:" #i " lds\n\t"
+#define EQL_M0(o) "s_add_u32 m0, %[l], %[" #o "]\n\ts_nop 0\n\t"
+template <int N, int OFF>
+__device__ __forceinline__ void dma16_run(const u32x4& desc, uint32_t voff, uint32_t ldsBase) {
+  static_assert(N >= 1 && N <= 8 && N != 5 && N != 7, "run length");
+  const uint32_t l = (uint32_t)__builtin_amdgcn_readfirstlane(ldsBase);
+  if constexpr (N == 1) {
+    asm volatile("s_nop 4\n\t" EQL_M0(o) EQL_DMAO(v, 0)
+                 : : [v] "v"(voff), [l] "s"(l), [o] "i"(OFF), [desc] "s"(desc) : "memory", "scc");
+  } else if constexpr (N == 2) {
+    asm volatile("s_nop 4\n\t" EQL_M0(o) EQL_DMAO(v, 0) EQL_DMAO(v, 1024)
+                 : : [v] "v"(voff), [l] "s"(l), [o] "i"(OFF), [desc] "s"(desc) : "memory", "scc");
+  } else if constexpr (N == 3) {
+    asm volatile("s_nop 4\n\t" EQL_M0(o) EQL_DMAO(v, 0) EQL_DMAO(v, 1024) EQL_DMAO(v, 2048)
+                 : : [v] "v"(voff), [l] "s"(l), [o] "i"(OFF), [desc] "s"(desc) : "memory", "scc");
+  } else if constexpr (N == 4) {
+    asm volatile("s_nop 4\n\t" EQL_M0(o) EQL_DMAO(v, 0) EQL_DMAO(v, 1024) EQL_DMAO(v, 2048) EQL_DMAO(v, 3072)
+                 : : [v] "v"(voff), [l] "s"(l), [o] "i"(OFF), [desc] "s"(desc) : "memory", "scc");
+  } else {
+    // Past four loads the instruction offset would exceed its 12 bits: a second run
+    // starts 4 KB on in both address spaces, from a second lane offset.
+    const uint32_t voff2 = voff + 4096u;
+    if constexpr (N == 6) {
+      asm volatile("s_nop 4\n\t" EQL_M0(o) EQL_DMAO(v, 0) EQL_DMAO(v, 1024) EQL_DMAO(v, 2048) EQL_DMAO(v, 3072)
+                   EQL_M0(o2) EQL_DMAO(v2, 0) EQL_DMAO(v2, 1024)
+                   : : [v] "v"(voff), [v2] "v"(voff2), [l] "s"(l), [o] "i"(OFF), [o2] "i"(OFF + 4096),
+                       [desc] "s"(desc) : "memory", "scc");
+    } else {
+      asm volatile("s_nop 4\n\t" EQL_M0(o) EQL_DMAO(v, 0) EQL_DMAO(v, 1024) EQL_DMAO(v, 2048) EQL_DMAO(v, 3072)
+                   EQL_M0(o2) EQL_DMAO(v2, 0) EQL_DMAO(v2, 1024) EQL_DMAO(v2, 2048) EQL_DMAO(v2, 3072)
+                   : : [v] "v"(voff), [v2] "v"(voff2), [l] "s"(l), [o] "i"(OFF), [o2] "i"(OFF + 4096),
+                       [desc] "s"(desc) : "memory", "scc");
+    }
+  }
+}
+
+// N loads (1, 2 or 4) of 16 bytes per lane with lane offsets voff[i] into LDS at
+// ldsBase + OFF + 1024 i + 16 lane: one M0 write per load, formed inside the statement.
+#define EQL_DMAX(k) EQL_M0(o##k) "buffer_load_dwordx4 %[v" #k "], %[desc], 0 offen lds\n\t"
+template <int N, int OFF>
+__device__ __forceinline__ void dma16_each(const u32x4& desc, const uint32_t (&voff)[N], uint32_t ldsBase) {
+  static_assert(N == 1 || N == 2 || N == 4, "batch size");
+  const uint32_t l = (uint32_t)__builtin_amdgcn_readfirstlane(ldsBase);
+  if constexpr (N == 1) {
+    asm volatile("s_nop 4\n\t" EQL_DMAX(0)
+                 : : [v0] "v"(voff[0]), [l] "s"(l), [o0] "i"(OFF), [desc] "s"(desc) : "memory", "scc");
+  } else if constexpr (N == 2) {
+    asm volatile("s_nop 4\n\t" EQL_DMAX(0) EQL_DMAX(1)
+                 : : [v0] "v"(voff[0]), [v1] "v"(voff[1]), [l] "s"(l), [o0] "i"(OFF), [o1] "i"(OFF + 1024),
+                     [desc] "s"(desc) : "memory", "scc");
+  } else {
+    asm volatile("s_nop 4\n\t" EQL_DMAX(0) EQL_DMAX(1) EQL_DMAX(2) EQL_DMAX(3)
+                 : : [v0] "v"(voff[0]), [v1] "v"(voff[1]), [v2] "v"(voff[2]), [v3] "v"(voff[3]), [l] "s"(l),
+                     [o0] "i"(OFF), [o1] "i"(OFF + 1024), [o2] "i"(OFF + 2048), [o3] "i"(OFF + 3072),
+                     [desc] "s"(desc) : "memory", "scc");
+  }
+}
+#undef EQL_DMAX
+#undef EQL_M0
+#undef EQL_DMAO
+
 // Descriptor of `bytes` bytes at `base` (words built from scalar values).
 __device__ __forceinline__ BufDesc desc_at(uint64_t base, uint32_t bytes) {
   BufDesc d;

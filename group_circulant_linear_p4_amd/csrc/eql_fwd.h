@@ -1,36 +1,36 @@
-// Fused forward kernel of the EQ-Linear layer: y = x W^T evaluated as
+// Fused forward kernels of the EQ-Linear layer: y = x W^T evaluated as
 // group DFT (prologue) -> per-frequency channel GEMMs on MFMA -> inverse DFT
 // (epilogue), with no intermediate global writes ("Implementacao" in "Resumo
 // Tecnico: Flash EQ-Linear": fused data flow, Fourier fragments kept in registers
-// and shared memory).  The input-gradient pass runs the same kernel on the
+// and shared memory).  The input-gradient pass runs the same kernels on the
 // conjugate-transposed packed weight.
 //
-// Work decomposition (gfx950, wave64, one persistent 256-thread workgroup per CU):
-//   * an output tile is 128 rows x BN = 32*NB output channels for all T planes;
-//     each of the 4 waves owns 32 rows; a workgroup walks its tiles as one stream
-//     of K stages, so loads run ahead across tile boundaries;
-//   * the K loop runs over "stages" of JC 16-byte channel groups (two groups per
-//     MFMA k-step);
-//   * x of a stage (the workgroup's 128 rows x JC groups) streams into its own
-//     LDS ring the same way as the weight (16-byte rows only; otherwise each lane
-//     loads its x straight into registers with narrower bounds-checked loads).
-//     Lane l takes row l%32 and channel group 2s + l/32 of k-step s (G channels x
-//     T group elements) in MFMA A-operand order; rows past N and channels past
-//     C' read as zero without branches.  The group DFT runs in fp32 registers and
-//     rounds once to the element type; the negated Im planes needed by the real
-//     part of each complex product are made by a sign flip;
-//   * the packed spectrum of w for the workgroup's BN channels streams into an
-//     NS-deep LDS ring with buffer loads that write LDS directly (no VGPR
-//     staging).  A ring row holds the JC*T 16-byte units of one output channel,
-//     XOR-swizzled so that the 16-byte MFMA B-operand reads of 16 consecutive
-//     channels (one LDS cycle on the 64-bank LDS) touch 16 different 16-byte
-//     bank groups;
+// Work decomposition (gfx950, wave64, one persistent workgroup per CU):
+//   * an output tile is 128 rows x BN = 32*NB output channels for all T planes; a
+//     workgroup walks its tiles as one stream of K stages, so loads run ahead across
+//     tile boundaries;
+//   * a K stage is two 16-byte channel groups (one MFMA k-step);
+//   * x of a stage (the tile's 128 rows x 2 groups) streams into an LDS ring by
+//     buffer loads that write LDS directly (16-byte rows; otherwise each lane loads
+//     its x straight into registers with narrower bounds-checked loads).  Lane l
+//     takes row l%32 and channel group l/32 (G channels x T group elements) in MFMA
+//     A-operand order; rows past N and channels past C' read as zero.  The group DFT
+//     runs in fp32 registers and rounds once to the element type; the negated Im
+//     planes needed by the real part of each complex product are made by a sign flip;
+//   * the packed spectrum of w streams into its own LDS ring, one contiguous run per
+//     32-channel block and stage (see packed_unit);
 //   * per k-step and 32-column block: real planes take one MFMA, a complex pair
 //     four (Re += Xr Wr + (-Xi) Wi, Im += Xi Wr + Xr Wi);
 //   * the epilogue reads the T accumulators of one (row, channel) from the same
 //     register slot, applies the inverse DFT (its 1/T and 2/T are in the packed
 //     weight) and stores T contiguous outputs; adjacent lanes write adjacent
 //     channels.  EPI = 1 adds a per-channel bias, GELU and a residual first.
+//
+// eql_fwd4_kernel (T <= 4, 16-byte rows) is the fast path: a 4-slot ring walked by a
+// loop unrolled over the slots, so every LDS read takes an immediate offset from one
+// of two base registers and the stage bodies have no branches; 8 waves (two per SIMD,
+// each with half the tile's columns) when the tile has two or more column blocks.
+// eql_fwd_kernel serves every other T and unaligned rows.
 #pragma once
 
 #include <type_traits>
@@ -59,36 +59,30 @@ constexpr int kFwdRows = 128;   // rows per workgroup (4 waves x 32)
 #if defined(__HIP_DEVICE_COMPILE__)
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-// p4 group DFT of 8 fp16 channels (raw[2e], raw[2e+1] hold (x0,x1), (x2,x3) of
-// channel e) into the A-operand units X0, X2, Xr, Xi and -Xi (8 halves each).
-//   Xr = x0 - x2 and -Xi = x1 - x3 come from one packed fp16 subtraction per
-//   channel (a single rounding of the exact difference); X0 = (x0+x1) + (x2+x3)
-//   and X2 = (x0-x1) + (x2-x3) are fp32 dot products of the fp16 pairs, rounded
-//   once to fp16.  The 1/2 of the p4 forward transform is folded into the packed
+// p4 group DFT of 8 fp16 channels (raw[4q..4q+1] hold (x0,x1), (x2,x3) of channel 2q,
+// raw[4q+2..4q+3] those of channel 2q+1) into the A-operand units X0, X2, Xr, Xi and
+// -Xi (8 halves each), with instructions that issue alongside MFMAs (v_dot2 does not:
+// on gfx950 it occupies the matrix pipeline and serialises with the MFMAs).
+//   x0 + x2 and x1 + x3 are formed in fp32 from the fp16 halves by v_fma_mix_f32
+//   (x * 1 + y, exact for fp16 operands within 13 binades of each other), X0 / X2 are
+//   their fp32 sum / difference, rounded once to fp16.  Xr = x0 - x2 and -Xi = x1 - x3
+//   come from one packed fp16 subtraction per channel (one rounding of the exact
+//   difference).  The 1/2 of the p4 forward transform is folded into the packed
 //   weight's real planes.
-// b.lo*c.lo + b.hi*c.hi in fp32: v_dot2_f32_f16 with the addend given as the inline
-// constant 0 (the two-operand form accumulates into its destination, which then
-// has to be zeroed by a separate move first).
-__device__ __forceinline__ float dot2_f16(f16x2 b, f16x2 c) {
-  float r;
-  asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(b), "v"(c));
-  return r;
-}
-
 __device__ __forceinline__ void dft_p4_f16(const uint32_t (&raw)[16], u32x4 (&out)[5]) {
-  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-  const f16x2 pm = {(_Float16)1.0f, (_Float16)-1.0f};
 #pragma unroll
   for (int q = 0; q < 4; ++q) {  // channel pair (2q, 2q+1) -> word q of each unit
-    const f16x2 a0 = __builtin_bit_cast(f16x2, raw[4 * q + 0]), b0 = __builtin_bit_cast(f16x2, raw[4 * q + 1]);
-    const f16x2 a1 = __builtin_bit_cast(f16x2, raw[4 * q + 2]), b1 = __builtin_bit_cast(f16x2, raw[4 * q + 3]);
-    const f16x2 d0 = a0 - b0, d1 = a1 - b1;  // (Xr, -Xi) of each channel
-    const float x0e = __builtin_amdgcn_fdot2(a0, ones, dot2_f16(b0, ones), false);
-    const float x0o = __builtin_amdgcn_fdot2(a1, ones, dot2_f16(b1, ones), false);
-    const float x2e = __builtin_amdgcn_fdot2(a0, pm, dot2_f16(b0, pm), false);
-    const float x2o = __builtin_amdgcn_fdot2(a1, pm, dot2_f16(b1, pm), false);
-    const f16x2 X0 = {(_Float16)x0e, (_Float16)x0o};
-    const f16x2 X2 = {(_Float16)x2e, (_Float16)x2o};
+    const uint32_t a0 = raw[4 * q + 0], b0 = raw[4 * q + 1];
+    const uint32_t a1 = raw[4 * q + 2], b1 = raw[4 * q + 3];
+    float s02e, s13e, s02o, s13o;
+    asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,1]" : "=v"(s02e) : "v"(a0), "v"(b0));
+    asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "=v"(s13e) : "v"(a0), "v"(b0));
+    asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,1]" : "=v"(s02o) : "v"(a1), "v"(b1));
+    asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "=v"(s13o) : "v"(a1), "v"(b1));
+    const f16x2 X0 = {(_Float16)(s02e + s13e), (_Float16)(s02o + s13o)};
+    const f16x2 X2 = {(_Float16)(s02e - s13e), (_Float16)(s02o - s13o)};
+    const f16x2 d0 = __builtin_bit_cast(f16x2, a0) - __builtin_bit_cast(f16x2, b0);  // (Xr, -Xi) of channel 2q
+    const f16x2 d1 = __builtin_bit_cast(f16x2, a1) - __builtin_bit_cast(f16x2, b1);
     const uint32_t nxi = __builtin_bit_cast(uint32_t, __builtin_shufflevector(d0, d1, 1, 3));
     out[0][q] = __builtin_bit_cast(uint32_t, X0);
     out[1][q] = __builtin_bit_cast(uint32_t, X2);
@@ -145,6 +139,86 @@ __device__ __forceinline__ float gelu_erf(float v) {
   return __builtin_fmaf(h, erf_as(v * 0.7071067811865475f), h);
 }
 
+#if defined(__HIP_DEVICE_COMPILE__)
+// Epilogue of one wave's part of a tile: rows row0 + rowOff .. +31, columns colBase ..
+// colBase + 32 NBW - 1.  Accumulator slot r of lane l in block nb holds row
+// 8 (r/4) + 4 (l/32) + r%4 and column colBase + 32 nb + l%32.  Stores go through a
+// buffer descriptor covering the tile's valid rows; columns past D' take an offset
+// beyond every range, so no store needs a branch.  EPI = 1 adds the per-channel bias,
+// applies the activation and adds the residual (all in fp32) before the single
+// rounding to Elt, and writes the activation's input to pre when that is given.
+template <int T, typename Elt, int NBW, int EPI>
+__device__ __forceinline__ void fwd_epilogue(const FwdArgs& a, const f32x16 (&acc)[T][NBW], int row0, int rowOff,
+                                             int colBase) {
+  constexpr int ELT = (int)sizeof(Elt);
+  const uint32_t outRow = (uint32_t)a.Dout * T * ELT;  // bytes of one output row
+  const uint32_t rows = (uint32_t)min(kFwdRows, a.N - row0);
+  const __amdgpu_buffer_rsrc_t yr = make_rsrc(static_cast<char*>(a.y) + (size_t)row0 * outRow, rows * outRow);
+  // The lane index is recomputed here rather than kept live through the main loop.
+  const int ln = lane_index();
+  const uint32_t laneOff = (uint32_t)(rowOff + 4 * (ln >> 5)) * outRow;
+  // Fused epilogue operands: an absent bias or residual gets an empty range, so its
+  // loads read zero.
+  const __amdgpu_buffer_rsrc_t br = make_rsrc(a.bias, EPI && a.bias ? (uint32_t)a.Dout * ELT : 0u);
+  const __amdgpu_buffer_rsrc_t rr =
+      make_rsrc(EPI && a.res ? static_cast<const char*>(a.res) + (size_t)row0 * outRow : nullptr,
+                EPI && a.res ? rows * outRow : 0u);
+  const __amdgpu_buffer_rsrc_t pr =
+      make_rsrc(EPI && a.pre ? static_cast<char*>(a.pre) + (size_t)row0 * outRow : nullptr,
+                EPI && a.pre ? rows * outRow : 0u);
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) {
+    const int col = colBase + nb * 32 + (ln & 31);
+    const uint32_t cOff = col < a.Dout ? laneOff + (uint32_t)col * T * ELT : kOob;
+    float bv = 0.0f;
+    if constexpr (EPI) {
+      uint32_t b1[1];
+      load_group_raw<1, Elt>(br, col < a.Dout ? (uint32_t)col * ELT : kOob, b1);
+      float bf1[1];
+      group_from_raw<1, Elt>(b1, bf1);
+      bv = bf1[0];
+    }
+    // Fused epilogue: the residual groups of a chunk are loaded before any of its
+    // stores (the compiler may not move a load above a store to y, which the residual
+    // may alias), so one wait covers the chunk.
+    constexpr int RW = group_words<T, Elt>();
+    constexpr int CH = EPI ? floor_pow2(32 / RW < 1 ? 1 : (32 / RW > 16 ? 16 : 32 / RW)) : 16;
+    static_assert(16 % CH == 0, "chunks must tile the 16 accumulator slots");
+#pragma unroll
+    for (int r0 = 0; r0 < 16; r0 += CH) {
+      uint32_t rw[CH][RW];
+      if constexpr (EPI) {
+#pragma unroll
+        for (int j = 0; j < CH; ++j)
+          load_group_raw<T, Elt>(rr, cOff + (uint32_t)(8 * ((r0 + j) >> 2) + ((r0 + j) & 3)) * outRow, rw[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < CH; ++j) {
+        const int r = r0 + j;
+        float P[T], yv[T];
+#pragma unroll
+        for (int p = 0; p < T; ++p) P[p] = acc[p][nb][r];
+        Idft<T, false>::run(P, yv, a.tw);
+        const uint32_t off = cOff + (uint32_t)(8 * (r >> 2) + (r & 3)) * outRow;
+        if constexpr (EPI) {
+          float rv[T];
+          group_from_raw<T, Elt>(rw[j], rv);
+#pragma unroll
+          for (int g = 0; g < T; ++g) yv[g] += bv;
+          if (a.pre) store_group_buf<T, Elt>(pr, off, yv);
+#pragma unroll
+          for (int g = 0; g < T; ++g) {
+            const float v = a.act == 1 ? gelu_erf(yv[g]) : yv[g];
+            yv[g] = v + rv[g];
+          }
+        }
+        store_group_buf<T, Elt>(yr, off, yv);
+      }
+    }
+  }
+}
+#endif
+
 // EPI = 1: the epilogue adds the per-channel bias, applies the activation and adds
 // the residual (all in fp32) before the single rounding to Elt.
 template <int T, typename Elt, int NB, int JC, int LOAD, int EPI>
@@ -172,7 +246,7 @@ __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
   constexpr int GB = G * T * ELT;         // bytes of one lane's x block per k-step (16*T)
   constexpr int NW = LOAD == kLoadNarrow ? pow2_part(T * ELT) : 16;  // register-path width
   constexpr int XL = XLDS ? 0 : KS * GB / NW;  // register-path x loads per stage
-  static_assert(JC % 2 == 0 && (BN * RP) % 256 == 0 && (32 * RP) % 64 == 0, "tile shape");
+  static_assert(JC == 2 && (BN * RP) % 256 == 0 && (32 * RP) % 64 == 0, "tile shape (a stage is one packed chunk)");
   static_assert(NS * STAGE_UNITS * 16 <= 160 * 1024, "LDS budget");
   // vmcnt at the top of a stage (see the pipeline notes below); a count beyond the
   // counter's range falls back to waiting for every load.
@@ -202,7 +276,9 @@ __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
   int lane = lane_index();
   int lrow = lane & 31, khalf = lane >> 5;
   const uint32_t rowBytes = (uint32_t)a.Cin * T * ELT;
-  const uint32_t colStride = (uint32_t)a.Jpad * T * 16u;  // packed bytes per output channel
+  const uint32_t chunkBytes = (uint32_t)T * 1024u;         // one 32-channel block, one stage
+  const uint32_t blockStride = (uint32_t)nst * chunkBytes;  // packed bytes per 32-channel block
+  const int nblk = (a.Dout + 31) >> 5;
 
   auto tile_row0 = [&](int k) __attribute__((always_inline)) {
     return (xcd_remap(b0 + k * grid, a.numTiles) / a.colTiles) * kFwdRows;
@@ -213,9 +289,10 @@ __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
   };
 
   // Weight ring: position P = (wave*IPW + i)*64 + lane of a stage holds unit
-  // r = (P % RP) ^ ring_swz(o) of output channel o = P / RP.  Offsets are relative
-  // to the stage's first byte in output channel col0; channels past D' fall
-  // outside the descriptor and read zero.
+  // r = (P % RP) ^ ring_swz(o) (group r / T of the stage, plane r % T) of the tile's
+  // output channel o = P / RP.  Offsets are relative to the stage's chunk of the
+  // tile's first 32-channel block (see packed_unit); blocks past D' fall outside the
+  // descriptor and read zero.
   uint32_t bOff[IPW];
   uint32_t xOff[IPWX > 0 ? IPWX : 1];
   int xCh[IPWX > 0 ? IPWX : 1];
@@ -226,7 +303,9 @@ __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
       const int o = P / RP, pos = P - o * RP;
       const int r = pos ^ ring_swz<RP>(o);
       const int rr = r < R ? r : 0;  // padding positions load an arbitrary unit
-      bOff[i] = (uint32_t)o * colStride + (uint32_t)rr * 16u;
+      const int ol = o & 31;
+      bOff[i] = (uint32_t)(o >> 5) * blockStride + (uint32_t)(rr % T) * 1024u + (uint32_t)ol * 32u +
+                (uint32_t)((rr / T) ^ ((ol >> 3) & 1)) * 16u;
     }
     // x ring (each wave loads and reads only its own 32 rows): position
     // P = wave*32*RP + i*64 + lane holds unit u = (P % RP) ^ ring_swz(row) of row
@@ -254,8 +333,8 @@ __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
   auto set_issue_tile = [&](int k) __attribute__((always_inline)) {
     if (k < myTiles) {
       const int row0 = tile_row0(k), col0 = tile_col0(k);
-      bTileBase = reinterpret_cast<uint64_t>(a.wp) + (uint64_t)col0 * colStride;
-      bTileBytes = (uint32_t)(a.Dout - col0) * colStride;
+      bTileBase = reinterpret_cast<uint64_t>(a.wp) + (uint64_t)(col0 >> 5) * blockStride;
+      bTileBytes = (uint32_t)(min(NB, nblk - (col0 >> 5)) - 1) * blockStride + chunkBytes;
       xTileBase = reinterpret_cast<uint64_t>(a.x) + (uint64_t)row0 * rowBytes;
       xTileBytes = (uint32_t)min(kFwdRows, a.N - row0) * rowBytes;
     } else {
@@ -266,10 +345,8 @@ __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
   set_issue_tile(0);
   auto issue_stage = [&](int g) __attribute__((always_inline)) {
     {
-      // Bytes left in the tile from this stage on (0 past the stream, and for x 0
-      // once the stage starts beyond the row's last channel, in the padding).
-      const uint32_t st0 = (uint32_t)issSt * JC * T * 16u;
-      const BufDesc d = desc_at(bTileBase + st0, (issK < myTiles && bTileBytes > st0) ? bTileBytes - st0 : 0u);
+      // The tile's blocks from this stage's chunk on (an empty range past the stream).
+      const BufDesc d = desc_at(bTileBase + (uint64_t)issSt * chunkBytes, issK < myTiles ? bTileBytes : 0u);
       const uint32_t dst = lds_addr(&ringB[g % NS][wave * IPW * 64]);
       uint32_t l[IPW];
 #pragma unroll
@@ -430,78 +507,8 @@ __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
     }
   };
 
-  // Epilogue of tile k: accumulator slot r of lane l holds row 8*(r/4) + 4*(l/32) +
-  // r%4 and column l%32 of each 32x32 block.  Stores go through a buffer
-  // descriptor covering the tile's valid rows; columns past D' take an offset
-  // beyond every range, so no store needs a branch.
-  const uint32_t outRow = (uint32_t)a.Dout * T * ELT;  // bytes of one output row
   auto epilogue = [&](int k) __attribute__((always_inline)) {
-    const int row0 = tile_row0(k), col0 = tile_col0(k);
-    const uint32_t rows = (uint32_t)min(kFwdRows, a.N - row0);
-    const __amdgpu_buffer_rsrc_t yr = make_rsrc(static_cast<char*>(a.y) + (size_t)row0 * outRow, rows * outRow);
-    // The lane index is recomputed here rather than kept live through the main
-    // loop, where every register is taken.
-    const int ln = lane_index();
-    const uint32_t laneOff = (uint32_t)(wave * 32 + 4 * (ln >> 5)) * outRow;
-    // Fused epilogue operands: an absent bias or residual gets an empty range, so
-    // its loads read zero.
-    const __amdgpu_buffer_rsrc_t br = make_rsrc(a.bias, EPI && a.bias ? (uint32_t)a.Dout * ELT : 0u);
-    const __amdgpu_buffer_rsrc_t rr =
-        make_rsrc(EPI && a.res ? static_cast<const char*>(a.res) + (size_t)row0 * outRow : nullptr,
-                  EPI && a.res ? rows * outRow : 0u);
-    const __amdgpu_buffer_rsrc_t pr =
-        make_rsrc(EPI && a.pre ? static_cast<char*>(a.pre) + (size_t)row0 * outRow : nullptr,
-                  EPI && a.pre ? rows * outRow : 0u);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int col = col0 + nb * 32 + (ln & 31);
-      const uint32_t cOff = col < a.Dout ? laneOff + (uint32_t)col * T * ELT : kOob;
-      float bv = 0.0f;
-      if constexpr (EPI) {
-        uint32_t b1[1];
-        load_group_raw<1, Elt>(br, col < a.Dout ? (uint32_t)col * ELT : kOob, b1);
-        float bf1[1];
-        group_from_raw<1, Elt>(b1, bf1);
-        bv = bf1[0];
-      }
-      // Fused epilogue: the residual groups of a chunk are loaded before any of its
-      // stores (the compiler may not move a load above a store to y, which the
-      // residual may alias), so one wait covers the chunk.
-      constexpr int RW = group_words<T, Elt>();
-      constexpr int CH = EPI ? floor_pow2(32 / RW < 1 ? 1 : (32 / RW > 16 ? 16 : 32 / RW)) : 16;
-      static_assert(16 % CH == 0, "chunks must tile the 16 accumulator slots");
-#pragma unroll
-      for (int r0 = 0; r0 < 16; r0 += CH) {
-        uint32_t rw[CH][RW];
-        if constexpr (EPI) {
-#pragma unroll
-          for (int j = 0; j < CH; ++j)
-            load_group_raw<T, Elt>(rr, cOff + (uint32_t)(8 * ((r0 + j) >> 2) + ((r0 + j) & 3)) * outRow, rw[j]);
-        }
-#pragma unroll
-        for (int j = 0; j < CH; ++j) {
-          const int r = r0 + j;
-          float P[T], yv[T];
-#pragma unroll
-          for (int p = 0; p < T; ++p) P[p] = acc[p][nb][r];
-          Idft<T, false>::run(P, yv, a.tw);
-          const uint32_t off = cOff + (uint32_t)(8 * (r >> 2) + (r & 3)) * outRow;
-          if constexpr (EPI) {
-            float rv[T];
-            group_from_raw<T, Elt>(rw[j], rv);
-#pragma unroll
-            for (int g = 0; g < T; ++g) yv[g] += bv;
-            if (a.pre) store_group_buf<T, Elt>(pr, off, yv);
-#pragma unroll
-            for (int g = 0; g < T; ++g) {
-              const float v = a.act == 1 ? gelu_erf(yv[g]) : yv[g];
-              yv[g] = v + rv[g];
-            }
-          }
-          store_group_buf<T, Elt>(yr, off, yv);
-        }
-      }
-    }
+    fwd_epilogue<T, Elt, NB, EPI>(a, acc, tile_row0(k), wave * 32, tile_col0(k));
   };
 
   using I0 = std::integral_constant<int, 0>;
@@ -577,6 +584,302 @@ __global__ void __launch_bounds__(256) eql_fwd_kernel(const FwdArgs a) {
   }
   // Drain the look-ahead loads (all out of range) before the workgroup's LDS can
   // be reused.
+  wait_vmcnt<0>();
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+// Waves per workgroup of eql_fwd4_kernel: two per SIMD (each with half the tile's
+// column blocks) when the tile has two column blocks or more, else one.  With T = 3 and
+// four blocks the weight stage (12 KB) does not split into whole 1 KB loads over 8 waves.
+__host__ __device__ constexpr int fwd4_waves(int T, int NB) { return NB >= 2 && !(T == 3 && NB == 4) ? 8 : 4; }
+
+// The fast forward kernel for T <= 4 and 16-byte-aligned rows (see the file comment).
+//   * Ring: 4 slots of (weight stage, x stage).  Stage g of the workgroup's stream
+//     lives in slot g % 4 and is loaded 3 stages ahead.  The loop body is unrolled over
+//     the 4 slots; nst is even, so a tile starts at slot 0 or 2 ("phase").  Slots 0, 1
+//     of the body live at pair base A (physical slots phase, phase + 1), slots 2, 3 at
+//     pair base B; both bases are kept per lane for reads and per wave for DMA, so every
+//     LDS address is a base register plus an immediate.
+//   * Weight DMA: a stage of the tile is NB contiguous T KB chunks (packed_unit); wave w
+//     loads IPW consecutive KB of it with one M0 write.  x DMA: the tile's 128 rows x
+//     128 bytes (p4 fp16) in 1 KB loads spread over the waves.
+//   * Issue state (next stage's weight and x addresses, x bytes left in the tile) is
+//     bumped by constants per stage; the one tile boundary the issue side crosses
+//     during a compute tile switches to the next tile's state, prepared at the compute
+//     tile's start, by scalar selects: the stage bodies have no branches, so the
+//     compiler keeps the next stage's transform interleaved with the MFMAs.
+//   * Stage g: read block 0's weight fragments (landed before the previous barrier),
+//     wait for this wave's loads of stage g+1, barrier, issue stage g+3, read x of
+//     stage g+1, then per column block: next block's fragments, the block's MFMAs,
+//     and after block 0 the transform of x stage g+1 into the other fragment buffer.
+template <int T, typename Elt, int NB, int LOAD, int EPI>
+__global__ void __launch_bounds__(64 * fwd4_waves(T, NB)) eql_fwd4_kernel(const FwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using E = EltT<Elt>;
+  constexpr int WAVES = fwd4_waves(T, NB);
+  constexpr int G = E::kPerUnit;
+  constexpr int NR = n_real_planes(T);
+  constexpr int NP = n_pairs(T);
+  constexpr int BN = 32 * NB;
+  constexpr int NBW = NB * 4 / WAVES;      // column blocks per wave
+  constexpr int RP = 8;                    // x ring row: 2T <= 8 units
+  constexpr int ELT = (int)sizeof(Elt);
+  constexpr int NS = 4, DIST = 3;
+  constexpr int BKB = NB * T;              // KB of packed weight per stage
+  constexpr int BSLOT = BKB * 1024;
+  constexpr int XSLOT = kFwdRows * RP * 16;
+  constexpr int IPW = BKB >= WAVES ? BKB / WAVES : 1;  // weight DMA loads per wave per stage
+  constexpr int IPWX = kFwdRows * RP / 64 / WAVES;     // x DMA loads per wave per stage
+  constexpr int SB = 2 * G * T * ELT;                  // bytes of one x row per stage
+  static_assert(T <= 4 && LOAD != kLoadNarrow && NBW >= 1, "fast path: T <= 4, 16-byte rows");
+  static_assert(BKB < WAVES || BKB % WAVES == 0, "whole 1 KB weight loads per wave");
+  static_assert(IPW <= 4 || IPW == 6 || IPW == 8, "weight run length");
+  static_assert(IPWX == 2 || IPWX == 4, "x loads per wave");
+  static_assert(NS * (BSLOT + XSLOT) <= 160 * 1024, "LDS budget");
+  // Per-slot immediate offsets stay below 64 KB: slot pairs are 2 slots apart.
+  static_assert(BSLOT + BKB * 1024 <= 65536 && XSLOT + XSLOT <= 65536, "ds_read offset range");
+  constexpr int WAIT_TOP = (DIST - 2) * (IPW + IPWX);
+  constexpr int WAIT_PRO = (DIST - 1) * (IPW + IPWX);
+  static_assert(WAIT_PRO < 64, "vmcnt range");
+
+  __shared__ u32x4 ringB[NS][BSLOT / 16];
+  __shared__ u32x4 ringX[NS][XSLOT / 16];
+
+  // Persistent schedule as eql_fwd_kernel: workgroup b takes tiles xcd_remap(b + k grid).
+  const int b0 = blockIdx.x, grid = gridDim.x;
+  if (b0 >= a.numTiles) return;
+  const int myTiles = (a.numTiles - b0 + grid - 1) / grid;
+  const int nst = a.Jpad / 2;
+  const int nblk = (a.Dout + 31) >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int rb = wave & 3;                 // 32-row block of the tile
+  const int cb = WAVES == 8 ? wave >> 2 : 0;  // column half (8 waves)
+  // This wave's weight KBs of a stage: q = qw .. qw + IPW - 1 (block q / T, KB q % T).
+  const int qw = BKB >= WAVES ? wave * IPW : wave % BKB;
+  const int cw = qw / T, kbw = qw - cw * T;
+  const uint32_t rowBytes = (uint32_t)a.Cin * T * ELT;
+  const uint64_t chunkStride = (uint64_t)T * 1024;
+  const uint64_t blockStride = (uint64_t)nst * chunkStride;
+
+  auto tile_of = [&](int k) __attribute__((always_inline)) { return xcd_remap(b0 + k * grid, a.numTiles); };
+
+  // Lane-derived values, re-derived after every epilogue (none is live there; see
+  // eql_fwd_kernel).
+  int phase = 0;
+  uint32_t bRdA, bRdB, xRdA[T], xRdB[T], bVoff, xOff[IPWX];
+  int xCh[IPWX];
+  auto lane_setup = [&]() __attribute__((always_inline)) {
+    const int lane = lane_index();
+    const int lrow = lane & 31, khalf = lane >> 5;
+    bVoff = (uint32_t)lane * 16u;
+    const uint32_t pa = (uint32_t)phase, pb = (uint32_t)((phase + 2) & 3);
+    // Weight fragment (block 0, plane 0) of this lane: channel lrow of the block, group
+    // khalf of the stage (packed_unit's order within a chunk).
+    const uint32_t bl = (uint32_t)(lrow * 32 + ((khalf ^ ((lrow >> 3) & 1)) * 16));
+    bRdA = lds_addr(&ringB[0][0]) + pa * BSLOT + bl;
+    bRdB = lds_addr(&ringB[0][0]) + pb * BSLOT + bl;
+    const int row = rb * 32 + lrow;
+#pragma unroll
+    for (int v = 0; v < T; ++v) {
+      const int u = khalf * T + v;
+      const uint32_t xl = (uint32_t)((row * RP + (u ^ ring_swz<RP>(row))) * 16);
+      xRdA[v] = lds_addr(&ringX[0][0]) + pa * XSLOT + xl;
+      xRdB[v] = lds_addr(&ringX[0][0]) + pb * XSLOT + xl;
+    }
+    // x DMA: ring position P = (wave IPWX + i) 64 + lane holds unit (P % RP) ^ swz of
+    // row P / RP (padding units past 2T load an arbitrary unit of the row).
+#pragma unroll
+    for (int i = 0; i < IPWX; ++i) {
+      const int P = (wave * IPWX + i) * 64 + lane;
+      const int rw = P / RP, pos = P - rw * RP;
+      const int u = pos ^ ring_swz<RP>(rw);
+      const int uu = u < 2 * T ? u : 0;
+      xOff[i] = (uint32_t)rw * rowBytes + (uint32_t)uu * 16u;
+      xCh[i] = (uu * 16) / (T * ELT);
+    }
+  };
+  lane_setup();
+
+  // Issue side.
+  int issSt = 0, issK = 0;
+  uint64_t bCur = 0, xCur = 0, nbCur = 0, nxCur = 0;
+  uint32_t bLen = 0, xLeft = 0, nbLen = 0, nxLeft = 0;
+  auto tile_state = [&](int k, uint64_t& bc, uint32_t& bl, uint64_t& xc, uint32_t& xl) __attribute__((always_inline)) {
+    if (k < myTiles) {
+      const int t = tile_of(k);
+      const int rt = t / a.colTiles;
+      const int row0 = rt * kFwdRows, col0 = (t - rt * a.colTiles) * BN;
+      const int ob = (col0 >> 5) + cw;
+      bc = reinterpret_cast<uint64_t>(a.wp) + (uint64_t)ob * blockStride + (uint64_t)kbw * 1024;
+      bl = ob < nblk ? (uint32_t)(IPW * 1024) : 0u;
+      xc = reinterpret_cast<uint64_t>(a.x) + (uint64_t)row0 * rowBytes;
+      xl = (uint32_t)min(kFwdRows, a.N - row0) * rowBytes;
+    } else {
+      bc = xc = 0;
+      bl = xl = 0;
+    }
+  };
+  tile_state(0, bCur, bLen, xCur, xLeft);
+  uint32_t bDmaA, bDmaB, xDmaA, xDmaB;
+  auto ring_setup = [&]() __attribute__((always_inline)) {
+    const uint32_t pa = (uint32_t)phase, pb = (uint32_t)((phase + 2) & 3);
+    bDmaA = lds_addr(&ringB[0][0]) + pa * BSLOT + (uint32_t)qw * 1024u;
+    bDmaB = lds_addr(&ringB[0][0]) + pb * BSLOT + (uint32_t)qw * 1024u;
+    xDmaA = lds_addr(&ringX[0][0]) + pa * XSLOT + (uint32_t)(wave * IPWX * 1024);
+    xDmaB = lds_addr(&ringX[0][0]) + pb * XSLOT + (uint32_t)(wave * IPWX * 1024);
+  };
+  ring_setup();
+  auto issue = [&](auto slotTag) __attribute__((always_inline)) {
+    constexpr int S = decltype(slotTag)::value;
+    dma16_run<IPW, (S & 1) * BSLOT>(desc_words(bCur, bLen), bVoff, S < 2 ? bDmaA : bDmaB);
+    {
+      uint32_t off[IPWX];
+      const int c0 = issSt * 2 * G;
+#pragma unroll
+      for (int i = 0; i < IPWX; ++i) off[i] = (LOAD == kLoadFull || c0 + xCh[i] < a.Cin) ? xOff[i] : kOob;
+      dma16_each<IPWX, (S & 1) * XSLOT>(desc_words(xCur, xLeft), off, S < 2 ? xDmaA : xDmaB);
+    }
+    bCur += chunkStride;
+    xCur += SB;
+    xLeft = xLeft > (uint32_t)SB ? xLeft - SB : 0u;
+    const bool wrap = ++issSt == nst;
+    issSt = wrap ? 0 : issSt;
+    issK = wrap ? issK + 1 : issK;
+    bCur = wrap ? nbCur : bCur;
+    bLen = wrap ? nbLen : bLen;
+    xCur = wrap ? nxCur : xCur;
+    xLeft = wrap ? nxLeft : xLeft;
+  };
+
+  auto rd = [&](uint32_t addr, int imm) __attribute__((always_inline)) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(
+        (const __attribute__((address_space(3))) char*)(uintptr_t)addr + imm);
+  };
+
+  uint32_t raw[4 * T];
+  u32x4 af[2][T + NP];
+  auto read_x = [&](auto slotTag) __attribute__((always_inline)) {
+    constexpr int S = decltype(slotTag)::value;
+#pragma unroll
+    for (int v = 0; v < T; ++v) {
+      const u32x4 val = rd(S < 2 ? xRdA[v] : xRdB[v], (S & 1) * XSLOT);
+      raw[4 * v + 0] = val[0];
+      raw[4 * v + 1] = val[1];
+      raw[4 * v + 2] = val[2];
+      raw[4 * v + 3] = val[3];
+    }
+  };
+  auto transform = [&](auto abTag) __attribute__((always_inline)) {
+    constexpr int ab = decltype(abTag)::value;
+    if constexpr (T == 4 && ELT == 2) {
+      dft_p4_f16(raw, af[ab]);
+    } else {
+      float pl[T][G];
+#pragma unroll
+      for (int e = 0; e < G; ++e) {
+        float v[T], o[T];
+#pragma unroll
+        for (int h = 0; h < T; ++h) {
+          const int i = e * T + h;
+          if constexpr (ELT == 2) v[h] = (float)__builtin_bit_cast(_Float16, (uint16_t)(raw[i / 2] >> ((i & 1) * 16)));
+          else v[h] = __builtin_bit_cast(float, raw[i]);
+        }
+        Dft<T>::run(v, o, a.tw);
+#pragma unroll
+        for (int p = 0; p < T; ++p) pl[p][e] = o[p];
+      }
+#pragma unroll
+      for (int p = 0; p < T; ++p) af[ab][p] = E::pack(pl[p]);
+#pragma unroll
+      for (int q = 0; q < NP; ++q) af[ab][T + q] = neg_unit(af[ab][NR + 2 * q + 1], E::kSignMask);
+    }
+  };
+
+  f32x16 acc[T][NBW];
+  auto zero_acc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < T; ++p)
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) E::zero(acc[p][nb]);
+  };
+
+  auto stage = [&](auto slotTag) __attribute__((always_inline)) {
+    constexpr int S = decltype(slotTag)::value;
+    constexpr int cur = S & 1;
+    using Nxt = std::integral_constant<int, cur ^ 1>;
+    using SN = std::integral_constant<int, (S + 1) % NS>;
+    using SI = std::integral_constant<int, (S + DIST) % NS>;
+    u32x4 bf[2][T];
+#pragma unroll
+    for (int p = 0; p < T; ++p) bf[0][p] = rd(S < 2 ? bRdA : bRdB, (S & 1) * BSLOT + (cb * NBW * T + p) * 1024);
+    wait_vmcnt<WAIT_TOP>();
+    // Plain barrier (no fence): the ring reads of stage g-1 are consumed, and a fence
+    // would also wait for the loads in flight.
+    __builtin_amdgcn_s_barrier();
+    issue(SI{});
+    read_x(SN{});
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) {
+      if (nb + 1 < NBW) {
+#pragma unroll
+        for (int p = 0; p < T; ++p)
+          bf[(nb + 1) & 1][p] = rd(S < 2 ? bRdA : bRdB, (S & 1) * BSLOT + ((cb * NBW + nb + 1) * T + p) * 1024);
+      }
+      const u32x4(&b)[T] = bf[nb & 1];
+#pragma unroll
+      for (int p = 0; p < NR; ++p) E::mfma(acc[p][nb], af[cur][p], b[p]);
+#pragma unroll
+      for (int q = 0; q < NP; ++q) {
+        const int re = NR + 2 * q, im = re + 1;
+        E::mfma(acc[re][nb], af[cur][re], b[re]);
+        E::mfma(acc[re][nb], af[cur][T + q], b[im]);
+        E::mfma(acc[im][nb], af[cur][im], b[re]);
+        E::mfma(acc[im][nb], af[cur][re], b[im]);
+      }
+      if (nb == 0) transform(Nxt{});  // x stage g+1; overlaps the MFMA chains
+    }
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+
+  // Prologue: stages 0..2 into slots 0..2 (with nst = 2 the third is tile 1's stage 0),
+  // then x of stage 0.
+  tile_state(1, nbCur, nbLen, nxCur, nxLeft);
+  issue(I0{});
+  issue(I1{});
+  issue(I2{});
+  wait_vmcnt<WAIT_PRO>();
+  __builtin_amdgcn_s_barrier();
+  read_x(I0{});
+  transform(I0{});
+
+  for (int k = 0; k < myTiles; ++k) {
+    // During this tile's nst stages the issue side crosses exactly one tile boundary.
+    tile_state(issK + 1, nbCur, nbLen, nxCur, nxLeft);
+    zero_acc();
+    int st = 0;
+    for (; st + 4 <= nst; st += 4) {
+      stage(I0{});
+      stage(I1{});
+      stage(I2{});
+      stage(I3{});
+    }
+    if (st < nst) {  // nst = 2 (mod 4): the next tile starts two slots on
+      stage(I0{});
+      stage(I1{});
+    }
+    phase = (phase + nst) & 3;
+    ring_setup();
+    const int t = tile_of(k);
+    const int rt = t / a.colTiles;
+    fwd_epilogue<T, Elt, NBW, EPI>(a, acc, rt * kFwdRows, rb * 32, (t - rt * a.colTiles) * BN + cb * NBW * 32);
+    lane_setup();
+  }
+  // Drain the look-ahead loads (all out of range) before the workgroup's LDS can be
+  // reused.
   wait_vmcnt<0>();
 #endif  // __HIP_DEVICE_COMPILE__
 }

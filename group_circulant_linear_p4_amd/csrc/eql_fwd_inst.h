@@ -1,7 +1,7 @@
 // Forward-kernel instantiations for one element type and epilogue: T = 1..16, the
 // full-width tile (fwd_nb_max(T) column blocks), the two-block tile where the full
 // width is four blocks, the one-block tile, and the three load modes (see
-// eql_fwd.h).  Each of eql_fwd_{f16,f32}.hip (plain epilogue) and
+// eql_fwd.h); T <= 4 with 16-byte rows takes eql_fwd4_kernel.  Each of eql_fwd_{f16,f32}.hip (plain epilogue) and
 // eql_fwd_fused_{f16,f32}.hip (bias / activation / residual) instantiates one.
 #pragma once
 
@@ -11,9 +11,15 @@ namespace eql {
 
 template <typename Elt, int EPI>
 struct FwdInst {
+  // T <= 4 with 16-byte rows: the fast kernel; otherwise the generic one.
   template <int T, int NB, int MODE>
   static hipError_t launch(const FwdArgs& a, unsigned grid, hipStream_t s) {
-    return launch_kernel((const void*)&eql_fwd_kernel<T, Elt, NB, fwd_jc(T), MODE, EPI>, grid, a, s);
+    if constexpr (T <= 4 && MODE != kLoadNarrow) {
+      return launch_kernel((const void*)&eql_fwd4_kernel<T, Elt, NB, MODE, EPI>, grid, a, s,
+                           64u * (unsigned)fwd4_waves(T, NB));
+    } else {
+      return launch_kernel((const void*)&eql_fwd_kernel<T, Elt, NB, fwd_jc(T), MODE, EPI>, grid, a, s);
+    }
   }
 
   // Narrow loads with the one-column-block tile only.

@@ -44,9 +44,9 @@ hipError_t launch_epi_bias(bool f16, const EpiBwdArgs& a, unsigned grid, hipStre
 hipError_t launch_pack_f32(int T, const PackArgs& a, unsigned grid, hipStream_t s);
 
 template <typename A>
-inline hipError_t launch_kernel(const void* fn, unsigned grid, const A& args, hipStream_t s) {
+inline hipError_t launch_kernel(const void* fn, unsigned grid, const A& args, hipStream_t s, unsigned block = 256) {
   void* kargs[] = {const_cast<A*>(&args)};
-  return hipLaunchKernel(fn, dim3(grid), dim3(256), kargs, 0, s);
+  return hipLaunchKernel(fn, dim3(grid), dim3(block), kargs, 0, s);
 }
 
 // Expands F(T) for T = 1..16 inside a switch on `t`.

@@ -2,8 +2,9 @@
 // ("Abordagem Algoritmica" in "Resumo Tecnico: Flash EQ-Linear": the Fourier-domain
 // products need the DFT of w, and conjugate symmetry keeps half of it).
 //
-// One thread per (out, in) pair of the packed matrix (plus the zero padding of the
-// input axis up to the padded group count).  It reads the T shared parameters,
+// One thread per (out, in) pair of the packed matrix (plus the zero padding of both
+// axes: output channels to a multiple of 32, input channels to the padded group
+// count).  It reads the T shared parameters,
 // transforms them in fp32 (p4: butterflies only), divides each plane by its share
 // of the inverse transform's scale and rounds it once to the element type.  In the input-gradient mode the weight is the transposed,
 // group-reversed w~[c][d][t] = w[d][c][(-t) mod T]; its spectrum is the conjugate,
@@ -16,10 +17,24 @@ namespace eql {
 
 struct PackArgs {
   const void* w;    // [Dp][Cp][T]
-  void* wp;         // packed: ((o * Jin + i / G) * T + p) * G + i % G
+  void* wp;         // packed: packed_unit(o, i / G, p) * G + i % G
   int Dp, Cp, outCh, inCh, Jin, transposed;
   Twiddles tw;
 };
+
+// Output channels per block of the packed weight.
+constexpr int kPackBlock = 32;
+
+// 16-byte unit of the packed weight holding input-channel group j of plane p for
+// output channel o.  Output channels form blocks of 32; a block's data is one chunk of
+// T * 64 units per K stage (two groups), and inside a chunk the units are ordered
+// [plane][channel of the block][group of the stage, XOR bit 3 of the channel].  A
+// forward kernel stage then reads each block as one contiguous T KB run, and the
+// fragment reads of 16 consecutive channels land on distinct LDS bank groups.
+__host__ __device__ inline size_t packed_unit(int o, int j, int p, int T, int stages) {
+  const int ob = o / kPackBlock, ol = o % kPackBlock, s = j >> 1, jj = j & 1;
+  return (((size_t)ob * stages + s) * T + p) * 64 + (size_t)ol * 2 + (jj ^ ((ol >> 3) & 1));
+}
 
 template <int T, typename Elt>
 __global__ void __launch_bounds__(256) eql_pack_kernel(const PackArgs a) {
@@ -27,13 +42,14 @@ __global__ void __launch_bounds__(256) eql_pack_kernel(const PackArgs a) {
   constexpr int NR = n_real_planes(T);
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   const size_t row = (size_t)a.Jin * G;
-  if (idx >= (size_t)a.outCh * row) return;
+  const int outPad = (a.outCh + kPackBlock - 1) / kPackBlock * kPackBlock;
+  if (idx >= (size_t)outPad * row) return;
   const int o = (int)(idx / row);
   const int i = (int)(idx - (size_t)o * row);
   float pl[T];
 #pragma unroll
   for (int p = 0; p < T; ++p) pl[p] = 0.0f;
-  if (i < a.inCh) {
+  if (i < a.inCh && o < a.outCh) {
     const int d = a.transposed ? i : o;
     const int c = a.transposed ? o : i;
     float v[T];
@@ -49,9 +65,9 @@ __global__ void __launch_bounds__(256) eql_pack_kernel(const PackArgs a) {
       for (int p = NR + 1; p < T; p += 2) pl[p] = -pl[p];
     }
   }
-  Elt* out = static_cast<Elt*>(a.wp) + (((size_t)o * a.Jin + i / G) * T) * G + (i % G);
+  Elt* out = static_cast<Elt*>(a.wp);
 #pragma unroll
-  for (int p = 0; p < T; ++p) out[p * G] = (Elt)pl[p];
+  for (int p = 0; p < T; ++p) out[packed_unit(o, i / G, p, T, a.Jin / 2) * G + (i % G)] = (Elt)pl[p];
 }
 
 }  // namespace eql

@@ -330,12 +330,21 @@ def test_fwd_fused_mlp_expansion_full_size():
 
 # ------------------------------------------------------------------ pack layout
 def unpack(buf, out_ch, in_ch, T, dtype):
+    """Planes of the packed weight in the documented layout: output channels in blocks
+    of 32; per block and stage of two 16-byte input groups one chunk of T*64 units,
+    ordered [plane][channel of the block][group of the stage XOR bit 3 of the channel]."""
     G = 16 // np.dtype(NPDT[dtype]).itemsize
     jin = -(-(-(-in_ch // G)) // 4) * 4          # ceil(in / G) rounded up to a multiple of 4
-    a = host(buf).view(NPDT[dtype]).astype(np.float64).reshape(out_ch, jin, T, G)
-    planes = a.transpose(0, 1, 3, 2).reshape(out_ch, jin * G, T)
-    assert np.all(planes[:, in_ch:, :] == 0)
-    planes = planes[:, :in_ch, :]
+    opad = -(-out_ch // 32) * 32
+    a = host(buf).view(NPDT[dtype]).astype(np.float64)
+    assert a.size == opad * jin * T * G
+    a = a.reshape(opad // 32, jin // 2, T, 32, 2, G)  # [block][stage][plane][channel][half'][element]
+    ol = np.arange(32)
+    swz = (ol >> 3) & 1
+    halves = np.stack([a[:, :, :, ol, h ^ swz, :] for h in (0, 1)], axis=4)  # undo the XOR: [.., ol, half, G]
+    planes = halves.transpose(0, 3, 1, 4, 5, 2).reshape(opad, jin * G, T)  # [o][input channel][plane]
+    assert np.all(planes[out_ch:] == 0) and np.all(planes[:, in_ch:, :] == 0)
+    planes = planes[:out_ch, :in_ch, :]
     nr = 2 if (T % 2 == 0 and T > 1) else 1
     planes[:, :, :nr] *= T                         # stored with the inverse's 1/T ...
     planes[:, :, nr:] *= T / 2.0                   # ... and 2/T on the complex planes
