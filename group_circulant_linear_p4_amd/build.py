@@ -55,8 +55,10 @@ def hipcc() -> str:
     return path
 
 
-def _compile(src: str, extra: list[str]) -> str:
+def _compile(src: str, extra: list[str], reuse: bool = False) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    if reuse and os.path.exists(obj):
+        return obj
     cmd = [hipcc(), *CFLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -64,13 +66,17 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build_library(jobs: int | None = None, extra_flags: list[str] | None = None, verbose: bool = False) -> str:
-    """Compile every source and link libeqlinear.so; returns the library path."""
+def build_library(jobs: int | None = None, extra_flags: list[str] | None = None, verbose: bool = False,
+                  only: list[str] | None = None) -> str:
+    """Compile every source and link libeqlinear.so; returns the library path.
+
+    only: recompile just these sources and reuse the other objects of an earlier full
+    build (for iterating on one translation unit; the default compiles everything)."""
     os.makedirs(BUILD, exist_ok=True)
     extra = list(extra_flags or [])
     jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 2)))
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, extra, reuse=only is not None and s not in only), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -83,5 +89,7 @@ def build_library(jobs: int | None = None, extra_flags: list[str] | None = None,
 
 
 if __name__ == "__main__":
-    build_library(verbose=True)
+    # python -m group_circulant_linear_p4_amd.build [source.hip ...]: with arguments,
+    # only those sources are recompiled (see build_library's `only`).
+    build_library(verbose=True, only=sys.argv[1:] or None)
     sys.exit(0)

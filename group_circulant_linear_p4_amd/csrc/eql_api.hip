@@ -218,7 +218,7 @@ BwdwPlan plan_bwdw(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype) {
 
 extern "C" {
 
-int eqlinear_abi_version(void) { return 101; }
+int eqlinear_abi_version(void) { return 200; }
 
 const char* eqlinear_status_string(int status) {
   switch (status) {

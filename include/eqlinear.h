@@ -93,13 +93,16 @@ typedef enum {
  * (out = c, in = d), whose spectrum is the complex conjugate: the Im planes
  * change sign.
  *
- * Layout: G = 16 / sizeof(element) (8 for fp16, 4 for fp32) input channels form
- * one 16-byte group; Jin = ceil(in / G) rounded up to a multiple of 4.  Element
- * (o, i, plane p) is stored at
- *     ((o * Jin + i / G) * T + p) * G + i % G
- * and entries with i >= in are zero.  Size = out * Jin * G * T elements
- * (out * Jin * 16 * T bytes), given by eqlinear_packed_weight_bytes(out, in, T,
- * dtype); it must stay below 2^32 bytes.
+ * Layout (blocked for the forward kernels' loads): G = 16 / sizeof(element) (8 for
+ * fp16, 4 for fp32) input channels form one 16-byte group j = i / G;
+ * Jin = ceil(in / G) rounded up to a multiple of 4; S = Jin / 2 stages of two groups;
+ * output channels form blocks of 32 (out padded to Opad = 32 * ceil(out / 32)).  With
+ * b = o / 32, c = o % 32, the 16-byte unit holding group j of plane p is
+ *     u(o, j, p) = ((b * S + j / 2) * T + p) * 64 + 2 c + ((j % 2) XOR ((c / 8) % 2))
+ * and element (o, i, p) is stored at u(o, i / G, p) * G + i % G: per block and stage
+ * one contiguous run of T * 64 units.  Entries with i >= in or o >= out are zero.
+ * Size = Opad * Jin * G * T elements (Opad * Jin * 16 * T bytes), given by
+ * eqlinear_packed_weight_bytes(out, in, T, dtype); it must stay below 2^32 bytes.
  * The transform runs in fp32 and rounds once to `dtype`.
  */
 size_t eqlinear_packed_weight_bytes(int64_t out_ch, int64_t in_ch, int T, int dtype);
@@ -219,7 +222,8 @@ int eqlinear_bwd_w(const void* x, const void* dy, void* dw, void* workspace, siz
 /* Static, human-readable name of a status code (never NULL). */
 const char* eqlinear_status_string(int status);
 
-/* ABI version of this header (major * 100 + minor). */
+/* ABI version of this header (major * 100 + minor).  2.00: the blocked packed-weight
+ * layout above (1.xx stored ((o * Jin + i / G) * T + p) * G + i % G). */
 int eqlinear_abi_version(void);
 
 #ifdef __cplusplus

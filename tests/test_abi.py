@@ -33,20 +33,21 @@ def test_library_loads_and_exports_every_declared_function():
 
 
 def test_version_and_status_strings():
-    assert eql.eqlinear_abi_version() == 101
+    assert eql.eqlinear_abi_version() == 200
     for s in range(5):
         assert eql.eqlinear_status_string(s)
     assert eql.eqlinear_status_string(99) == "unknown status"
 
 
 def test_packed_weight_bytes():
-    # out * Jin * 16 * T bytes, Jin = ceil(in / G) rounded up to a multiple of 4,
-    # G = 16 / sizeof(elt)
-    assert eql.eqlinear_packed_weight_bytes(3, 5, 4, eql.EQL_F16) == 3 * 4 * 16 * 4
-    assert eql.eqlinear_packed_weight_bytes(3, 33, 4, eql.EQL_F16) == 3 * 8 * 16 * 4
+    # Opad * Jin * 16 * T bytes: Opad = out rounded up to a multiple of 32, Jin =
+    # ceil(in / G) rounded up to a multiple of 4, G = 16 / sizeof(elt)
+    assert eql.eqlinear_packed_weight_bytes(3, 5, 4, eql.EQL_F16) == 32 * 4 * 16 * 4
+    assert eql.eqlinear_packed_weight_bytes(3, 33, 4, eql.EQL_F16) == 32 * 8 * 16 * 4
     assert eql.eqlinear_packed_weight_bytes(1024, 1024, 4, eql.EQL_F16) == 1024 * 1024 * 4 * 2
     assert eql.eqlinear_packed_weight_bytes(64, 64, 8, eql.EQL_F32) == 64 * 64 * 8 * 4
-    assert eql.eqlinear_packed_weight_bytes(7, 3, 3, eql.EQL_F32) == 7 * 4 * 16 * 3
+    assert eql.eqlinear_packed_weight_bytes(7, 3, 3, eql.EQL_F32) == 32 * 4 * 16 * 3
+    assert eql.eqlinear_packed_weight_bytes(33, 3, 3, eql.EQL_F32) == 64 * 4 * 16 * 3
     assert eql.eqlinear_packed_weight_bytes(3, 3, 0, eql.EQL_F32) == 0
     assert eql.eqlinear_packed_weight_bytes(3, 3, 17, eql.EQL_F32) == 0
     assert eql.eqlinear_packed_weight_bytes(3, 3, 4, 7) == 0
