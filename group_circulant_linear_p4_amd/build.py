@@ -34,11 +34,12 @@ SOURCES = [
     "eql_bwdw_real_f32.hip",
     "eql_bwdw_pair_f16.hip",
     "eql_bwdw_pair_f32.hip",
+    "eql_bwdw4.hip",
     "eql_epi.hip",
 ]
 
 CFLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
+    "-O3", "-std=c++20", "-fPIC", "--offload-arch=" + ARCH,
     # No packed-fp32 instructions: every fp32 op is scalar per lane.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # Rounding is decided by the source: no implicit multiply-add contraction.

@@ -5,6 +5,8 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
+#include <cstring>
 
 #include "eql_launch.h"
 #include "eqlinear.h"
@@ -168,9 +170,40 @@ int64_t tile_width(int64_t ch) { return ceil_div(ch, 256) * 256 * 3 <= ch * 4 ? 
 struct BwdwPlan {
   int64_t kgCount = 0, Dpad = 0, Cpad = 0;
   GemmPlan real, pair;
+  // Fused path (dy transformed inside the GEMM, eql_bwdw4_kernel): one launch over
+  // S x dTiles x cTiles items of 128 x 128 output channels, all planes.
+  bool fused = false;
+  int64_t fS = 0, fKgPerSplit = 0, fDTiles = 0, fCTiles = 0;
   size_t dyhBytes = 0, xhBytes = 0, partRBytes = 0, partPBytes = 0;
   size_t total() const { return dyhBytes + xhBytes + partRBytes + partPBytes; }
 };
+
+// Which weight-gradient path a shape takes.  The fused path (dy's transform inside
+// the GEMM, all T planes per tile) reads dy once and never writes its spectrum, but
+// its 128 x 128 x T tiles move more operand bytes per MFMA than the separate path's
+// per-plane tiles.  It wins where the layer is bound by memory traffic: actual FLOPs
+// per algorithmic byte below kFusedIntensity (the fp16 MFMA / HBM ridge is about
+// 315).  It needs T in {1, 2, 4} and 16-byte dy rows.  The environment variable
+// EQL_BWDW_PATH=fused|separate overrides the choice where the fused path applies
+// (for measurement).
+constexpr double kFusedIntensity = 400.0;
+
+bool bwdw_fused(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype) {
+  const int elt = elt_bytes(dtype);
+  if (N == 0 || !(T == 1 || T == 2 || T == 4) || (Dp * T * elt) % 16 != 0) return false;
+  if ((double)N * (double)(Dp * T * elt) >= 4294967296.0) return false;  // dy within one 32-bit range
+  static const int forced = [] {
+    const char* v = std::getenv("EQL_BWDW_PATH");
+    if (v && std::strcmp(v, "fused") == 0) return 1;
+    if (v && std::strcmp(v, "separate") == 0) return 2;
+    return 0;
+  }();
+  if (forced) return forced == 1;
+  const double planes = T == 1 ? 1.0 : (T == 2 ? 2.0 : 6.0);  // real products per (d, c) pair
+  const double flops = 2.0 * planes * (double)N * (double)Dp * (double)Cp;
+  const double bytes = (double)elt * T * (double)N * (double)(Cp + Dp);
+  return flops / bytes < kFusedIntensity;
+}
 
 constexpr int64_t kMinStepsPerSplit = 16;  // keeps partial-spectrum traffic small
 
@@ -205,6 +238,22 @@ BwdwPlan plan_bwdw(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype) {
   p.pair.cTiles = p.Cpad / (64 * p.pair.CB);
   if (N == 0) return p;
   p.kgCount = ceil_div(N, 2 * group_channels(dtype));
+  if (bwdw_fused(N, Cp, Dp, T, dtype)) {
+    p.fused = true;
+    p.fDTiles = ceil_div(Dp, kBwdw4Tile);
+    p.fCTiles = ceil_div(Cp, kBwdw4Tile);
+    p.Cpad = p.fCTiles * kBwdw4Tile;
+    const int64_t tiles = p.fDTiles * p.fCTiles;
+    int64_t S = std::max<int64_t>(1, kTargetWorkgroups / tiles);
+    S = std::min<int64_t>(S, std::max<int64_t>(1, p.kgCount / kMinStepsPerSplit));
+    p.fKgPerSplit = ceil_div(p.kgCount, S);
+    p.fS = ceil_div(p.kgCount, p.fKgPerSplit);
+    p.real.S = p.pair.S = p.fS;
+    p.xhBytes = align256((size_t)p.kgCount * T * 2 * (size_t)p.Cpad * 16);
+    p.partRBytes = align256((size_t)p.fS * nr * (size_t)Dp * (size_t)Cp * sizeof(float));
+    p.partPBytes = (size_t)p.fS * (T - nr) * (size_t)Dp * (size_t)Cp * sizeof(float);
+    return p;
+  }
   plan_splits(p.real, p.kgCount);
   plan_splits(p.pair, p.kgCount);
   p.dyhBytes = align256((size_t)p.kgCount * T * 2 * (size_t)p.Dpad * 16);
@@ -372,8 +421,9 @@ int eqlinear_bwd_w(const void* x, const void* dy, void* dw, void* workspace, siz
   const int64_t gx = ceil_div(p.kgCount * 2 * p.Cpad, 256);
   const int rwaves = reduce_waves(p.real.S * n_real_planes(T) + p.pair.S * (T - n_real_planes(T)));
   const int64_t rgrid = ceil_div(Dp * Cp, 256 / rwaves);
+  const int64_t fItems = p.fS * p.fDTiles * p.fCTiles;
   if (p.real.items() > kMaxGrid || p.pair.items() > kMaxGrid || gdy > kMaxGrid || gx > kMaxGrid ||
-      rgrid > kMaxGrid)
+      rgrid > kMaxGrid || fItems > kMaxGrid)
     return EQL_EINVAL;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -382,7 +432,36 @@ int eqlinear_bwd_w(const void* x, const void* dy, void* dw, void* workspace, siz
   float* partR = reinterpret_cast<float*>(ws + p.dyhBytes + p.xhBytes);
   float* partP = reinterpret_cast<float*>(ws + p.dyhBytes + p.xhBytes + p.partRBytes);
   const bool f16 = dtype == EQL_F16;
-  if (N > 0) {
+  if (N > 0 && p.fused) {
+    // x's spectrum only; dy is transformed inside the GEMM.
+    SpecArgs sp{};
+    sp.N = (int)N;
+    sp.kgCount = (int)p.kgCount;
+    sp.tw = tw;
+    sp.m = x;
+    sp.out = ws;
+    sp.K = (int)Cp;
+    sp.Kpad = (int)p.Cpad;
+    hipError_t e = f16 ? launch_spec_f16(T, sp, (unsigned)gx, s) : launch_spec_f32(T, sp, (unsigned)gx, s);
+    if (e != hipSuccess) return EQL_EHIP;
+    Bwdw4Args a{};
+    a.dy = dy;
+    a.xh = ws;
+    a.wsR = partR;
+    a.wsP = partP;
+    a.N = (int)N;
+    a.Dp = (int)Dp;
+    a.Cp = (int)Cp;
+    a.Cpad = (int)p.Cpad;
+    a.kgCount = (int)p.kgCount;
+    a.kgPerSplit = (int)p.fKgPerSplit;
+    a.dTiles = (int)p.fDTiles;
+    a.cTiles = (int)p.fCTiles;
+    a.numItems = (int)fItems;
+    a.tw = tw;
+    e = launch_bwdw4(f16, T, a, (unsigned)fItems, s);
+    if (e != hipSuccess) return EQL_EHIP;
+  } else if (N > 0) {
     SpecArgs sp{};
     sp.N = (int)N;
     sp.kgCount = (int)p.kgCount;

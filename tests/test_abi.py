@@ -53,26 +53,44 @@ def test_packed_weight_bytes():
     assert eql.eqlinear_packed_weight_bytes(3, 3, 4, 7) == 0
 
 
+def bwdw_fused(N, Cp, Dp, T, elt):
+    """The weight gradient's path rule as documented in the header: the fused path for
+    T in {1, 2, 4}, 16-byte dy rows and fewer than 400 actual FLOPs per algorithmic byte."""
+    if N == 0 or T not in (1, 2, 4) or (Dp * T * elt) % 16 or N * Dp * T * elt >= 2**32:
+        return False
+    planes = {1: 1, 2: 2, 4: 6}[T]
+    return 2 * planes * N * Dp * Cp / (elt * T * N * (Cp + Dp)) < 400
+
+
 def test_workspace_bytes():
     assert eql.eqlinear_bwd_w_workspace_bytes(0, 4, 4, 4, eql.EQL_F16) == 0
-    # Layout: dy and x half spectra as 16-byte units (2G rows per k-step, G = 8 for
-    # fp16 and 4 for fp32; channels padded to the GEMM tile width, 256 unless that
-    # pads more than a third of the channels, else 64; each section 256-byte
-    # aligned), then fp32 partial spectra: whole [D'][C'] planes, at least one set
-    # of T planes and at most one set per k-step.
+    # Separate path: dy and x half spectra as 16-byte units (2G rows per k-step, G = 8
+    # for fp16 and 4 for fp32; channels padded to the GEMM tile width, 256 unless that
+    # pads more than a third of the channels, else 64; each section 256-byte aligned),
+    # then fp32 partial spectra: whole [D'][C'] planes, at least one set of T planes
+    # and at most one set per k-step.  Fused path: x's spectrum only, channels padded
+    # to a multiple of 128, then the partials.
     def padded(ch):
         w = 256 if -(-ch // 256) * 256 * 3 <= ch * 4 else 64
         return -(-ch // w) * w
 
+    paths = set()
     for (N, Cp, Dp, G, code) in ((65536, 1024, 1024, 8, eql.EQL_F16), (37, 5, 3, 4, eql.EQL_F32),
-                                 (100352, 192, 768, 8, eql.EQL_F16)):
+                                 (100352, 192, 768, 8, eql.EQL_F16), (1000, 96, 200, 8, eql.EQL_F16)):
         T = 4
+        elt = 16 // G
         n = eql.eqlinear_bwd_w_workspace_bytes(N, Cp, Dp, T, code)
         steps = -(-N // (2 * G))
-        spec = sum(-(-(steps * T * 2 * padded(K) * 16) // 256) * 256 for K in (Dp, Cp))
+        fused = bwdw_fused(N, Cp, Dp, T, elt)
+        paths.add(fused)
+        if fused:
+            spec = -(-(steps * T * 2 * (-(-Cp // 128) * 128) * 16) // 256) * 256
+        else:
+            spec = sum(-(-(steps * T * 2 * padded(K) * 16) // 256) * 256 for K in (Dp, Cp))
         part = n - spec
         plane = Dp * Cp * 4
         assert T * plane <= part <= steps * T * plane + 256
+    assert paths == {True, False}
     assert eql.eqlinear_bwd_w_workspace_bytes(10, 4, 4, 0, eql.EQL_F16) == 0
 
 

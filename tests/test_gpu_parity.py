@@ -721,3 +721,55 @@ def test_layer_autograd_matches_oracle():
     assert rel_err(host(y.detach()).reshape(N, -1), oracle.fwd(xn, w)) <= 1e-5
     assert rel_err(host(x.grad).reshape(N, -1), oracle.bwd_x(dyn, w)) <= 1e-5
     assert rel_err(host(layer.weight.grad), oracle.bwd_w(xn, dyn, T)) <= 1e-5
+
+
+# ------------------------------------------------- weight gradient: both paths
+_PATH_CHILD = r"""
+import json, sys
+sys.path.insert(0, sys.argv[1])
+import numpy as np, torch
+import group_circulant_linear_p4_amd as eql
+import oracle, workloads as W
+out = {}
+for (T, dtype, N, Cp, Dp) in json.loads(sys.argv[2]):
+    wl = W.Workload("t", "test", T, N, Cp, Dp, dtype, ("bwd_w",), seed=50 + T)
+    x, dy = W.make_x(wl), W.make_dy(wl)
+    code = eql.EQL_F16 if dtype == "f16" else eql.EQL_F32
+    xd, dyd = torch.from_numpy(x).cuda(), torch.from_numpy(dy).cuda()
+    nbytes = eql.eqlinear_bwd_w_workspace_bytes(N, Cp, Dp, T, code)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+    dw = torch.empty((Dp, Cp, T), dtype=xd.dtype, device="cuda")
+    print("case T=%d %s N=%d C'=%d D'=%d" % (T, dtype, N, Cp, Dp), flush=True)
+    eql.eqlinear_bwd_w(xd, dyd, dw, ws, nbytes, N, Cp, Dp, T, code)
+    torch.cuda.synchronize()
+    ref = oracle.bwd_w(x, dy, T)
+    got = dw.cpu().numpy().astype(np.float64)
+    out["%d/%s/%d/%d/%d" % (T, dtype, N, Cp, Dp)] = [float(np.linalg.norm(got - ref) / np.linalg.norm(ref)), nbytes]
+print("RESULT " + json.dumps(out), flush=True)
+"""
+
+# Shapes with 16-byte dy rows (the fused path's condition): ragged d and c tiles, partial
+# last k-steps, and enough rows for several row ranges.
+_PATH_CASES = [(4, "f16", 700, 300, 520), (4, "f16", 20000, 64, 64), (2, "f16", 1000, 70, 132),
+               (1, "f16", 333, 17, 40), (4, "f32", 257, 33, 41), (2, "f32", 129, 5, 130), (1, "f32", 1100, 200, 132)]
+
+
+@pytest.mark.parametrize("path", ["fused", "separate"])
+def test_bwd_w_both_paths(path):
+    """eqlinear_bwd_w through each of its two paths (the transform of dy inside the
+    GEMM, or both spectra first), selected with EQL_BWDW_PATH in a child process (the
+    library reads it once), against the oracle."""
+    import json
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, EQL_BWDW_PATH=path)
+    r = subprocess.run([sys.executable, "-c", _PATH_CHILD, root, json.dumps(_PATH_CASES)], env=env,
+                       capture_output=True, text=True, timeout=170)
+    print(r.stdout[-3000:], r.stderr[-3000:], flush=True)
+    assert r.returncode == 0
+    res = json.loads([l for l in r.stdout.splitlines() if l.startswith("RESULT ")][-1][7:])
+    assert len(res) == len(_PATH_CASES)
+    for key, (err, nbytes) in res.items():
+        assert err <= TOL[key.split("/")[1]], (key, err)
