@@ -173,6 +173,7 @@ struct BwdwPlan {
   // Fused path (dy transformed inside the GEMM, eql_bwdw4_kernel): one launch over
   // S x dTiles x cTiles items of 128 x 128 output channels, all planes.
   bool fused = false;
+  int fNB = 4;  // 32-channel blocks of c per tile
   int64_t fS = 0, fKgPerSplit = 0, fDTiles = 0, fCTiles = 0;
   size_t dyhBytes = 0, xhBytes = 0, partRBytes = 0, partPBytes = 0;
   size_t total() const { return dyhBytes + xhBytes + partRBytes + partPBytes; }
@@ -240,9 +241,20 @@ BwdwPlan plan_bwdw(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype) {
   p.kgCount = ceil_div(N, 2 * group_channels(dtype));
   if (bwdw_fused(N, Cp, Dp, T, dtype)) {
     p.fused = true;
+    // Column tile of 32 NB channels: the least padding of C', ties to the wider tile;
+    // the tile's spectrum stage (T NB KB) must split evenly over the four waves.
+    int64_t best = -1;
+    for (int nb = 4; nb >= 2; --nb) {
+      if ((T * nb) % 4 != 0) continue;
+      const int64_t padded = ceil_div(Cp, 32 * nb) * 32 * nb;
+      if (best < 0 || padded < best) {
+        best = padded;
+        p.fNB = nb;
+      }
+    }
     p.fDTiles = ceil_div(Dp, kBwdw4Tile);
-    p.fCTiles = ceil_div(Cp, kBwdw4Tile);
-    p.Cpad = p.fCTiles * kBwdw4Tile;
+    p.fCTiles = ceil_div(Cp, 32 * p.fNB);
+    p.Cpad = p.fCTiles * 32 * p.fNB;
     const int64_t tiles = p.fDTiles * p.fCTiles;
     int64_t S = std::max<int64_t>(1, kTargetWorkgroups / tiles);
     S = std::min<int64_t>(S, std::max<int64_t>(1, p.kgCount / kMinStepsPerSplit));
@@ -459,7 +471,7 @@ int eqlinear_bwd_w(const void* x, const void* dy, void* dw, void* workspace, siz
     a.cTiles = (int)p.fCTiles;
     a.numItems = (int)fItems;
     a.tw = tw;
-    e = launch_bwdw4(f16, T, a, (unsigned)fItems, s);
+    e = launch_bwdw4(f16, T, p.fNB, a, (unsigned)fItems, s);
     if (e != hipSuccess) return EQL_EHIP;
   } else if (N > 0) {
     SpecArgs sp{};

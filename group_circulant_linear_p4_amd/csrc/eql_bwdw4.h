@@ -12,12 +12,13 @@
 // dy is thus read once from memory and its spectrum is never written ("Implementacao":
 // fused data flow, no intermediate global writes).
 //
-// Work decomposition: an item is a 128 (d) x 128 (c) output tile for all T planes
-// and one range of k-steps (split-K over the rows); one workgroup of 4 waves per item,
-// wave w owning output channels d0 + 32w .. +31 and all four 32-channel blocks of c.
-// A k-step is 2G rows (G = 16 / sizeof(element)).  Per k-step the stage holds the
-// raw dy rows' 128-channel chunks (4T KB) and x's spectrum units of the tile's 128
-// channels (4T KB, [plane][half][channel]).  The ring, its 4-slot unrolled loop and
+// Work decomposition: an item is a 128 (d) x 32 NB (c) output tile for all T planes
+// (NB = 2, 3 or 4, the width that pads C' least) and one range of k-steps (split-K
+// over the rows); one workgroup of 4 waves per item, wave w owning output channels
+// d0 + 32w .. +31 and all NB 32-channel blocks of c.  A k-step is 2G rows
+// (G = 16 / sizeof(element)).  Per k-step the stage holds the raw dy rows' 128-channel
+// chunks (4T KB) and x's spectrum units of the tile's 32 NB channels (T NB KB,
+// [plane][half][channel]).  The ring, its 4-slot unrolled loop and
 // the DMA issue follow eql_fwd4_kernel.  Each item writes its fp32 partial spectrum;
 // eql_bwdw_reduce sums the items of a tile in a fixed order and applies the inverse.
 #pragma once
@@ -38,7 +39,7 @@ struct Bwdw4Args {
   Twiddles tw;
 };
 
-constexpr int kBwdw4Tile = 128;  // output channels per tile in d and in c
+constexpr int kBwdw4Tile = 128;  // output channels per tile in d
 
 // Ring depth: 5 slots (160 KB of LDS at T = 4) keep four stages in flight per CU; the
 // kernel is bound by load latency, not bandwidth, at the layer shapes it serves.  The
@@ -46,30 +47,31 @@ constexpr int kBwdw4Tile = 128;  // output channels per tile in d and in c
 template <int T, typename Elt>
 __host__ __device__ constexpr int bwdw4_slots() { return T == 4 ? (sizeof(Elt) == 2 ? 5 : 4) : 6; }
 
-template <int T, typename Elt>
+template <int T, typename Elt, int NB>
 __global__ void __launch_bounds__(256) eql_bwdw4_kernel(const Bwdw4Args a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using E = EltT<Elt>;
   constexpr int G = E::kPerUnit;           // rows per operand unit
   constexpr int NR = n_real_planes(T);
   constexpr int NP = n_pairs(T);
-  constexpr int NB = 4;                    // 32-channel blocks of c per wave
+  constexpr int CT = 32 * NB;              // input channels c per tile
   constexpr int ELT = (int)sizeof(Elt);
   constexpr int TB = T * ELT;              // bytes of one (row, channel) group
   constexpr int CHUNK = kBwdw4Tile * TB;   // bytes of one dy row's tile chunk
   constexpr int UPR = CHUNK / 16;          // 16-byte units per row chunk
   constexpr int ASLOT = 2 * G * CHUNK;     // raw dy bytes per stage (4T KB)
-  constexpr int BSLOT = T * 2 * kBwdw4Tile * 16;  // spectrum bytes per stage (4T KB)
+  constexpr int BSLOT = T * 2 * CT * 16;   // spectrum bytes per stage (T NB KB)
   constexpr int NS = bwdw4_slots<T, Elt>(), DIST = NS - 1;
   constexpr int U = NS % 2 ? 2 * NS : NS;   // loop unroll: slot and fragment buffer both fixed
   constexpr int SPLIT = NS / 2 + 1;         // slots SPLIT.. read from a second base register
   constexpr int IPA = ASLOT / 4096;        // dy DMA loads per wave per stage (T)
-  constexpr int IPB = BSLOT / 4096;        // spectrum DMA loads per wave per stage (T)
+  constexpr int IPB = BSLOT / 4096;        // spectrum DMA loads per wave per stage
   static_assert(T == 1 || T == 2 || T == 4, "fused weight gradient: T in {1, 2, 4}");
   static_assert(IPA == 1 || IPA == 2 || IPA == 4, "dy loads per wave");
+  static_assert(NB >= 2 && NB <= 4 && IPB * 4096 == BSLOT && IPB >= 1 && IPB <= 4, "spectrum loads per wave");
   static_assert(NS * (ASLOT + BSLOT) <= 160 * 1024, "LDS budget");
   static_assert((SPLIT - 1) * ASLOT + (G - 1) * CHUNK < 65536 && (NS - SPLIT - 1) * ASLOT + (G - 1) * CHUNK < 65536 &&
-                    (SPLIT - 1) * BSLOT + (T - 1) * 2 * kBwdw4Tile * 16 + (NB - 1) * 512 < 65536,
+                    (SPLIT - 1) * BSLOT + (2 * T - 1) * CT * 16 + (NB - 1) * 512 < 65536,
                 "ds_read immediate offsets");
   constexpr int WAIT_TOP = (DIST - 2) * (IPA + IPB);
   constexpr int WAIT_PRO = (DIST - 1) * (IPA + IPB);
@@ -85,7 +87,7 @@ __global__ void __launch_bounds__(256) eql_bwdw4_kernel(const Bwdw4Args a) {
   const int split = item / tiles;
   const int tile = item - split * tiles;
   const int dTile = tile / a.cTiles, cTile = tile - dTile * a.cTiles;
-  const int d0 = dTile * kBwdw4Tile, c0 = cTile * kBwdw4Tile;
+  const int d0 = dTile * kBwdw4Tile, c0 = cTile * CT;
   const int kgBegin = split * a.kgPerSplit;
   const int nst = max(0, min(a.kgCount, kgBegin + a.kgPerSplit) - kgBegin);
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -106,20 +108,21 @@ __global__ void __launch_bounds__(256) eql_bwdw4_kernel(const Bwdw4Args a) {
     const int dl = (u * 16) / TB;  // first channel of the unit within the tile
     aOff[i] = d0 + dl < a.Dp ? (uint32_t)r * rowBytes + (uint32_t)(d0 * TB + u * 16) : kOob;
   }
-  // Spectrum DMA: load q = wave IPB + i covers run q / 2 = (plane, half) of the stage,
-  // half q % 2 of its 128 units.
+  // Spectrum DMA: load i of the wave covers stage unit P = (wave IPB + i) 64 + lane,
+  // which is channel c0 + P % CT of run P / CT = (plane, half).
   uint32_t bOff[IPB];
 #pragma unroll
   for (int i = 0; i < IPB; ++i) {
-    const int q = wave * IPB + i;
-    bOff[i] = (uint32_t)(q >> 1) * (uint32_t)a.Cpad * 16u + (uint32_t)(c0 + (q & 1) * 64 + lane) * 16u;
+    const int P = (wave * IPB + i) * 64 + lane;
+    const int run = P / CT;
+    bOff[i] = (uint32_t)run * (uint32_t)a.Cpad * 16u + (uint32_t)(c0 + P - run * CT) * 16u;
   }
   // Fragment reads: dY of output channel d0 + 32 wave + lrow, rows khalf G .. +G-1 of
   // the stage; X units of channel c0 + 32 nb + lrow, half khalf, plane p.
   // Slots 0 .. SPLIT-1 are read at immediate offsets from aRd / bRd, the others from
   // aRd2 / bRd2 (ds_read offsets stop at 64 KB).
   const uint32_t aRd = lds_addr(&ringA[0][0]) + (uint32_t)(khalf * G * CHUNK + (wave * 32 + lrow) * TB);
-  const uint32_t bRd = lds_addr(&ringB[0][0]) + (uint32_t)((khalf * kBwdw4Tile + lrow) * 16);
+  const uint32_t bRd = lds_addr(&ringB[0][0]) + (uint32_t)((khalf * CT + lrow) * 16);
   const uint32_t aRd2 = aRd + (uint32_t)(SPLIT * ASLOT), bRd2 = bRd + (uint32_t)(SPLIT * BSLOT);
 
   // Issue side: the stage to load next; its dy rows start at aCur, its spectrum units
@@ -238,7 +241,7 @@ __global__ void __launch_bounds__(256) eql_bwdw4_kernel(const Bwdw4Args a) {
     using SI = std::integral_constant<int, (S + DIST) % NS>;
     u32x4 bf[2][T];
 #pragma unroll
-    for (int p = 0; p < T; ++p) bf[0][p] = rd16(bBase, SB0 + p * 2 * kBwdw4Tile * 16);
+    for (int p = 0; p < T; ++p) bf[0][p] = rd16(bBase, SB0 + p * 2 * CT * 16);
     wait_vmcnt<WAIT_TOP>();
     __builtin_amdgcn_s_barrier();
     issue(SI{});
@@ -247,7 +250,7 @@ __global__ void __launch_bounds__(256) eql_bwdw4_kernel(const Bwdw4Args a) {
     for (int nb = 0; nb < NB; ++nb) {
       if (nb + 1 < NB) {
 #pragma unroll
-        for (int p = 0; p < T; ++p) bf[(nb + 1) & 1][p] = rd16(bBase, SB0 + p * 2 * kBwdw4Tile * 16 + (nb + 1) * 512);
+        for (int p = 0; p < T; ++p) bf[(nb + 1) & 1][p] = rd16(bBase, SB0 + p * 2 * CT * 16 + (nb + 1) * 512);
       }
       const u32x4(&b)[T] = bf[nb & 1];
 #pragma unroll

@@ -227,12 +227,12 @@ __device__ __forceinline__ void dma16_run(const u32x4& desc, uint32_t voff, uint
   }
 }
 
-// N loads (1, 2 or 4) of 16 bytes per lane with lane offsets voff[i] into LDS at
+// N loads (1 to 4) of 16 bytes per lane with lane offsets voff[i] into LDS at
 // ldsBase + OFF + 1024 i + 16 lane: one M0 write per load, formed inside the statement.
 #define EQL_DMAX(k) EQL_M0(o##k) "buffer_load_dwordx4 %[v" #k "], %[desc], 0 offen lds\n\t"
 template <int N, int OFF>
 __device__ __forceinline__ void dma16_each(const u32x4& desc, const uint32_t (&voff)[N], uint32_t ldsBase) {
-  static_assert(N == 1 || N == 2 || N == 4, "batch size");
+  static_assert(N >= 1 && N <= 4, "batch size");
   const uint32_t l = (uint32_t)__builtin_amdgcn_readfirstlane(ldsBase);
   if constexpr (N == 1) {
     asm volatile("s_nop 4\n\t" EQL_DMAX(0)
@@ -241,6 +241,10 @@ __device__ __forceinline__ void dma16_each(const u32x4& desc, const uint32_t (&v
     asm volatile("s_nop 4\n\t" EQL_DMAX(0) EQL_DMAX(1)
                  : : [v0] "v"(voff[0]), [v1] "v"(voff[1]), [l] "s"(l), [o0] "i"(OFF), [o1] "i"(OFF + 1024),
                      [desc] "s"(desc) : "memory", "scc");
+  } else if constexpr (N == 3) {
+    asm volatile("s_nop 4\n\t" EQL_DMAX(0) EQL_DMAX(1) EQL_DMAX(2)
+                 : : [v0] "v"(voff[0]), [v1] "v"(voff[1]), [v2] "v"(voff[2]), [l] "s"(l),
+                     [o0] "i"(OFF), [o1] "i"(OFF + 1024), [o2] "i"(OFF + 2048), [desc] "s"(desc) : "memory", "scc");
   } else {
     asm volatile("s_nop 4\n\t" EQL_DMAX(0) EQL_DMAX(1) EQL_DMAX(2) EQL_DMAX(3)
                  : : [v0] "v"(voff[0]), [v1] "v"(voff[1]), [v2] "v"(voff[2]), [v3] "v"(voff[3]), [l] "s"(l),

@@ -193,27 +193,40 @@ int eqlinear_bwd_x(const void* dy, const void* w_packed_bwdx, void* dx, int64_t 
 
 /*
  * Scratch bytes eqlinear_bwd_w needs for this shape.  Depends only on the
- * arguments (0 when N == 0 or the arguments are invalid).  The workspace holds the
- * half spectra of dy and x (each about the size of that tensor: T real planes per
- * channel, rows padded to a multiple of 2 * 16 / sizeof(element), channels to a
- * multiple of the GEMM tile width: 256, or 64 where padding to 256 would add more
- * than a third of the channels) followed by fp32 partial spectra of the gradient: whole
- * Dp x Cp planes, one set per row range of the reduction over N (the real
- * frequencies and the complex pairs are split separately).
+ * arguments (0 when N == 0 or the arguments are invalid).  The layout follows the
+ * path the shape takes (see eqlinear_bwd_w).  Separate path: the half spectra of dy
+ * and x (each about the size of that tensor: T real planes per channel, rows padded
+ * to a multiple of 2 * 16 / sizeof(element), channels to a multiple of the GEMM tile
+ * width: 256, or 64 where padding to 256 would add more than a third of the
+ * channels).  Fused path: x's half spectrum only, channels padded to a column tile
+ * of 32 nb channels (nb in {4, 3, 2} with T nb a multiple of 4; the least padding,
+ * ties to the wider tile).  Both then hold fp32 partial spectra of the gradient:
+ * whole Dp x Cp planes, one set per row range of the reduction over N (on the
+ * separate path the real frequencies and the complex pairs are split separately).
  */
 size_t eqlinear_bwd_w_workspace_bytes(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype);
 
 /*
  * Weight gradient: dw[d][c][t] = sum_n sum_g dy[n][d*T+g] x[n][c*T+((g-t) mod T)],
- * the dense gradient dy^T x summed over the entries tied to w[d][c][t].  Launches:
- * the group transforms of dy and x (fp32, rounded once to `dtype`) into the
- * workspace; per frequency the channel GEMM dY_k^T conj(X_k) (K = N, fp32
- * accumulation, one partial per row range; one launch for the real frequencies and
- * one for the complex pairs); the sum of the partials in a fixed order
- * (deterministic), the inverse transform and the rounding to `dtype`.
- * x: [N][Cp*T], dy: [N][Dp*T] read; dw: [Dp][Cp][T] overwritten (zeros when
- * N == 0, which launches one small kernel); workspace: device memory of at least
- * eqlinear_bwd_w_workspace_bytes bytes, 16-byte aligned (contents on entry
+ * the dense gradient dy^T x summed over the entries tied to w[d][c][t]
+ * ("Resumo Tecnico: Flash EQ-Linear", "Implementacao": the gradient of the compressed weight is
+ * the per-frequency product of the output-gradient spectrum with the conjugate
+ * input spectrum).  Two paths compute the same sums:
+ *  - separate: the group transforms of dy and x (fp32, rounded once to `dtype`) into
+ *    the workspace, then per frequency the channel GEMM dY_k^T conj(X_k) (K = N,
+ *    fp32 accumulation; one launch for the real frequencies, one for the complex
+ *    pairs);
+ *  - fused (T in {1, 2, 4}, Dp T sizeof(element) a multiple of 16, and fewer than
+ *    400 real-product FLOPs per byte of x and dy, i.e. memory-bound shapes): only
+ *    x's transform goes to the workspace; the GEMM reads dy's raw rows and forms
+ *    their spectrum (rounded once to `dtype`, as on the separate path) as it goes.
+ *    The environment variable EQL_BWDW_PATH=fused|separate, read once per process,
+ *    overrides the choice among shapes the fused path accepts.
+ * Both write one fp32 partial per row range of N, then sum the partials in a fixed
+ * order (deterministic for a given shape and path), apply the inverse transform and
+ * round to `dtype`.  x: [N][Cp*T], dy: [N][Dp*T] read; dw: [Dp][Cp][T] overwritten
+ * (zeros when N == 0, which launches one small kernel); workspace: device memory of
+ * at least eqlinear_bwd_w_workspace_bytes bytes, 16-byte aligned (contents on entry
  * ignored, clobbered; EQL_EINVAL if ws_bytes is smaller).
  */
 int eqlinear_bwd_w(const void* x, const void* dy, void* dw, void* workspace, size_t ws_bytes,

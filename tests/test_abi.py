@@ -69,10 +69,15 @@ def test_workspace_bytes():
     # pads more than a third of the channels, else 64; each section 256-byte aligned),
     # then fp32 partial spectra: whole [D'][C'] planes, at least one set of T planes
     # and at most one set per k-step.  Fused path: x's spectrum only, channels padded
-    # to a multiple of 128, then the partials.
+    # to a multiple of a column tile of 32 nb channels (nb in 4, 3, 2 with T nb a
+    # multiple of 4, the least padding, ties to the wider), then the partials.
     def padded(ch):
         w = 256 if -(-ch // 256) * 256 * 3 <= ch * 4 else 64
         return -(-ch // w) * w
+
+    def fused_padded(ch, T):
+        widths = [32 * nb for nb in (4, 3, 2) if (T * nb) % 4 == 0]
+        return min((-(-ch // w) * w for w in widths))
 
     paths = set()
     for (N, Cp, Dp, G, code) in ((65536, 1024, 1024, 8, eql.EQL_F16), (37, 5, 3, 4, eql.EQL_F32),
@@ -84,7 +89,7 @@ def test_workspace_bytes():
         fused = bwdw_fused(N, Cp, Dp, T, elt)
         paths.add(fused)
         if fused:
-            spec = -(-(steps * T * 2 * (-(-Cp // 128) * 128) * 16) // 256) * 256
+            spec = -(-(steps * T * 2 * fused_padded(Cp, T) * 16) // 256) * 256
         else:
             spec = sum(-(-(steps * T * 2 * padded(K) * 16) // 256) * 256 for K in (Dp, Cp))
         part = n - spec
