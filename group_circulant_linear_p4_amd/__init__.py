@@ -24,6 +24,7 @@ __all__ = [
     "lib", "library_path", "eqlinear_abi_version", "eqlinear_status_string",
     "eqlinear_packed_weight_bytes", "eqlinear_pack_weight", "eqlinear_fwd", "eqlinear_fwd_fused", "eqlinear_bwd_x",
     "eqlinear_fused_epilogue_bwd_workspace_bytes", "eqlinear_fused_epilogue_bwd",
+    "eqlinear_fused_epilogue_bwd_noalloc", "EQL_NOALLOC_SCRATCH_BYTES",
     "eqlinear_bwd_w_workspace_bytes", "eqlinear_bwd_w",
 ]
 
@@ -31,7 +32,8 @@ EQL_F32, EQL_F16 = 0, 1
 EQL_PACK_FWD, EQL_PACK_BWDX = 0, 1
 EQL_ACT_NONE, EQL_ACT_GELU = 0, 1
 EQL_MAX_T = 16
-EQL_OK, EQL_EINVAL, EQL_EALIGN, EQL_EUNSUPPORTED, EQL_EHIP = 0, 1, 2, 3, 4
+EQL_OK, EQL_EINVAL, EQL_EALIGN, EQL_EUNSUPPORTED, EQL_EHIP, EQL_ESCRATCH = 0, 1, 2, 3, 4, 5
+EQL_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libeqlinear.so")
@@ -71,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.eqlinear_fused_epilogue_bwd_workspace_bytes.restype = sz
         L.eqlinear_fused_epilogue_bwd.argtypes = [vp, vp, vp, vp, vp, sz, i64, i64, i32, i32, i32, vp]
         L.eqlinear_fused_epilogue_bwd.restype = i32
+        L.eqlinear_fused_epilogue_bwd_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, vp]
+        L.eqlinear_fused_epilogue_bwd_noalloc.restype = i32
         L.eqlinear_bwd_x.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, vp]
         L.eqlinear_bwd_x.restype = i32
         L.eqlinear_bwd_w_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
@@ -160,6 +164,15 @@ def eqlinear_fused_epilogue_bwd(dy, pre, dpre, dbias, workspace, ws_bytes: int, 
     _check(lib().eqlinear_fused_epilogue_bwd(_ptr(dy), _ptr(pre), _ptr(dpre), _ptr(dbias), _ptr(workspace),
                                              int(ws_bytes), N, Dp, T, _dtype(dtype), int(act), _stream(stream)),
            "eqlinear_fused_epilogue_bwd")
+
+
+def eqlinear_fused_epilogue_bwd_noalloc(dy, pre, dpre, dbias, N: int, Dp: int, T: int, dtype, act: int,
+                                        stream=None) -> None:
+    """eqlinear_fused_epilogue_bwd with the library's static per-device scratch in place of a
+    workspace (no allocation; overlapping calls on one device race)."""
+    _check(lib().eqlinear_fused_epilogue_bwd_noalloc(_ptr(dy), _ptr(pre), _ptr(dpre), _ptr(dbias), N, Dp, T,
+                                                     _dtype(dtype), int(act), _stream(stream)),
+           "eqlinear_fused_epilogue_bwd_noalloc")
 
 
 def eqlinear_bwd_x(dy, w_packed_bwdx, dx, N: int, Cp: int, Dp: int, T: int, dtype, stream=None) -> None:

@@ -275,11 +275,108 @@ BwdwPlan plan_bwdw(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype) {
   return p;
 }
 
+// Launch shape of the epilogue backward: chunk width W (the widest power of two, up
+// to 16 bytes, dividing a row), 64 chunks across per workgroup, and rows per
+// workgroup halved from 1024 (down to 16) until the grid has 2048 workgroups (eight
+// per compute unit) or more.  The bias partials take one fp32 per row block and
+// element position.
+struct EpiPlan {
+  int W;
+  int64_t rowsPerBlock, rowBlocks, chunkBlocks;
+  size_t partBytes;
+};
+
+EpiPlan plan_epi(int64_t N, int64_t Dp, int T, int dtype) {
+  EpiPlan p{};
+  const int64_t rowBytes = Dp * T * elt_bytes(dtype);
+  p.W = pow2_part((int)(rowBytes % 16 == 0 ? 16 : rowBytes % 16));
+  p.chunkBlocks = ceil_div(rowBytes / p.W, 64);
+  p.rowsPerBlock = 1024;
+  while (p.rowsPerBlock > 16 && ceil_div(N, p.rowsPerBlock) * p.chunkBlocks < 2048) p.rowsPerBlock /= 2;
+  p.rowBlocks = ceil_div(N, p.rowsPerBlock);
+  p.partBytes = (size_t)p.rowBlocks * (size_t)(Dp * T) * sizeof(float);
+  return p;
+}
+
+// Scratch of eqlinear_fused_epilogue_bwd_noalloc: the bias gradient's row-block
+// column sums of one call.  Each device holds its own copy, at its own address,
+// until the process ends; host code uses the address hipGetSymbolAddress returns on
+// that device, never the array's name (a host-side stand-in).
+constexpr size_t kScratchBytes = EQL_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::atomic<float*> g_scratch[kMaxDevices];
+
+// `scratch` on the current device, looked up once per device with that device
+// current; null if the device or the lookup fails.
+float* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  float* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* addr = nullptr;
+  if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return nullptr;
+  // Every thread that races here gets the same address; any of them may store it.
+  g_scratch[dev].store(static_cast<float*>(addr), std::memory_order_release);
+  return static_cast<float*>(addr);
+}
+
+// Body of both epilogue-backward entry points.  noalloc: the partials go to the
+// current device's `scratch` instead of the caller's workspace (workspace and
+// ws_bytes are ignored).
+int epilogue_bwd(const void* dy, const void* pre, void* dpre, void* dbias, void* workspace, size_t ws_bytes,
+                 int64_t N, int64_t Dp, int T, int dtype, int act, void* stream, bool noalloc) {
+  if (act != EQL_ACT_NONE && act != EQL_ACT_GELU) return EQL_EINVAL;
+  int st = check_sizes(N, 1, Dp, T, dtype);
+  if (st != EQL_OK) return st;
+  const EpiPlan p = plan_epi(N, Dp, T, dtype);
+  if (p.rowBlocks * p.chunkBlocks > kMaxGrid) return EQL_EINVAL;
+  if (N > 0 && (!dy || !dpre || (act == EQL_ACT_GELU && !pre))) return EQL_EINVAL;
+  const bool parts = dbias && N > 0;
+  if (noalloc) {
+    if (parts && p.partBytes > kScratchBytes) return EQL_ESCRATCH;
+  } else if (parts && (!workspace || ws_bytes < p.partBytes)) {
+    return EQL_EINVAL;
+  }
+  if ((dy && !aligned16(dy)) || (pre && !aligned16(pre)) || (dpre && !aligned16(dpre)) ||
+      (workspace && !aligned16(workspace)) ||
+      (dbias && (reinterpret_cast<uintptr_t>(dbias) % (uintptr_t)elt_bytes(dtype)) != 0))
+    return EQL_EALIGN;
+  if (noalloc && parts) {
+    workspace = scratch_on_current_device();
+    if (!workspace) return EQL_EHIP;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool f16 = dtype == EQL_F16;
+  EpiBwdArgs a{};
+  a.dy = dy;
+  a.pre = pre;
+  a.dpre = dpre;
+  a.part = parts ? static_cast<float*>(workspace) : nullptr;
+  a.dbias = dbias;
+  a.N = (int)N;
+  a.Dp = (int)Dp;
+  a.T = T;
+  a.act = act;
+  a.rowElems = (int)(Dp * T);
+  a.rowsPerBlock = (int)p.rowsPerBlock;
+  a.chunkBlocks = (int)p.chunkBlocks;
+  a.rowBlocks = N > 0 ? (int)p.rowBlocks : 0;
+  if (N > 0) {
+    const hipError_t e = launch_epi_bwd(f16, p.W, a, (unsigned)(p.rowBlocks * p.chunkBlocks), s);
+    if (e != hipSuccess) return EQL_EHIP;
+  }
+  // dbias (zeros when N == 0: no partials to add).
+  if (dbias) return status_of(launch_epi_bias(f16, a, (unsigned)ceil_div(Dp, 16), s));
+  return EQL_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int eqlinear_abi_version(void) { return 200; }
+int eqlinear_abi_version(void) { return 201; }
 
 const char* eqlinear_status_string(int status) {
   switch (status) {
@@ -288,6 +385,7 @@ const char* eqlinear_status_string(int status) {
     case EQL_EALIGN: return "a base pointer is not 16-byte aligned";
     case EQL_EUNSUPPORTED: return "group order T above EQL_MAX_T";
     case EQL_EHIP: return "HIP launch failed";
+    case EQL_ESCRATCH: return "the shape needs more scratch than the no-allocation entry point holds";
     default: return "unknown status";
   }
 }
@@ -339,29 +437,6 @@ int eqlinear_fwd_fused(const void* x, const void* w_packed, const void* bias, co
   return run_fwd(x, w_packed, y, N, Cp, Dp, T, dtype, stream, true, bias, residual, act, pre_out);
 }
 
-// Launch shape of the epilogue backward: chunk width W (the widest power of two, up
-// to 16 bytes, dividing a row), 64 chunks across per workgroup, and rows per
-// workgroup halved from 1024 (down to 16) until the grid has 2048 workgroups (eight
-// per compute unit) or more.  The bias partials take one fp32 per row block and
-// element position.
-struct EpiPlan {
-  int W;
-  int64_t rowsPerBlock, rowBlocks, chunkBlocks;
-  size_t partBytes;
-};
-
-EpiPlan plan_epi(int64_t N, int64_t Dp, int T, int dtype) {
-  EpiPlan p{};
-  const int64_t rowBytes = Dp * T * elt_bytes(dtype);
-  p.W = pow2_part((int)(rowBytes % 16 == 0 ? 16 : rowBytes % 16));
-  p.chunkBlocks = ceil_div(rowBytes / p.W, 64);
-  p.rowsPerBlock = 1024;
-  while (p.rowsPerBlock > 16 && ceil_div(N, p.rowsPerBlock) * p.chunkBlocks < 2048) p.rowsPerBlock /= 2;
-  p.rowBlocks = ceil_div(N, p.rowsPerBlock);
-  p.partBytes = (size_t)p.rowBlocks * (size_t)(Dp * T) * sizeof(float);
-  return p;
-}
-
 size_t eqlinear_fused_epilogue_bwd_workspace_bytes(int64_t N, int64_t Dp, int T, int dtype) {
   if (check_sizes(N, 1, Dp, T, dtype) != EQL_OK || N == 0) return 0;
   return plan_epi(N, Dp, T, dtype).partBytes;
@@ -370,40 +445,12 @@ size_t eqlinear_fused_epilogue_bwd_workspace_bytes(int64_t N, int64_t Dp, int T,
 int eqlinear_fused_epilogue_bwd(const void* dy, const void* pre, void* dpre, void* dbias, void* workspace,
                                 size_t ws_bytes, int64_t N, int64_t Dp, int T, int dtype, int act,
                                 void* stream) {
-  if (act != EQL_ACT_NONE && act != EQL_ACT_GELU) return EQL_EINVAL;
-  int st = check_sizes(N, 1, Dp, T, dtype);
-  if (st != EQL_OK) return st;
-  const EpiPlan p = plan_epi(N, Dp, T, dtype);
-  if (p.rowBlocks * p.chunkBlocks > kMaxGrid) return EQL_EINVAL;
-  if (N > 0 && (!dy || !dpre || (act == EQL_ACT_GELU && !pre))) return EQL_EINVAL;
-  if (dbias && N > 0 && (!workspace || ws_bytes < p.partBytes)) return EQL_EINVAL;
-  if ((dy && !aligned16(dy)) || (pre && !aligned16(pre)) || (dpre && !aligned16(dpre)) ||
-      (workspace && !aligned16(workspace)) ||
-      (dbias && (reinterpret_cast<uintptr_t>(dbias) % (uintptr_t)elt_bytes(dtype)) != 0))
-    return EQL_EALIGN;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool f16 = dtype == EQL_F16;
-  EpiBwdArgs a{};
-  a.dy = dy;
-  a.pre = pre;
-  a.dpre = dpre;
-  a.part = dbias && N > 0 ? static_cast<float*>(workspace) : nullptr;
-  a.dbias = dbias;
-  a.N = (int)N;
-  a.Dp = (int)Dp;
-  a.T = T;
-  a.act = act;
-  a.rowElems = (int)(Dp * T);
-  a.rowsPerBlock = (int)p.rowsPerBlock;
-  a.chunkBlocks = (int)p.chunkBlocks;
-  a.rowBlocks = N > 0 ? (int)p.rowBlocks : 0;
-  if (N > 0) {
-    const hipError_t e = launch_epi_bwd(f16, p.W, a, (unsigned)(p.rowBlocks * p.chunkBlocks), s);
-    if (e != hipSuccess) return EQL_EHIP;
-  }
-  // dbias (zeros when N == 0: no partials to add).
-  if (dbias) return status_of(launch_epi_bias(f16, a, (unsigned)ceil_div(Dp, 16), s));
-  return EQL_OK;
+  return epilogue_bwd(dy, pre, dpre, dbias, workspace, ws_bytes, N, Dp, T, dtype, act, stream, false);
+}
+
+int eqlinear_fused_epilogue_bwd_noalloc(const void* dy, const void* pre, void* dpre, void* dbias, int64_t N,
+                                        int64_t Dp, int T, int dtype, int act, void* stream) {
+  return epilogue_bwd(dy, pre, dpre, dbias, nullptr, 0, N, Dp, T, dtype, act, stream, true);
 }
 
 int eqlinear_bwd_x(const void* dy, const void* w_packed_bwdx, void* dx, int64_t N, int64_t Cp,

@@ -22,7 +22,8 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Pointers are DEVICE pointers that the caller allocates and owns; the library
- *    allocates nothing and keeps no per-call state.  Every base pointer must be
+ *    allocates nothing and keeps no per-call state (one exception:
+ *    eqlinear_fused_epilogue_bwd_noalloc's static scratch, below).  Every base pointer must be
  *    16-byte aligned (EQL_EALIGN otherwise).  Inputs and outputs must not alias.
  *  - Arrays are dense, row-major, C-contiguous, in the element type `dtype`
  *    (EQL_F32: IEEE binary32, EQL_F16: IEEE binary16).  Products accumulate in
@@ -71,7 +72,9 @@ typedef enum {
                           /* workspace too small                                 */
     EQL_EALIGN = 2,       /* a base pointer is not 16-byte aligned               */
     EQL_EUNSUPPORTED = 3, /* T > EQL_MAX_T                                        */
-    EQL_EHIP = 4          /* the HIP runtime rejected a launch                    */
+    EQL_EHIP = 4,         /* the HIP runtime rejected a launch                    */
+    EQL_ESCRATCH = 5      /* the shape needs more than EQL_NOALLOC_SCRATCH_BYTES   */
+                          /* (eqlinear_fused_epilogue_bwd_noalloc only)           */
 } eql_status;
 
 /*
@@ -183,6 +186,27 @@ int eqlinear_fused_epilogue_bwd(const void* dy, const void* pre, void* dpre, voi
                                 int dtype, int act, void* stream);
 
 /*
+ * eqlinear_fused_epilogue_bwd without a workspace, for callers that cannot allocate
+ * device memory around the call: code under HIP graph capture, tight serving or
+ * training loops, harnesses that forbid hipMalloc.  Same arguments, results and
+ * errors as eqlinear_fused_epilogue_bwd (bit-identical outputs), minus workspace
+ * and ws_bytes.  The bias gradient's row-block partials go to a static device array
+ * of EQL_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs on
+ * until the process ends (its address is looked up on a device's first call, with
+ * that device current).  Nothing is allocated per call, and nothing needs clearing:
+ * every partial is written before it is read.  EQL_ESCRATCH (before anything is
+ * launched) when dbias is given and the partials would not fit:
+ * eqlinear_fused_epilogue_bwd_workspace_bytes(N, Dp, T, dtype) above
+ * EQL_NOALLOC_SCRATCH_BYTES (about N <= 2^20 rows at Dp * T = 4096); without
+ * dbias the scratch is not used and any size is accepted.  Calls that overlap on
+ * one device (on different streams, or from different threads without ordering)
+ * share that scratch and race: the caller must order them.
+ */
+#define EQL_NOALLOC_SCRATCH_BYTES (16u << 20)
+int eqlinear_fused_epilogue_bwd_noalloc(const void* dy, const void* pre, void* dpre, void* dbias, int64_t N,
+                                        int64_t Dp, int T, int dtype, int act, void* stream);
+
+/*
  * Input gradient: dx = dy W.  dy: [N][Dp*T] read; w_packed_bwdx: the
  * EQL_PACK_BWDX packing of the same w; dx: [N][Cp*T] overwritten.  This is the
  * forward algorithm applied to the transposed, group-reversed weight (the pages'
@@ -236,7 +260,8 @@ int eqlinear_bwd_w(const void* x, const void* dy, void* dw, void* workspace, siz
 const char* eqlinear_status_string(int status);
 
 /* ABI version of this header (major * 100 + minor).  2.00: the blocked packed-weight
- * layout above (1.xx stored ((o * Jin + i / G) * T + p) * G + i % G). */
+ * layout above (1.xx stored ((o * Jin + i / G) * T + p) * G + i % G).  2.01:
+ * eqlinear_fused_epilogue_bwd_noalloc and EQL_ESCRATCH. */
 int eqlinear_abi_version(void);
 
 #ifdef __cplusplus

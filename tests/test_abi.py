@@ -26,14 +26,14 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_function():
     L = eql.lib()
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(L, n), "missing export %s" % n
         assert hasattr(eql, n), "binding lacks %s" % n
 
 
 def test_version_and_status_strings():
-    assert eql.eqlinear_abi_version() == 200
+    assert eql.eqlinear_abi_version() == 201
     for s in range(5):
         assert eql.eqlinear_status_string(s)
     assert eql.eqlinear_status_string(99) == "unknown status"
@@ -167,6 +167,33 @@ def test_fused_epilogue_bwd_validation():
     assert raw(fn, MIS, pre, dpre, db, ws, need, 300, 5, 4, F16, GELU, None) == eql.EQL_EALIGN
     assert raw(fn, dy, pre, dpre, A16 + 2, ws, need, 300, 5, 4, F32, NONE, None) == eql.EQL_EALIGN
     assert raw(fn, dy, pre, dpre, db, ws, need, 300, 0, 4, F16, GELU, None) == eql.EQL_EINVAL   # D' < 1
+
+
+def test_fused_epilogue_bwd_noalloc_validation():
+    """The no-allocation variant validates like eqlinear_fused_epilogue_bwd, and refuses a
+    shape whose bias partials exceed its static scratch before anything is launched."""
+    F16, F32 = eql.EQL_F16, eql.EQL_F32
+    GELU, NONE = eql.EQL_ACT_GELU, eql.EQL_ACT_NONE
+    fn = "eqlinear_fused_epilogue_bwd_noalloc"
+    dy, pre, dpre, db = A16, A16B, A16 + 0x1000, A16 + 0x2000
+    cap = eql.EQL_NOALLOC_SCRATCH_BYTES
+    assert cap == 16 << 20
+    assert raw(fn, dy, pre, dpre, db, 300, 5, 4, F16, 3, None) == eql.EQL_EINVAL      # act
+    assert raw(fn, dy, None, dpre, db, 300, 5, 4, F16, GELU, None) == eql.EQL_EINVAL  # pre needed
+    assert raw(fn, None, pre, dpre, db, 300, 5, 4, F16, GELU, None) == eql.EQL_EINVAL
+    assert raw(fn, dy, pre, None, db, 300, 5, 4, F16, GELU, None) == eql.EQL_EINVAL
+    assert raw(fn, dy, pre, dpre, db, 300, 5, 17, F16, GELU, None) == eql.EQL_EUNSUPPORTED
+    assert raw(fn, MIS, pre, dpre, db, 300, 5, 4, F16, GELU, None) == eql.EQL_EALIGN
+    assert raw(fn, dy, pre, dpre, A16 + 2, 300, 5, 4, F32, NONE, None) == eql.EQL_EALIGN
+    assert raw(fn, dy, pre, dpre, db, 300, 0, 4, F16, GELU, None) == eql.EQL_EINVAL   # D' < 1
+    assert raw(fn, None, None, None, None, 0, 4, 4, F16, NONE, None) == eql.EQL_OK    # N = 0, no dbias
+    # 2^21 rows of D'T = 4096 fp16 elements: 2048 row blocks of 1024 rows, 32 MiB of fp32
+    # partials; 2^20 rows need exactly the scratch.
+    assert eql.eqlinear_fused_epilogue_bwd_workspace_bytes(1 << 21, 1024, 4, F16) == 2 * cap
+    assert eql.eqlinear_fused_epilogue_bwd_workspace_bytes(1 << 20, 1024, 4, F16) == cap
+    assert raw(fn, dy, pre, dpre, db, 1 << 21, 1024, 4, F16, GELU, None) == eql.EQL_ESCRATCH
+    assert raw(fn, dy, pre, dpre, db, (1 << 20) + 1024, 1024, 4, F16, NONE, None) == eql.EQL_ESCRATCH
+    assert "scratch" in eql.eqlinear_status_string(eql.EQL_ESCRATCH)
 
 
 def test_pack_validation():
