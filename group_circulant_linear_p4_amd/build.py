@@ -76,6 +76,9 @@ def build_library(jobs: int | None = None, extra_flags: list[str] | None = None,
     os.makedirs(BUILD, exist_ok=True)
     extra = list(extra_flags or [])
     jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 2)))
+    unknown = sorted(set(only or ()) - set(SOURCES))
+    if unknown:
+        raise ValueError("not library sources: %s (sources: %s)" % (", ".join(unknown), ", ".join(SOURCES)))
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, extra, reuse=only is not None and s not in only), SOURCES))
     tmp = LIB + ".tmp"

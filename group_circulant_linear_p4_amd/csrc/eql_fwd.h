@@ -633,6 +633,10 @@ __global__ void __launch_bounds__(64 * fwd4_waves(T, NB)) eql_fwd4_kernel(const 
   constexpr int SB = 2 * G * T * ELT;                  // bytes of one x row per stage
   static_assert(T <= 4 && LOAD != kLoadNarrow && NBW >= 1, "fast path: T <= 4, 16-byte rows");
   static_assert(BKB < WAVES || BKB % WAVES == 0, "whole 1 KB weight loads per wave");
+  // A wave's run of IPW KB starts at KB qw % T of a block's T KB chunk and must end
+  // inside it: the packed weight is block-major, so the next KB belongs to another
+  // stage (and past the last block, to no buffer at all).
+  static_assert(BKB < WAVES || (IPW <= T && T % IPW == 0), "weight run inside one block's chunk");
   static_assert(IPW <= 4 || IPW == 6 || IPW == 8, "weight run length");
   static_assert(IPWX == 2 || IPWX == 4, "x loads per wave");
   static_assert(NS * (BSLOT + XSLOT) <= 160 * 1024, "LDS budget");
