@@ -53,8 +53,9 @@ int check_sizes(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype) {
   if (!dtype_ok(dtype) || T < 1) return EQL_EINVAL;
   if (T > EQL_MAX_T) return EQL_EUNSUPPORTED;
   if (N < 0 || Cp < 1 || Dp < 1) return EQL_EINVAL;
-  if (N > kMaxN || Cp * T * elt_bytes(dtype) > kMaxRowBytes || Dp * T * elt_bytes(dtype) > kMaxRowBytes)
-    return EQL_EINVAL;
+  // Row widths compared by division first: Cp or Dp near INT64_MAX must not overflow.
+  const int64_t maxCh = kMaxRowBytes / (T * elt_bytes(dtype));
+  if (N > kMaxN || Cp > maxCh || Dp > maxCh) return EQL_EINVAL;
   return EQL_OK;
 }
 
