@@ -36,7 +36,9 @@ EQL_OK, EQL_EINVAL, EQL_EALIGN, EQL_EUNSUPPORTED, EQL_EHIP, EQL_ESCRATCH = 0, 1,
 EQL_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_PKG, "libeqlinear.so")
+# EQL_LIBRARY names another build of the same library (for instance the NaN-poisoned
+# debug build, libeqlinear_poison.so); by default the in-tree libeqlinear.so.
+_LIB_PATH = os.environ.get("EQL_LIBRARY") or os.path.join(_PKG, "libeqlinear.so")
 _lib = None
 
 

@@ -124,6 +124,28 @@ struct BufDesc {
   u32x4 w;
 };
 
+// Debug builds (EQL_POISON_RING): before a DMA load fills a 1 KB LDS chunk, the
+// issuing wave sets the chunk to all-ones bits (NaN in fp16 and fp32) and waits for
+// that store.  A fragment read that runs ahead of its load, or a load that leaves its
+// chunk unwritten (out-of-range lanes must write zeros), then shows up as NaN in the
+// outputs instead of as plausible stale data.  Only the issuing wave touches the
+// chunk, which the ring protocol has already freed, so the stores race with nothing.
+#if defined(EQL_POISON_RING)
+__device__ __forceinline__ void poison_chunk(uint32_t chunk) {
+  __attribute__((address_space(3))) char* p = (__attribute__((address_space(3))) char*)(uintptr_t)chunk;
+  *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(p + 16 * lane_index()) = (u32x4){~0u, ~0u, ~0u, ~0u};
+}
+#define EQL_POISON_CHUNKS(N, base, stride)                                    \
+  do {                                                                        \
+    _Pragma("unroll") for (int i_ = 0; i_ < (N); ++i_) poison_chunk((base) + (uint32_t)i_ * (stride)); \
+    wait_lgkm0();                                                             \
+  } while (0)
+#else
+#define EQL_POISON_CHUNKS(N, base, stride) \
+  do {                                      \
+  } while (0)
+#endif
+
 // 16 bytes per lane from buffer offset `voff` straight into LDS at
 // lds_base + 16 * lane (no VGPR destination).  Written as an asm statement so that
 // the compiler does not add a wait for all LDS-bound loads before every later LDS
@@ -136,6 +158,7 @@ struct BufDesc {
 //     SGPRs even where the compiler cannot prove uniformity.  M0 is reserved by
 //     the compiler (never allocated to other values), so it needs no clobber.
 __device__ __forceinline__ void dma16(const BufDesc& d, uint32_t voff, uint32_t lds_base) {
+  EQL_POISON_CHUNKS(1, (uint32_t)__builtin_amdgcn_readfirstlane(lds_base), 1024u);
   const u32x4 w = {(uint32_t)__builtin_amdgcn_readfirstlane(d.w[0]), (uint32_t)__builtin_amdgcn_readfirstlane(d.w[1]),
                    (uint32_t)__builtin_amdgcn_readfirstlane(d.w[2]), (uint32_t)__builtin_amdgcn_readfirstlane(d.w[3])};
   asm volatile("s_nop 4\n\ts_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
@@ -158,6 +181,11 @@ __device__ __forceinline__ void dma16_batch(const BufDesc& d, const uint32_t (&v
   uint32_t l[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) l[i] = (uint32_t)__builtin_amdgcn_readfirstlane(lds[i]);
+#if defined(EQL_POISON_RING)
+#pragma unroll
+  for (int i = 0; i < N; ++i) poison_chunk(l[i]);
+  wait_lgkm0();
+#endif
   if constexpr (N == 1) {
     asm volatile("s_nop 4\n\t" EQL_DMA_ONE(0, 1) : : "v"(voff[0]), "s"(l[0]), [desc] "s"(w) : "memory");
   } else if constexpr (N == 2) {
@@ -197,6 +225,7 @@ template <int N, int OFF>
 __device__ __forceinline__ void dma16_run(const u32x4& desc, uint32_t voff, uint32_t ldsBase) {
   static_assert(N >= 1 && N <= 8 && N != 5 && N != 7, "run length");
   const uint32_t l = (uint32_t)__builtin_amdgcn_readfirstlane(ldsBase);
+  EQL_POISON_CHUNKS(N, l + (uint32_t)OFF, 1024u);
   if constexpr (N == 1) {
     asm volatile("s_nop 4\n\t" EQL_M0(o) EQL_DMAO(v, 0)
                  : : [v] "v"(voff), [l] "s"(l), [o] "i"(OFF), [desc] "s"(desc) : "memory", "scc");
@@ -234,6 +263,7 @@ template <int N, int OFF>
 __device__ __forceinline__ void dma16_each(const u32x4& desc, const uint32_t (&voff)[N], uint32_t ldsBase) {
   static_assert(N >= 1 && N <= 4, "batch size");
   const uint32_t l = (uint32_t)__builtin_amdgcn_readfirstlane(ldsBase);
+  EQL_POISON_CHUNKS(N, l + (uint32_t)OFF, 1024u);
   if constexpr (N == 1) {
     asm volatile("s_nop 4\n\t" EQL_DMAX(0)
                  : : [v0] "v"(voff[0]), [l] "s"(l), [o0] "i"(OFF), [desc] "s"(desc) : "memory", "scc");
