@@ -207,17 +207,6 @@ bool bwdw_fused(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype) {
   return flops / bytes < kFusedIntensity;
 }
 
-// The fused path's complex pair with three real products instead of four (p4 fp16,
-// column tiles of at most 96 channels).  Off unless EQL_BWDW_3M=1 (read once): it was
-// measured, not adopted (see the kernel).
-bool bwdw_three_products(int T, int dtype, int nb) {
-  static const bool on = [] {
-    const char* v = std::getenv("EQL_BWDW_3M");
-    return v && std::strcmp(v, "1") == 0;
-  }();
-  return on && T == 4 && dtype == EQL_F16 && nb <= 3;
-}
-
 constexpr int64_t kMinStepsPerSplit = 16;  // keeps partial-spectrum traffic small
 
 // Row ranges (k-step ranges) of one GEMM launch: enough to give every compute unit
@@ -530,7 +519,7 @@ int eqlinear_bwd_w(const void* x, const void* dy, void* dw, void* workspace, siz
     a.cTiles = (int)p.fCTiles;
     a.numItems = (int)fItems;
     a.tw = tw;
-    e = launch_bwdw4(f16, T, p.fNB, bwdw_three_products(T, dtype, p.fNB), a, (unsigned)fItems, s);
+    e = launch_bwdw4(f16, T, p.fNB, a, (unsigned)fItems, s);
     if (e != hipSuccess) return EQL_EHIP;
   } else if (N > 0) {
     SpecArgs sp{};

@@ -47,24 +47,7 @@ constexpr int kBwdw4Tile = 128;  // output channels per tile in d
 template <int T, typename Elt>
 __host__ __device__ constexpr int bwdw4_slots() { return T == 4 ? (sizeof(Elt) == 2 ? 5 : 4) : 6; }
 
-// Sum and difference of two units of 8 fp16 values (v_pk_add_f16: one rounding each).
-// Whole-vector casts: __builtin_bit_cast of one element of an ext_vector_type value
-// reads element 0 whatever the index (a compiler defect seen with ROCm 7.2's clang).
-__device__ __forceinline__ u32x4 add_units_f16(const u32x4& a, const u32x4& b) {
-  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-  return __builtin_bit_cast(u32x4, __builtin_bit_cast(h8, a) + __builtin_bit_cast(h8, b));
-}
-__device__ __forceinline__ u32x4 sub_units_f16(const u32x4& a, const u32x4& b) {
-  typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-  return __builtin_bit_cast(u32x4, __builtin_bit_cast(h8, a) - __builtin_bit_cast(h8, b));
-}
-
-// G3 (p4 fp16 only, an option measured against the default): the complex pair's
-// product dY conj(X) with three real products instead of four (Gauss's method):
-// K1 = Xr (dYr + dYi), K2 = -dYr (Xr + Xi), K3 = dYi (Xr - Xi), then Re = K1 - K3 and
-// Im = K1 + K2 in fp32 when the partials are written.  The sums are rounded to fp16
-// once more than the plain operands (dYr + dYi from the rounded dYr and dYi).
-template <int T, typename Elt, int NB, bool G3 = false>
+template <int T, typename Elt, int NB>
 __global__ void __launch_bounds__(256) eql_bwdw4_kernel(const Bwdw4Args a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using E = EltT<Elt>;
@@ -84,8 +67,6 @@ __global__ void __launch_bounds__(256) eql_bwdw4_kernel(const Bwdw4Args a) {
   constexpr int IPA = ASLOT / 4096;        // dy DMA loads per wave per stage (T)
   constexpr int IPB = BSLOT / 4096;        // spectrum DMA loads per wave per stage
   static_assert(T == 1 || T == 2 || T == 4, "fused weight gradient: T in {1, 2, 4}");
-  static_assert(!G3 || (T == 4 && ELT == 2 && NB <= 3), "three-product form: p4 fp16, at most 3 blocks");
-  constexpr int NACC = G3 ? T + 1 : T;     // accumulator planes (K1, K2, K3 for the pair)
   static_assert(IPA == 1 || IPA == 2 || IPA == 4, "dy loads per wave");
   static_assert(NB >= 2 && NB <= 4 && IPB * 4096 == BSLOT && IPB >= 1 && IPB <= 4, "spectrum loads per wave");
   static_assert(NS * (ASLOT + BSLOT) <= 160 * 1024, "LDS budget");
@@ -213,15 +194,9 @@ __global__ void __launch_bounds__(256) eql_bwdw4_kernel(const Bwdw4Args a) {
       dft_p4_f16(raw, o);  // the G rows play the role of the forward's G channels
       af[ab][0] = o[0];
       af[ab][1] = o[1];
-      if constexpr (G3) {
-        af[ab][2] = add_units_f16(o[2], o[3]);     // dYr + dYi
-        af[ab][3] = neg_unit(o[2], E::kSignMask);  // -dYr
-        af[ab][4] = o[3];                          // dYi
-      } else {
-        af[ab][2] = o[2];
-        af[ab][3] = o[3];
-        af[ab][4] = neg_unit(o[2], E::kSignMask);
-      }
+      af[ab][2] = o[2];
+      af[ab][3] = o[3];
+      af[ab][4] = neg_unit(o[2], E::kSignMask);
     } else {
       float pl[T][G];
 #pragma unroll
@@ -244,9 +219,9 @@ __global__ void __launch_bounds__(256) eql_bwdw4_kernel(const Bwdw4Args a) {
     }
   };
 
-  f32x16 acc[NACC][NB];
+  f32x16 acc[T][NB];
 #pragma unroll
-  for (int p = 0; p < NACC; ++p)
+  for (int p = 0; p < T; ++p)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) E::zero(acc[p][nb]);
 
@@ -280,19 +255,13 @@ __global__ void __launch_bounds__(256) eql_bwdw4_kernel(const Bwdw4Args a) {
       const u32x4(&b)[T] = bf[nb & 1];
 #pragma unroll
       for (int p = 0; p < NR; ++p) E::mfma(acc[p][nb], af[cur][p], b[p]);
-      if constexpr (G3) {
-        E::mfma(acc[2][nb], af[cur][2], b[2]);                       // K1 = (dYr + dYi) Xr
-        E::mfma(acc[3][nb], af[cur][3], add_units_f16(b[2], b[3]));  // K2 = -dYr (Xr + Xi)
-        E::mfma(acc[4][nb], af[cur][4], sub_units_f16(b[2], b[3]));  // K3 = dYi (Xr - Xi)
-      } else {
 #pragma unroll
-        for (int q = 0; q < NP; ++q) {
-          const int re = NR + 2 * q, im = re + 1;
-          E::mfma(acc[re][nb], af[cur][re], b[re]);      // Re += dYr Xr
-          E::mfma(acc[re][nb], af[cur][im], b[im]);      //    + dYi Xi
-          E::mfma(acc[im][nb], af[cur][im], b[re]);      // Im += dYi Xr
-          E::mfma(acc[im][nb], af[cur][T + q], b[im]);   //    - dYr Xi
-        }
+      for (int q = 0; q < NP; ++q) {
+        const int re = NR + 2 * q, im = re + 1;
+        E::mfma(acc[re][nb], af[cur][re], b[re]);      // Re += dYr Xr
+        E::mfma(acc[re][nb], af[cur][im], b[im]);      //    + dYi Xi
+        E::mfma(acc[im][nb], af[cur][im], b[re]);      // Im += dYi Xr
+        E::mfma(acc[im][nb], af[cur][T + q], b[im]);   //    - dYr Xi
       }
       if (nb == 0) transform(Nxt{});
     }
@@ -332,12 +301,7 @@ __global__ void __launch_bounds__(256) eql_bwdw4_kernel(const Bwdw4Args a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int d = d0 + 32 * wave + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        float v = acc[p][nb][r];
-        if constexpr (G3) {
-          if (p == 2) v = acc[2][nb][r] - acc[4][nb][r];  // Re = K1 - K3
-          if (p == 3) v = acc[2][nb][r] + acc[3][nb][r];  // Im = K1 + K2
-        }
-        if (d < a.Dp && c < a.Cp) out[(size_t)d * a.Cp + c] = v;
+        if (d < a.Dp && c < a.Cp) out[(size_t)d * a.Cp + c] = acc[p][nb][r];
       }
     }
   }

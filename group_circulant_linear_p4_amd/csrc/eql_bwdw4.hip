@@ -1,5 +1,5 @@
 // Fused weight-gradient kernel instantiations: T in {1, 2, 4}, column tiles of 64, 96
-// and 128 channels, fp16 and fp32; the three-product option (p4 fp16, 64 and 96).
+// and 128 channels, fp16 and fp32.
 #include "eql_bwdw4.h"
 #include "eql_launch.h"
 
@@ -20,13 +20,7 @@ static hipError_t bwdw4_one(int T, int NB, const Bwdw4Args& a, unsigned grid, hi
   }
 }
 
-hipError_t launch_bwdw4(bool f16, int T, int NB, bool g3, const Bwdw4Args& a, unsigned grid, hipStream_t s) {
-  if (g3) {
-    if (!f16 || T != 4) return hipErrorInvalidValue;
-    if (NB == 2) return launch_kernel((const void*)&eql_bwdw4_kernel<4, _Float16, 2, true>, grid, a, s);
-    if (NB == 3) return launch_kernel((const void*)&eql_bwdw4_kernel<4, _Float16, 3, true>, grid, a, s);
-    return hipErrorInvalidValue;
-  }
+hipError_t launch_bwdw4(bool f16, int T, int NB, const Bwdw4Args& a, unsigned grid, hipStream_t s) {
   return f16 ? bwdw4_one<_Float16>(T, NB, a, grid, s) : bwdw4_one<float>(T, NB, a, grid, s);
 }
 

@@ -37,7 +37,7 @@ hipError_t launch_bwdw_real_f32(int T, int DB, int CB, const BwdwArgs& a, unsign
 hipError_t launch_bwdw_pair_f16(int T, int DB, int CB, const BwdwArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_bwdw_pair_f32(int T, int DB, int CB, const BwdwArgs& a, unsigned grid, hipStream_t s);
 // Weight gradient with dy's transform fused into the GEMM (T in {1, 2, 4}).
-hipError_t launch_bwdw4(bool f16, int T, int NB, bool g3, const Bwdw4Args& a, unsigned grid, hipStream_t s);
+hipError_t launch_bwdw4(bool f16, int T, int NB, const Bwdw4Args& a, unsigned grid, hipStream_t s);
 hipError_t launch_bwdw_reduce_f16(int T, int waves, const BwdwReduceArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_bwdw_reduce_f32(int T, int waves, const BwdwReduceArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_pack_f16(int T, const PackArgs& a, unsigned grid, hipStream_t s);
