@@ -197,8 +197,11 @@ def main():
     # gradient, one launch each: every workload here fits one launch's tile range),
     # the weight gradient is four launches (two transforms, the GEMM, the reduce).
     fwd_kernel_ms = per["fwd"] + per["bwd_x"]
+    # T <= 4 with 16-byte rows runs the ring kernel eql_fwd4_kernel, other shapes eql_fwd_kernel.
+    fwd_name = "eql_fwd4_kernel" if T <= 4 and (Cp * T * elt) % 16 == 0 and (Dp * T * elt) % 16 == 0 \
+        else "eql_fwd_kernel"
     if fwd_kernel_ms >= per["bwd_w"]:
-        dom, kname, t_dom = "fwd", "eql_fwd_kernel", 0.5 * fwd_kernel_ms * 1e-3
+        dom, kname, t_dom = "fwd", fwd_name, 0.5 * fwd_kernel_ms * 1e-3
     else:
         dom, kname, t_dom = "bwd_w", "eqlinear_bwd_w", per["bwd_w"] * 1e-3
     flop_bound = actual / MFMA_PEAK[wl.dtype] / 1e12 >= bytes_pass[dom] / HBM_PEAK / 1e9
