@@ -2,6 +2,7 @@
 
 Only the test suite, the smoke check and the benchmark's CPU-baseline leg use this
 package. The product path (the HIP library and its binding) never imports it.
+The p4m (dihedral D4) layer's oracle is the submodule `oracle.p4m_oracle`.
 """
 from .eqlinear_oracle import (  # noqa: F401
     unroll,
