@@ -26,6 +26,7 @@ __all__ = [
     "eqlinear_fused_epilogue_bwd_workspace_bytes", "eqlinear_fused_epilogue_bwd",
     "eqlinear_fused_epilogue_bwd_noalloc", "EQL_NOALLOC_SCRATCH_BYTES",
     "eqlinear_bwd_w_workspace_bytes", "eqlinear_bwd_w",
+    "eqlinear_p4m_expand_weight", "eqlinear_p4m_fold_weight_grad",
 ]
 
 EQL_F32, EQL_F16 = 0, 1
@@ -77,6 +78,9 @@ def lib() -> ctypes.CDLL:
         L.eqlinear_fused_epilogue_bwd.restype = i32
         L.eqlinear_fused_epilogue_bwd_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, vp]
         L.eqlinear_fused_epilogue_bwd_noalloc.restype = i32
+        for name in ("eqlinear_p4m_expand_weight", "eqlinear_p4m_fold_weight_grad"):
+            getattr(L, name).argtypes = [vp, vp, i64, i64, i32, vp]
+            getattr(L, name).restype = i32
         L.eqlinear_bwd_x.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, vp]
         L.eqlinear_bwd_x.restype = i32
         L.eqlinear_bwd_w_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
@@ -190,3 +194,15 @@ def eqlinear_bwd_w(x, dy, dw, workspace, ws_bytes: int, N: int, Cp: int, Dp: int
                    stream=None) -> None:
     _check(lib().eqlinear_bwd_w(_ptr(x), _ptr(dy), _ptr(dw), _ptr(workspace), ws_bytes, N, Cp, Dp, T,
                                 _dtype(dtype), _stream(stream)), "eqlinear_bwd_w")
+
+
+def eqlinear_p4m_expand_weight(w, w_c4, Dp: int, Cp: int, dtype, stream=None) -> None:
+    """p4m parameters w [Dp][Cp][8] -> the tied C_4 weight [2Dp][2Cp][4]."""
+    _check(lib().eqlinear_p4m_expand_weight(_ptr(w), _ptr(w_c4), Dp, Cp, _dtype(dtype), _stream(stream)),
+           "eqlinear_p4m_expand_weight")
+
+
+def eqlinear_p4m_fold_weight_grad(dw_c4, dw, Dp: int, Cp: int, dtype, stream=None) -> None:
+    """C_4 weight gradient [2Dp][2Cp][4] -> the p4m weight gradient [Dp][Cp][8]."""
+    _check(lib().eqlinear_p4m_fold_weight_grad(_ptr(dw_c4), _ptr(dw), Dp, Cp, _dtype(dtype), _stream(stream)),
+           "eqlinear_p4m_fold_weight_grad")

@@ -39,6 +39,7 @@ SOURCES = [
     "eql_bwdw_pair_f32.hip",
     "eql_bwdw4.hip",
     "eql_epi.hip",
+    "eql_p4m.hip",
 ]
 
 CFLAGS = [

@@ -377,7 +377,7 @@ int epilogue_bwd(const void* dy, const void* pre, void* dpre, void* dbias, void*
 
 extern "C" {
 
-int eqlinear_abi_version(void) { return 201; }
+int eqlinear_abi_version(void) { return 202; }
 
 const char* eqlinear_status_string(int status) {
   switch (status) {
@@ -576,6 +576,35 @@ int eqlinear_bwd_w(const void* x, const void* dy, void* dw, void* workspace, siz
   r.tw = tw;
   return status_of(f16 ? launch_bwdw_reduce_f16(T, rwaves, r, (unsigned)rgrid, s)
                        : launch_bwdw_reduce_f32(T, rwaves, r, (unsigned)rgrid, s));
+}
+
+
+// p4m (dihedral D4) through the C_4 layer on 2C' x 2D' channels (eql_p4m.h).
+static int p4m_map(const void* src, void* dst, int64_t Dp, int64_t Cp, int dtype, void* stream, bool expand) {
+  // The C_4 view has 2C' inputs and 2D' outputs of 4 values each: its size rules apply.
+  if (Dp < 1 || Cp < 1 || Dp > (INT64_MAX / 4) || Cp > (INT64_MAX / 4)) return EQL_EINVAL;
+  const int st = check_sizes(0, 2 * Cp, 2 * Dp, 4, dtype);
+  if (st != EQL_OK) return st;
+  if (!src || !dst) return EQL_EINVAL;
+  if (!aligned16(src) || !aligned16(dst)) return EQL_EALIGN;
+  const int64_t grid = ceil_div(Dp * Cp * (expand ? 4 : 8), 256);
+  if (grid > kMaxGrid) return EQL_EINVAL;
+  P4mArgs a{};
+  a.src = src;
+  a.dst = dst;
+  a.Dp = (int)Dp;
+  a.Cp = (int)Cp;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool f16 = dtype == EQL_F16;
+  return status_of(expand ? launch_p4m_expand(f16, a, (unsigned)grid, s) : launch_p4m_fold(f16, a, (unsigned)grid, s));
+}
+
+int eqlinear_p4m_expand_weight(const void* w, void* w_c4, int64_t Dp, int64_t Cp, int dtype, void* stream) {
+  return p4m_map(w, w_c4, Dp, Cp, dtype, stream, true);
+}
+
+int eqlinear_p4m_fold_weight_grad(const void* dw_c4, void* dw, int64_t Dp, int64_t Cp, int dtype, void* stream) {
+  return p4m_map(dw_c4, dw, Dp, Cp, dtype, stream, false);
 }
 
 }  // extern "C"

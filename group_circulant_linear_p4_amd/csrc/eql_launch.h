@@ -8,6 +8,7 @@
 #include "eql_bwdw4.h"
 #include "eql_epi.h"
 #include "eql_fwd.h"
+#include "eql_p4m.h"
 #include "eql_pack.h"
 
 namespace eql {
@@ -38,6 +39,9 @@ hipError_t launch_bwdw_pair_f16(int T, int DB, int CB, const BwdwArgs& a, unsign
 hipError_t launch_bwdw_pair_f32(int T, int DB, int CB, const BwdwArgs& a, unsigned grid, hipStream_t s);
 // Weight gradient with dy's transform fused into the GEMM (T in {1, 2, 4}).
 hipError_t launch_bwdw4(bool f16, int T, int NB, const Bwdw4Args& a, unsigned grid, hipStream_t s);
+// p4m: the tied C_4 weight from w, and the p4m weight gradient from the C_4 one.
+hipError_t launch_p4m_expand(bool f16, const P4mArgs& a, unsigned grid, hipStream_t s);
+hipError_t launch_p4m_fold(bool f16, const P4mArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_bwdw_reduce_f16(int T, int waves, const BwdwReduceArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_bwdw_reduce_f32(int T, int waves, const BwdwReduceArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_pack_f16(int T, const PackArgs& a, unsigned grid, hipStream_t s);

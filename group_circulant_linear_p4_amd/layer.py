@@ -4,7 +4,9 @@ weight can be used as is ("Implementacao" in "Resumo Tecnico: Flash EQ-Linear":
 training-free, plug-and-play replacement).
 
 Forward packs the half spectrum of w and runs eqlinear_fwd; backward runs
-eqlinear_bwd_x on the conjugate-transposed packing and eqlinear_bwd_w.  With a bias,
+eqlinear_bwd_x on the conjugate-transposed packing and eqlinear_bwd_w.  EQLinearP4M is the
+layer over p4m's point group (rotations and reflections), run through the same kernels on
+the C_4 view described in include/eqlinear.h.  With a bias,
 GELU or a residual, the forward is eqlinear_fwd_fused and the backward starts with
 eqlinear_fused_epilogue_bwd.  Torch only allocates the buffers; every arithmetic step
 runs in the HIP library.
@@ -18,7 +20,8 @@ import torch
 from . import (EQL_ACT_GELU, EQL_ACT_NONE, EQL_PACK_BWDX, EQL_PACK_FWD, eqlinear_bwd_w,
                eqlinear_bwd_w_workspace_bytes, eqlinear_bwd_x, eqlinear_fused_epilogue_bwd,
                eqlinear_fused_epilogue_bwd_workspace_bytes, eqlinear_fwd, eqlinear_fwd_fused,
-               eqlinear_pack_weight, eqlinear_packed_weight_bytes)
+               eqlinear_p4m_expand_weight, eqlinear_p4m_fold_weight_grad, eqlinear_pack_weight,
+               eqlinear_packed_weight_bytes)
 
 
 def _packed(w: torch.Tensor, mode: int) -> torch.Tensor:
@@ -189,3 +192,72 @@ class EQLinear(torch.nn.Module):
     def extra_repr(self) -> str:
         return "in_channels=%d, out_channels=%d, group_order=%d, bias=%s, activation=%s" % (
             self.in_channels, self.out_channels, self.group_order, self.bias is not None, self.activation)
+
+
+class EQLinearP4MFunction(torch.autograd.Function):
+    """The layer over p4m's point group (dihedral D4): y[..., D'*8] = x[..., C'*8] W^T with
+    W[(d,g),(c,h)] = w[d, c, g h^-1], group axis r^0..r^3 then r^-m s (m = 0..3).  Run as the
+    C_4 layer on 2C' x 2D' channels with the tied weight eqlinear_p4m_expand_weight builds;
+    the weight gradient is the C_4 one folded back onto the shared parameters."""
+
+    @staticmethod
+    def forward(ctx, x: torch.Tensor, w: torch.Tensor):
+        Dp, Cp, G = w.shape
+        if G != 8:
+            raise ValueError("a p4m weight has 8 group elements per (out, in) pair, got %d" % G)
+        if x.shape[-1] != Cp * 8:
+            raise ValueError("x has %d features, the weight expects C'*8 = %d" % (x.shape[-1], Cp * 8))
+        if x.dtype != w.dtype:
+            raise ValueError("x and w must share a dtype (fp16 or fp32)")
+        w4 = torch.empty((2 * Dp, 2 * Cp, 4), dtype=w.dtype, device=w.device)
+        eqlinear_p4m_expand_weight(w.contiguous(), w4, Dp, Cp, w.dtype)
+        x2 = x.reshape(-1, Cp * 8).contiguous()
+        N = x2.shape[0]
+        y = torch.empty((N, Dp * 8), dtype=x.dtype, device=x.device)
+        eqlinear_fwd(x2, _packed(w4, EQL_PACK_FWD), y, N, 2 * Cp, 2 * Dp, 4, x.dtype)
+        ctx.save_for_backward(x2, w4)
+        ctx.lead_shape = x.shape[:-1]
+        ctx.p4m_shape = (Dp, Cp)
+        return y.reshape(*x.shape[:-1], Dp * 8)
+
+    @staticmethod
+    def backward(ctx, dy: torch.Tensor):
+        x2, w4 = ctx.saved_tensors
+        Dp, Cp = ctx.p4m_shape
+        N = x2.shape[0]
+        dy2 = dy.reshape(-1, Dp * 8).to(x2.dtype).contiguous()
+        dx = dw = None
+        if ctx.needs_input_grad[0]:
+            dx = torch.empty((N, Cp * 8), dtype=x2.dtype, device=x2.device)
+            eqlinear_bwd_x(dy2, _packed(w4, EQL_PACK_BWDX), dx, N, 2 * Cp, 2 * Dp, 4, x2.dtype)
+            dx = dx.reshape(*ctx.lead_shape, Cp * 8)
+        if ctx.needs_input_grad[1]:
+            ws_bytes = eqlinear_bwd_w_workspace_bytes(N, 2 * Cp, 2 * Dp, 4, x2.dtype)
+            ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=x2.device)
+            dw4 = torch.empty_like(w4)
+            eqlinear_bwd_w(x2, dy2, dw4, ws, ws_bytes, N, 2 * Cp, 2 * Dp, 4, x2.dtype)
+            dw = torch.empty((Dp, Cp, 8), dtype=x2.dtype, device=x2.device)
+            eqlinear_p4m_fold_weight_grad(dw4, dw, Dp, Cp, x2.dtype)
+        return dx, dw
+
+
+def eqlinear_p4m(x: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
+    return EQLinearP4MFunction.apply(x, w)
+
+
+class EQLinearP4M(torch.nn.Module):
+    """Equivariant linear layer over p4m's point group: in_channels*8 -> out_channels*8."""
+
+    def __init__(self, in_channels: int, out_channels: int, device=None, dtype=None):
+        super().__init__()
+        self.in_channels, self.out_channels = in_channels, out_channels
+        self.weight = torch.nn.Parameter(torch.empty(out_channels, in_channels, 8, device=device, dtype=dtype))
+        with torch.no_grad():
+            self.weight.normal_(0.0, 1.0 / math.sqrt(in_channels * 8))
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        return EQLinearP4MFunction.apply(x, self.weight)
+
+    def extra_repr(self) -> str:
+        return "in_channels=%d, out_channels=%d, group=p4m" % (self.in_channels, self.out_channels)
+

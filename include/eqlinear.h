@@ -256,12 +256,44 @@ size_t eqlinear_bwd_w_workspace_bytes(int64_t N, int64_t Cp, int64_t Dp, int T, 
 int eqlinear_bwd_w(const void* x, const void* dy, void* dw, void* workspace, size_t ws_bytes,
                    int64_t N, int64_t Cp, int64_t Dp, int T, int dtype, void* stream);
 
+/*
+ * The layer over p4m's point group (dihedral D4: four rotations r^a and four
+ * reflections r^a s; r^4 = s^2 = e, s r s = r^-1).  "Resumo Tecnico: Flash EQ-Linear",
+ * "Limitacoes e Trabalho Futuro", names other groups, reflection groups among them, as
+ * the method's next step; the construction is kept: shared parameters w[Dp][Cp][8]
+ * replicated into W[(d,g),(c,h)] = w[d][c][g h^-1].  The group axis of x, y and w lists
+ * r^0, r^1, r^2, r^3, then the reflections r^-m s for m = 0..3 (s, r^3 s, r^2 s, r s):
+ * x: [N][Cp*8], y: [N][Dp*8], flat index c*8 + j.
+ *
+ * With this order the p4m layer is exactly the C_4 layer (T = 4) with 2*Cp input and
+ * 2*Dp output channels, on the same memory of x and y, whose weight w4[2*Dp][2*Cp][4]
+ * is tied to w (the rotation half and the reflection half of a channel are C_4
+ * channels 2c and 2c+1; the four half-to-half blocks are circular convolutions with the
+ * kernels w(r^k), w(r^k s), w(r^-k s), w(r^-k)).  A p4m layer is therefore run as:
+ *   forward       eqlinear_p4m_expand_weight(w -> w4), eqlinear_pack_weight(w4, ..., 2Dp,
+ *                 2Cp, 4, dtype, EQL_PACK_FWD), eqlinear_fwd(x, .., y, N, 2Cp, 2Dp, 4, dtype)
+ *   input grad    the EQL_PACK_BWDX packing of w4, eqlinear_bwd_x(.., N, 2Cp, 2Dp, 4, ..)
+ *   weight grad   eqlinear_bwd_w(x, dy, dw4, ..., N, 2Cp, 2Dp, 4, dtype) into a
+ *                 [2Dp][2Cp][4] buffer, then eqlinear_p4m_fold_weight_grad(dw4 -> dw).
+ * The C_4 evaluation costs 24 real multiply-adds per (row, d, c) against 64 for the
+ * dense p4m layer.
+ *
+ * eqlinear_p4m_expand_weight: w [Dp][Cp][8] read; w_c4 [2Dp][2Cp][4] overwritten (a
+ * gather: values copied, no arithmetic).  eqlinear_p4m_fold_weight_grad: dw_c4
+ * [2Dp][2Cp][4] read; dw [Dp][Cp][8] overwritten, each entry the sum of the two entries of
+ * dw_c4 it is tied into, added in fp32 and rounded once to `dtype`.  Both: device
+ * pointers, 16-byte aligned, in `dtype`; the sizes of the C_4 view must be valid (as for
+ * the other entry points with C' = 2Cp, D' = 2Dp, T = 4); errors as there.
+ */
+int eqlinear_p4m_expand_weight(const void* w, void* w_c4, int64_t Dp, int64_t Cp, int dtype, void* stream);
+int eqlinear_p4m_fold_weight_grad(const void* dw_c4, void* dw, int64_t Dp, int64_t Cp, int dtype, void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* eqlinear_status_string(int status);
 
 /* ABI version of this header (major * 100 + minor).  2.00: the blocked packed-weight
  * layout above (1.xx stored ((o * Jin + i / G) * T + p) * G + i % G).  2.01:
- * eqlinear_fused_epilogue_bwd_noalloc and EQL_ESCRATCH. */
+ * eqlinear_fused_epilogue_bwd_noalloc and EQL_ESCRATCH.  2.02: the p4m entry points. */
 int eqlinear_abi_version(void);
 
 #ifdef __cplusplus

@@ -35,7 +35,7 @@ void* const MIS2 = reinterpret_cast<void*>(uintptr_t{0x10002});
 constexpr int F16 = EQL_F16, F32 = EQL_F32;
 
 void sizes() {
-  CHECK(eqlinear_abi_version() == 201);
+  CHECK(eqlinear_abi_version() == 202);
   for (int s = -3; s < 12; ++s) CHECK(eqlinear_status_string(s) != nullptr && std::strlen(eqlinear_status_string(s)) > 0);
   // Packed weight: out channels padded to 32, input 16-byte groups padded per stage.
   CHECK(eqlinear_packed_weight_bytes(3, 5, 4, F16) == 32u * 4 * 16 * 4);
@@ -134,6 +134,17 @@ void validation() {
         EQL_ESCRATCH);
   CHECK(eqlinear_fused_epilogue_bwd_noalloc(A, B, C, D, INT64_MAX, 1024, 4, F16, EQL_ACT_NONE, nullptr) ==
         EQL_EINVAL);
+  // p4m weight expansion and gradient fold (the C_4 view's size rules).
+  for (auto fn : {eqlinear_p4m_expand_weight, eqlinear_p4m_fold_weight_grad}) {
+    CHECK(fn(A, B, 4, 4, 7, nullptr) == EQL_EINVAL);
+    CHECK(fn(A, B, 0, 4, F16, nullptr) == EQL_EINVAL);
+    CHECK(fn(A, B, 4, INT64_MIN, F16, nullptr) == EQL_EINVAL);
+    CHECK(fn(A, B, INT64_MAX, 4, F32, nullptr) == EQL_EINVAL);
+    CHECK(fn(A, B, 4, (int64_t{1} << 20) + 1, F32, nullptr) == EQL_EINVAL);
+    CHECK(fn(nullptr, B, 4, 4, F16, nullptr) == EQL_EINVAL);
+    CHECK(fn(A, nullptr, 4, 4, F16, nullptr) == EQL_EINVAL);
+    CHECK(fn(MIS, B, 4, 4, F16, nullptr) == EQL_EALIGN);
+  }
 }
 
 }  // namespace

@@ -26,14 +26,14 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_function():
     L = eql.lib()
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 14
     for n in names:
         assert hasattr(L, n), "missing export %s" % n
         assert hasattr(eql, n), "binding lacks %s" % n
 
 
 def test_version_and_status_strings():
-    assert eql.eqlinear_abi_version() == 201
+    assert eql.eqlinear_abi_version() == 202
     for s in range(5):
         assert eql.eqlinear_status_string(s)
     assert eql.eqlinear_status_string(99) == "unknown status"
@@ -194,6 +194,22 @@ def test_fused_epilogue_bwd_noalloc_validation():
     assert raw(fn, dy, pre, dpre, db, 1 << 21, 1024, 4, F16, GELU, None) == eql.EQL_ESCRATCH
     assert raw(fn, dy, pre, dpre, db, (1 << 20) + 1024, 1024, 4, F16, NONE, None) == eql.EQL_ESCRATCH
     assert "scratch" in eql.eqlinear_status_string(eql.EQL_ESCRATCH)
+
+
+def test_p4m_map_validation():
+    """The p4m weight expansion and gradient fold validate like the other entry points,
+    with the size rules of the C_4 view (2C' inputs, 2D' outputs, T = 4)."""
+    F16, F32 = eql.EQL_F16, eql.EQL_F32
+    for fn in ("eqlinear_p4m_expand_weight", "eqlinear_p4m_fold_weight_grad"):
+        assert raw(fn, A16, A16B, 4, 4, 7, None) == eql.EQL_EINVAL               # dtype
+        assert raw(fn, A16, A16B, 0, 4, F16, None) == eql.EQL_EINVAL             # D' < 1
+        assert raw(fn, A16, A16B, 4, -3, F32, None) == eql.EQL_EINVAL            # C' < 1
+        assert raw(fn, A16, A16B, 4, 1 << 62, F32, None) == eql.EQL_EINVAL       # C' far too large
+        assert raw(fn, A16, A16B, 4, (1 << 20) + 1, F32, None) == eql.EQL_EINVAL  # 2C' x 4 x 4 B > 2^23
+        assert raw(fn, None, A16B, 4, 4, F16, None) == eql.EQL_EINVAL
+        assert raw(fn, A16, None, 4, 4, F16, None) == eql.EQL_EINVAL
+        assert raw(fn, MIS, A16B, 4, 4, F16, None) == eql.EQL_EALIGN
+        assert raw(fn, A16, MIS, 4, 4, F32, None) == eql.EQL_EALIGN
 
 
 def test_pack_validation():
