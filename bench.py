@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--rotate-mib", type=int, default=512,
                     help="rotate through enough copies of every buffer that one round of steps touches at "
                          "least this many MiB (above the 256 MiB Infinity Cache); 0: one resident set")
+    ap.add_argument("--group", default="cyclic", choices=["cyclic", "p4m"],
+                    help="p4m: time the layer over p4m's point group (dihedral D4, 8 elements) on the "
+                         "workload's feature widths C and D (C' = C/8, D' = D/8), instead of the C_T layer")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run a plain device copy of this size (a reference for "
                          "profiler traffic counters)")
@@ -97,6 +100,8 @@ def main():
         sys.exit(1)
     eql.lib()  # fail loudly if the HIP library is missing
     wl = W.WORKLOADS[args.workload]
+    if args.group == "p4m":
+        return bench_p4m(args, torch, eql, wl)
     T, N, Cp, Dp = wl.T, wl.N, wl.Cp, wl.Dp
     code = eql.EQL_F16 if wl.dtype == "f16" else eql.EQL_F32
     tdt = torch.float16 if wl.dtype == "f16" else torch.float32
@@ -530,6 +535,105 @@ def cpu_baseline(wl, x_h, w_h, dy_h, rows, n_passes, target_s=12.0, min_s=10.0, 
             "kind": "oracle",
             "sample": "%s of the same workload x %d run(s), forward + input gradient + weight gradient, "
                       "fp64 dense unroll (%.1f s)" % (what, reps, total)}
+
+
+def bench_p4m(args, torch, eql, wl):
+    """The p4m layer's training step on the workload's feature widths: weight expansion and
+    both packings, forward, input gradient, weight gradient and its fold; all on the C_4 view
+    (2C' x 2D' channels, T = 4) the library runs p4m as.  One JSON line like main()'s."""
+    C, D, N = wl.Cp * wl.T, wl.Dp * wl.T, wl.N
+    if C % 8 or D % 8:
+        print("p4m needs feature widths divisible by 8", file=sys.stderr)
+        sys.exit(2)
+    Cp, Dp = C // 8, D // 8
+    code = eql.EQL_F16 if wl.dtype == "f16" else eql.EQL_F32
+    tdt = torch.float16 if wl.dtype == "f16" else torch.float32
+    elt = 2 if wl.dtype == "f16" else 4
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("bench: generating %s as a p4m layer (C'=%d, D'=%d)" % (wl.name, Cp, Dp), file=sys.stderr, flush=True)
+    x_h, dy_h = W.make_x(wl), W.make_dy(wl)
+    g = np.random.default_rng(wl.seed + 101)
+    w_h = (g.standard_normal((Dp, Cp, 8), dtype=np.float32) / np.sqrt(C)).astype(x_h.dtype)
+    x, dy, w = (torch.from_numpy(a).to(dev) for a in (x_h, dy_h, w_h))
+    w4 = torch.empty((2 * Dp, 2 * Cp, 4), dtype=tdt, device=dev)
+    wp = torch.empty(eql.eqlinear_packed_weight_bytes(2 * Dp, 2 * Cp, 4, code), dtype=torch.uint8, device=dev)
+    wpb = torch.empty(eql.eqlinear_packed_weight_bytes(2 * Cp, 2 * Dp, 4, code), dtype=torch.uint8, device=dev)
+    y = torch.empty((N, D), dtype=tdt, device=dev)
+    dx = torch.empty((N, C), dtype=tdt, device=dev)
+    dw4 = torch.empty_like(w4)
+    dw = torch.empty_like(w)
+    ws_bytes = eql.eqlinear_bwd_w_workspace_bytes(N, 2 * Cp, 2 * Dp, 4, code)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    calls = {
+        "pack": lambda: (eql.eqlinear_p4m_expand_weight(w, w4, Dp, Cp, code, sp),
+                         eql.eqlinear_pack_weight(w4, wp, 2 * Dp, 2 * Cp, 4, code, eql.EQL_PACK_FWD, sp),
+                         eql.eqlinear_pack_weight(w4, wpb, 2 * Dp, 2 * Cp, 4, code, eql.EQL_PACK_BWDX, sp)),
+        "fwd": lambda: eql.eqlinear_fwd(x, wp, y, N, 2 * Cp, 2 * Dp, 4, code, sp),
+        "bwd_x": lambda: eql.eqlinear_bwd_x(dy, wpb, dx, N, 2 * Cp, 2 * Dp, 4, code, sp),
+        "bwd_w": lambda: (eql.eqlinear_bwd_w(x, dy, dw4, ws, ws_bytes, N, 2 * Cp, 2 * Dp, 4, code, sp),
+                          eql.eqlinear_p4m_fold_weight_grad(dw4, dw, Dp, Cp, code, sp)),
+    }
+    order = ["pack", "fwd", "bwd_x", "bwd_w"]
+    for _ in range(args.warmup):
+        for k in order:
+            calls[k]()
+    torch.cuda.synchronize()
+    evs = [{k: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for k in order}
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        for k in order:
+            evs[i][k][0].record(stream)
+            calls[k]()
+            evs[i][k][1].record(stream)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    per = {k: float(np.mean([e[k][0].elapsed_time(e[k][1]) for e in evs])) for k in order}
+    dense_eq = 2.0 * N * D * C
+    actual = 2.0 * 6 * N * (2 * Dp) * (2 * Cp)            # the C_4 view's six real GEMMs
+    value = 3 * dense_eq / (ms_step * 1e-3) / 1e12
+    bytes_pass = elt * (N * C + N * D + D * C // 4)        # x, y once; w4 (2D' x 2C' x 4: twice the parameters)
+    passes = {k: {"ms": round(per[k], 4), "dense_eq_tflops": round(dense_eq / (per[k] * 1e-3) / 1e12, 1),
+                  "actual_tflops": round(actual / (per[k] * 1e-3) / 1e12, 1)} for k in ("fwd", "bwd_x", "bwd_w")}
+    t_dom = 0.5 * (per["fwd"] + per["bwd_x"]) * 1e-3
+    if actual / MFMA_PEAK[wl.dtype] / 1e12 >= bytes_pass / HBM_PEAK / 1e9:
+        roofline = {"bound": "mfma", "achieved": round(actual / t_dom / 1e12, 1), "peak": MFMA_PEAK[wl.dtype],
+                    "unit": "TFLOP/s"}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(bytes_pass / t_dom / 1e9, 1), "peak": HBM_PEAK, "unit": "GB/s"}
+    roofline["frac"] = round(roofline["achieved"] / roofline["peak"], 4)
+    roofline["traffic"] = None
+    roofline["kernel"] = "eql_fwd4_kernel (C_4 view)"
+    roofline["ms_per_launch"] = round(t_dom * 1e3, 4)
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import p4m_oracle as P
+        rows = args.cpu_rows if args.cpu_rows > 0 else N
+        xs, dys = x_h[:rows], dy_h[:rows]
+        total, reps = 0.0, 0
+        while reps == 0 or (total < 10.0 and reps < 6):  # about 10 s of oracle work
+            t0 = time.perf_counter()
+            P.fwd(xs, w_h)
+            P.bwd_x(dys, w_h)
+            P.bwd_w(xs, dys)
+            total += time.perf_counter() - t0
+            reps += 1
+        cpu = {"value": round(3 * 2.0 * rows * D * C * reps / total / 1e12, 5), "unit": "TFLOP/s",
+               "cores": len(os.sched_getaffinity(0)), "cpu": cpu_model(), "kind": "oracle",
+               "sample": "rows 0..%d x %d run(s), p4m oracle forward + input gradient + weight gradient, "
+                         "fp64 dense unroll (%.1f s)" % (rows - 1, reps, total)}
+    line = {"metric": "p4m EQ-Linear dense-equivalent TFLOP/s, %s fwd/bwd, 1 MI355X" % wl.dtype,
+            "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": wl.dtype, "data": "synthetic (seeded; x, dy ~ N(0,1), w ~ N(0,1/C))",
+            "config": {"workload": "p4m layer on %s's widths: N=%d, C=%d (C'=%d x 8), D=%d (D'=%d x 8)"
+                                   % (wl.key, N, C, Cp, D, Dp),
+                       "group": "p4m (D4)", "step": "expand+pack x2, fwd, bwd_x, bwd_w+fold"},
+            "passes": passes, "pack_ms": round(per["pack"], 4), "roofline": roofline, "cpu_baseline": cpu}
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":
