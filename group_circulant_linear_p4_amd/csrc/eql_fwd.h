@@ -63,26 +63,23 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 // raw[4q+2..4q+3] those of channel 2q+1) into the A-operand units X0, X2, Xr, Xi and
 // -Xi (8 halves each), with instructions that issue alongside MFMAs (v_dot2 does not:
 // on gfx950 it occupies the matrix pipeline and serialises with the MFMAs).
-//   x0 + x2 and x1 + x3 are formed in fp32 from the fp16 halves by v_fma_mix_f32
-//   (x * 1 + y, exact for fp16 operands within 13 binades of each other), X0 / X2 are
-//   their fp32 sum / difference, rounded once to fp16.  Xr = x0 - x2 and -Xi = x1 - x3
-//   come from one packed fp16 subtraction per channel (one rounding of the exact
-//   difference).  The 1/2 of the p4 forward transform is folded into the packed
-//   weight's real planes.
+//   Everything is packed fp16 arithmetic, two channels or two group elements per op:
+//   one addition per channel gives (x0 + x2, x1 + x3), one subtraction gives
+//   (Xr, -Xi) = (x0 - x2, x1 - x3); X0 / X2 are the sum / difference of the two sums
+//   (so X0 and X2 take two fp16 roundings, Xr and Xi one).  The 1/2 of the p4 forward
+//   transform is folded into the packed weight's real planes.
 __device__ __forceinline__ void dft_p4_f16(const uint32_t (&raw)[16], u32x4 (&out)[5]) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {  // channel pair (2q, 2q+1) -> word q of each unit
     const uint32_t a0 = raw[4 * q + 0], b0 = raw[4 * q + 1];
     const uint32_t a1 = raw[4 * q + 2], b1 = raw[4 * q + 3];
-    float s02e, s13e, s02o, s13o;
-    asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,1]" : "=v"(s02e) : "v"(a0), "v"(b0));
-    asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "=v"(s13e) : "v"(a0), "v"(b0));
-    asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,1]" : "=v"(s02o) : "v"(a1), "v"(b1));
-    asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "=v"(s13o) : "v"(a1), "v"(b1));
-    const f16x2 X0 = {(_Float16)(s02e + s13e), (_Float16)(s02o + s13o)};
-    const f16x2 X2 = {(_Float16)(s02e - s13e), (_Float16)(s02o - s13o)};
-    const f16x2 d0 = __builtin_bit_cast(f16x2, a0) - __builtin_bit_cast(f16x2, b0);  // (Xr, -Xi) of channel 2q
-    const f16x2 d1 = __builtin_bit_cast(f16x2, a1) - __builtin_bit_cast(f16x2, b1);
+    const f16x2 A0 = __builtin_bit_cast(f16x2, a0), B0 = __builtin_bit_cast(f16x2, b0);
+    const f16x2 A1 = __builtin_bit_cast(f16x2, a1), B1 = __builtin_bit_cast(f16x2, b1);
+    const f16x2 s0 = A0 + B0, s1 = A1 + B1;                  // (x0+x2, x1+x3) of channels 2q, 2q+1
+    const f16x2 lo = __builtin_shufflevector(s0, s1, 0, 2);  // x0+x2 of both channels
+    const f16x2 hi = __builtin_shufflevector(s0, s1, 1, 3);  // x1+x3 of both channels
+    const f16x2 X0 = lo + hi, X2 = lo - hi;
+    const f16x2 d0 = A0 - B0, d1 = A1 - B1;                  // (Xr, -Xi) of channels 2q, 2q+1
     const uint32_t nxi = __builtin_bit_cast(uint32_t, __builtin_shufflevector(d0, d1, 1, 3));
     out[0][q] = __builtin_bit_cast(uint32_t, X0);
     out[1][q] = __builtin_bit_cast(uint32_t, X2);
