@@ -32,31 +32,37 @@ __host__ __device__ constexpr int n_pairs(int T) { return (T - n_real_planes(T))
 // cos / sin of 2*pi*m/T for m = 0..T-1, computed on the host in double and rounded
 // once to float.  Passed as a kernel argument, so the values live in scalar
 // registers.  Entries whose exact value is 0 or +-1 are never read: those cases are
-// folded at compile time (see mac_cos / mac_msin).
+// folded at compile time (see acc_cos / acc_msin).
 struct Twiddles {
   float cs[kMaxT];
   float sn[kMaxT];
   float inv_t;  // 1/T rounded to float
 };
 
-// s + v * cos(2 pi m / T) with the exact coefficient when it is 0 or +-1.
+// Twiddle sums.  s accumulates v * cos(2 pi m / T) (acc_cos) or -v * sin(2 pi m / T)
+// (acc_msin), with the exact coefficient when it is 0 or +-1; `any` says whether s
+// holds a term yet.  The first term is taken as it is rather than added to zero:
+// 0 + t differs from t only in the sign of a zero, so the compiler may not drop
+// that addition, and it would cost one instruction per sum.  m and `any` are
+// compile-time constants once the callers' loops are unrolled.
 template <int T>
-__device__ __forceinline__ float mac_cos(float s, float v, int m, const Twiddles& tw) {
+__device__ __forceinline__ void acc_cos(float& s, bool& any, float v, int m, const Twiddles& tw) {
   m %= T;
-  if (m == 0) return s + v;
-  if (2 * m == T) return s - v;
-  if (4 * m == T || 4 * m == 3 * T) return s;
-  return __builtin_fmaf(v, tw.cs[m], s);
+  if (4 * m == T || 4 * m == 3 * T) return;
+  if (m == 0) s = any ? s + v : v;
+  else if (2 * m == T) s = any ? s - v : -v;
+  else s = any ? __builtin_fmaf(v, tw.cs[m], s) : v * tw.cs[m];
+  any = true;
 }
 
-// s - v * sin(2 pi m / T) with the exact coefficient when it is 0 or +-1.
 template <int T>
-__device__ __forceinline__ float mac_msin(float s, float v, int m, const Twiddles& tw) {
+__device__ __forceinline__ void acc_msin(float& s, bool& any, float v, int m, const Twiddles& tw) {
   m %= T;
-  if (m == 0 || 2 * m == T) return s;
-  if (4 * m == T) return s - v;
-  if (4 * m == 3 * T) return s + v;
-  return __builtin_fmaf(-v, tw.sn[m], s);
+  if (m == 0 || 2 * m == T) return;
+  if (4 * m == T) s = any ? s - v : -v;
+  else if (4 * m == 3 * T) s = any ? s + v : v;
+  else s = any ? __builtin_fmaf(-v, tw.sn[m], s) : -v * tw.sn[m];
+  any = true;
 }
 
 // ---------------------------------------------------------------------------
@@ -72,8 +78,12 @@ struct Dft {
       const int k = p == 0 ? 0 : (p < NR ? T / 2 : (p - NR) / 2 + 1);
       const bool im = p >= NR && ((p - NR) & 1);
       float s = 0.0f;
+      bool any = false;
 #pragma unroll
-      for (int h = 0; h < T; ++h) s = im ? mac_msin<T>(s, v[h], h * k, tw) : mac_cos<T>(s, v[h], h * k, tw);
+      for (int h = 0; h < T; ++h) {
+        if (im) acc_msin<T>(s, any, v[h], h * k, tw);
+        else acc_cos<T>(s, any, v[h], h * k, tw);
+      }
       out[p] = s;
     }
   }
@@ -111,12 +121,14 @@ struct Idft {
       float s = P[0];
       if (NR == 2) s = (g & 1) ? s - P[1] : s + P[1];
       float u = 0.0f;
+      bool any = false;
 #pragma unroll
       for (int q = 0; q < n_pairs(T); ++q) {
-        u = mac_cos<T>(u, P[NR + 2 * q], g * (q + 1), tw);
-        u = mac_msin<T>(u, P[NR + 2 * q + 1], g * (q + 1), tw);
+        acc_cos<T>(u, any, P[NR + 2 * q], g * (q + 1), tw);
+        acc_msin<T>(u, any, P[NR + 2 * q + 1], g * (q + 1), tw);
       }
-      y[g] = kPlain ? (s + 2.0f * u) * tw.inv_t : s + u;
+      if (any) s = kPlain ? s + 2.0f * u : s + u;
+      y[g] = kPlain ? s * tw.inv_t : s;
     }
   }
 };
