@@ -479,7 +479,7 @@ int eqlinear_bwd_w(const void* x, const void* dy, void* dw, void* workspace, siz
     return EQL_EALIGN;
   const int64_t gdy = ceil_div(p.kgCount * 2 * p.Dpad, 256);
   const int64_t gx = ceil_div(p.kgCount * 2 * p.Cpad, 256);
-  const int rwaves = reduce_waves(p.real.S * n_real_planes(T) + p.pair.S * (T - n_real_planes(T)));
+  const int rwaves = reduce_waves(p.real.S * n_real_planes(T) + p.pair.S * (T - n_real_planes(T)), Dp * Cp);
   const int64_t rgrid = ceil_div(Dp * Cp, 256 / rwaves);
   const int64_t fItems = p.fS * p.fDTiles * p.fCTiles;
   if (p.real.items() > kMaxGrid || p.pair.items() > kMaxGrid || gdy > kMaxGrid || gx > kMaxGrid ||

@@ -301,11 +301,12 @@ __global__ void __launch_bounds__(256) eql_bwdw_gemm(const BwdwArgs a) {
 }
 
 // Sum of the split partials, then the inverse group transform.  WAVES = 1: one
-// output per thread, all splits in one chain.  WAVES = 4 (for long chains): a
-// workgroup covers 64 consecutive (d, c) outputs and wave w sums splits w, w+4,
-// w+8, ... for them (adjacent lanes read adjacent outputs); wave 0 adds the four
-// partial sums in a fixed order.  Either way the order depends only on the shape,
-// so the result does not depend on timing.  Both operands were transformed
+// output per thread, all splits in one chain.  WAVES = 4 or 16 (for long chains):
+// a workgroup covers 256 / WAVES consecutive (d, c) outputs, and the threads of
+// phase w sum splits w, w + WAVES, ... for them (adjacent threads read adjacent
+// outputs); the first phase adds the other phases' sums in a fixed order.  Either
+// way the order depends only on the shape, so the result does not depend on
+// timing.  Both operands were transformed
 // without scaling, so the inverse is the plain one,
 //   dw[t] = (1/T) (G0 + (-1)^t G_{T/2} + 2 sum_k (cos Re G_k - sin Im G_k)),
 // followed by one rounding to the element type.
@@ -354,9 +355,13 @@ __global__ void __launch_bounds__(256) eql_bwdw_reduce(const BwdwReduceArgs a) {
   }
 }
 
-// Waves per output group of the reduce, from the loads one thread would chain
-// (splits x planes): sharing them pays only for long chains (c5: 32 loads, one wave;
-// the small layers: 128 and more, four).
-__host__ __device__ constexpr int reduce_waves(int64_t chain) { return chain >= 64 ? 4 : 1; }
+// Phases per output group of the reduce, from the loads one thread would chain
+// (splits x planes) and the number of outputs: sharing the chain pays only when it
+// is long (c5: 32 loads, one phase), and 16 phases give small layers with long
+// chains enough workgroups to fill the chip (the C8 layer with 64 x 64 channels:
+// 4096 outputs and 766 loads, 256 workgroups instead of 64).
+__host__ __device__ constexpr int reduce_waves(int64_t chain, int64_t outputs) {
+  return chain < 64 ? 1 : (chain >= 256 && outputs / 64 < 256 ? 16 : 4);
+}
 
 }  // namespace eql

@@ -10,8 +10,9 @@ static hipError_t spec_one(const SpecArgs& a, unsigned grid, hipStream_t s) {
 
 template <int T>
 static hipError_t reduce_one(int waves, const BwdwReduceArgs& a, unsigned grid, hipStream_t s) {
-  return waves == 4 ? launch_kernel((const void*)&eql_bwdw_reduce<T, _Float16, 4>, grid, a, s)
-                    : launch_kernel((const void*)&eql_bwdw_reduce<T, _Float16, 1>, grid, a, s);
+  return waves == 16  ? launch_kernel((const void*)&eql_bwdw_reduce<T, _Float16, 16>, grid, a, s)
+         : waves == 4 ? launch_kernel((const void*)&eql_bwdw_reduce<T, _Float16, 4>, grid, a, s)
+                      : launch_kernel((const void*)&eql_bwdw_reduce<T, _Float16, 1>, grid, a, s);
 }
 
 hipError_t launch_spec_f16(int T, const SpecArgs& a, unsigned grid, hipStream_t s) {
