@@ -159,7 +159,7 @@ size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 // then the fp32 partial spectra of the real-plane GEMM [SR][NR][Dp][Cp] and of the
 // complex-pair GEMM [SP][T-NR][Dp][Cp].
 struct GemmPlan {
-  int DB = 1, CB = 1;  // workgroup tile 64 DB x 64 CB
+  int DB = 1, CB = 1, WCN = 2;  // 2 x WCN waves of DB x CB blocks: tile 64 DB x 32 CB WCN
   int64_t groups = 0, dTiles = 0, cTiles = 0, S = 0, kgPerSplit = 0;
   int64_t items() const { return S * groups * dTiles * cTiles; }
 };
@@ -207,6 +207,18 @@ bool bwdw_fused(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype) {
   return flops / bytes < kFusedIntensity;
 }
 
+// Waves per workgroup of the separate path's GEMMs on 256-wide tiles.
+// EQL_BWDW_WAVES=4|8 overrides the choice (for measurement).
+int bwdw_waves() {
+  static const int forced = [] {
+    const char* v = std::getenv("EQL_BWDW_WAVES");
+    if (v && std::strcmp(v, "4") == 0) return 4;
+    if (v && std::strcmp(v, "8") == 0) return 8;
+    return 0;
+  }();
+  return forced ? forced : 8;
+}
+
 constexpr int64_t kMinStepsPerSplit = 16;  // keeps partial-spectrum traffic small
 
 // Row ranges (k-step ranges) of one GEMM launch: enough to give every compute unit
@@ -232,12 +244,20 @@ BwdwPlan plan_bwdw(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype) {
   p.real.CB = (int)(wc / 64);
   p.pair.DB = p.real.DB;
   p.pair.CB = wc == 256 ? 2 : 1;
+  // 256 x 256 (real) and 256 x 128 (pair) tiles: 8 waves, two per SIMD, each with half
+  // the columns of the 4-wave arrangement.
+  if (bwdw_waves() == 8 && wd == 256 && wc == 256) {
+    p.real.CB = 2;
+    p.real.WCN = 4;
+    p.pair.CB = 1;
+    p.pair.WCN = 4;
+  }
   p.real.groups = nr;
   p.real.dTiles = p.Dpad / wd;
   p.real.cTiles = p.Cpad / wc;
   p.pair.groups = np;
   p.pair.dTiles = p.Dpad / wd;
-  p.pair.cTiles = p.Cpad / (64 * p.pair.CB);
+  p.pair.cTiles = p.Cpad / (32 * p.pair.CB * p.pair.WCN);
   if (N == 0) return p;
   p.kgCount = ceil_div(N, 2 * group_channels(dtype));
   if (bwdw_fused(N, Cp, Dp, T, dtype)) {
@@ -557,11 +577,11 @@ int eqlinear_bwd_w(const void* x, const void* dy, void* dw, void* workspace, siz
       a.cTiles = (int)g.cTiles;
       a.numItems = (int)g.items();
       if (pair)
-        e = f16 ? launch_bwdw_pair_f16(T, g.DB, g.CB, a, (unsigned)a.numItems, s)
-                : launch_bwdw_pair_f32(T, g.DB, g.CB, a, (unsigned)a.numItems, s);
+        e = f16 ? launch_bwdw_pair_f16(T, g.DB, g.CB, g.WCN, a, (unsigned)a.numItems, s)
+                : launch_bwdw_pair_f32(T, g.DB, g.CB, g.WCN, a, (unsigned)a.numItems, s);
       else
-        e = f16 ? launch_bwdw_real_f16(T, g.DB, g.CB, a, (unsigned)a.numItems, s)
-                : launch_bwdw_real_f32(T, g.DB, g.CB, a, (unsigned)a.numItems, s);
+        e = f16 ? launch_bwdw_real_f16(T, g.DB, g.CB, g.WCN, a, (unsigned)a.numItems, s)
+                : launch_bwdw_real_f32(T, g.DB, g.CB, g.WCN, a, (unsigned)a.numItems, s);
       if (e != hipSuccess) return EQL_EHIP;
     }
   }

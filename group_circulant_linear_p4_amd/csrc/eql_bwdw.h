@@ -15,10 +15,10 @@
 //      past the channel count are zero).  Layout [kg][p][half][Kpad] with the channel
 //      axis padded to a multiple of the GEMM tile width, so a tile's units of one
 //      k-step are 2 or 4 contiguous runs.  Purely bandwidth bound.
-//   2. eql_bwdw_gemm<T, Elt, PAIR, DB, CB>: the per-frequency GEMMs, one plane group
-//      per workgroup so that its output tile can be as large as the register file
-//      allows: 4 waves in a 2 x 2 arrangement, each with DB x CB blocks of 32 x 32
-//      outputs per plane.  For large channel counts a real plane takes a 256 (d) x
+//   2. eql_bwdw_gemm<T, Elt, PAIR, DB, CB, WCN>: the per-frequency GEMMs, one plane
+//      group per workgroup so that its output tile can be as large as the register
+//      file allows: 2 x WCN waves, each with DB x CB blocks of 32 x 32 outputs per
+//      plane (WCN = 2: one wave per SIMD; WCN = 4: two, each with half the columns).  For large channel counts a real plane takes a 256 (d) x
 //      256 (c) tile and a complex pair a 256 x 128 tile of both planes (256
 //      accumulator registers per lane either way); per MFMA that moves about
 //      0.56-0.75x the operand bytes of a tile holding all T planes.  Narrow channel
@@ -94,20 +94,22 @@ __global__ void __launch_bounds__(256) eql_spec_kernel(const SpecArgs a) {
   for (int p = 0; p < T; ++p) __builtin_nontemporal_store(E::pack(pl[p]), &out[(size_t)p * 2 * a.Kpad]);
 }
 
-template <int T, typename Elt, bool PAIR, int DB, int CB>
-__global__ void __launch_bounds__(256) eql_bwdw_gemm(const BwdwArgs a) {
+template <int T, typename Elt, bool PAIR, int DB, int CB, int WCN>
+__global__ void __launch_bounds__(128 * WCN) eql_bwdw_gemm(const BwdwArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using E = EltT<Elt>;
   constexpr int NR = n_real_planes(T);
   constexpr int NPL = PAIR ? 2 : 1;          // planes per item
+  constexpr int WAVES = 2 * WCN;             // 2 x WCN waves
   constexpr int WD = 64 * DB;                // output channels d per workgroup
-  constexpr int WC = 64 * CB;                // input channels c per workgroup
+  constexpr int WC = 32 * CB * WCN;          // input channels c per workgroup
   constexpr int UA = NPL * 2 * WD;           // A units per stage (one k-step)
   constexpr int UB = NPL * 2 * WC;           // B units per stage
-  // ... padded to whole loads of 4 waves x 64 lanes
-  constexpr int UAP = (UA + 255) / 256 * 256, UBP = (UB + 255) / 256 * 256;
+  // ... padded to whole loads of all waves x 64 lanes
+  constexpr int LW = 64 * WAVES;
+  constexpr int UAP = (UA + LW - 1) / LW * LW, UBP = (UB + LW - 1) / LW * LW;
   constexpr int NS = 4;
-  constexpr int IPWA = UAP / 256, IPWB = UBP / 256;  // DMA loads per wave per stage
+  constexpr int IPWA = UAP / LW, IPWB = UBP / LW;  // DMA loads per wave per stage
   constexpr int IPW = IPWA + IPWB;
   static_assert(NS * (UAP + UBP) * 16 <= 160 * 1024, "LDS budget");
   static_assert((NS - 1) * IPW < 64, "vmcnt range");
@@ -117,7 +119,7 @@ __global__ void __launch_bounds__(256) eql_bwdw_gemm(const BwdwArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wd = wave >> 1, wc = wave & 1;  // 2 x 2 waves
+  const int wd = wave / WCN, wc = wave % WCN;  // 2 x WCN waves
   const int lcol = lane & 31, khalf = lane >> 5;
   const int item = xcd_remap(blockIdx.x, a.numItems);
   const int per = a.groups * a.dTiles * a.cTiles;
@@ -189,7 +191,7 @@ __global__ void __launch_bounds__(256) eql_bwdw_gemm(const BwdwArgs a) {
         for (int r = 0; r < 16; ++r) acc[q][i][jc][r] = 0.0f;
 
   // Operand fragments of one k-step: lane (lcol, khalf) holds plane q of output
-  // channel d0 + (WD/2)*wd + 32*i + lcol (A) / input channel c0 + (WC/2)*wc + 32*jc
+  // channel d0 + (WD/2)*wd + 32*i + lcol (A) / input channel c0 + (WC/WCN)*wc + 32*jc
   // + lcol (B) for rows khalf*G .. +G of the step.
   struct Frags {
     u32x4 a[NPL][DB];
@@ -203,7 +205,7 @@ __global__ void __launch_bounds__(256) eql_bwdw_gemm(const BwdwArgs a) {
 #pragma unroll
       for (int i = 0; i < DB; ++i) f.a[q][i] = sa[(q * 2 + khalf) * WD + wd * (WD / 2) + i * 32 + lcol];
 #pragma unroll
-      for (int jc = 0; jc < CB; ++jc) f.b[q][jc] = sb[(q * 2 + khalf) * WC + wc * (WC / 2) + jc * 32 + lcol];
+      for (int jc = 0; jc < CB; ++jc) f.b[q][jc] = sb[(q * 2 + khalf) * WC + wc * (WC / WCN) + jc * 32 + lcol];
     }
   };
 
@@ -289,7 +291,7 @@ __global__ void __launch_bounds__(256) eql_bwdw_gemm(const BwdwArgs a) {
     for (int i = 0; i < DB; ++i)
 #pragma unroll
       for (int jc = 0; jc < CB; ++jc) {
-        const int c = c0 + wc * (WC / 2) + jc * 32 + lcol;
+        const int c = c0 + wc * (WC / WCN) + jc * 32 + lcol;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int d = d0 + wd * (WD / 2) + i * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);

@@ -33,10 +33,10 @@ hipError_t launch_spec_f16(int T, const SpecArgs& a, unsigned grid, hipStream_t 
 hipError_t launch_spec_f32(int T, const SpecArgs& a, unsigned grid, hipStream_t s);
 // Weight-gradient GEMMs: the real planes' (DB, CB in {4, 1}) and the complex pairs'
 // (DB in {4, 1}, CB in {2, 1}; T >= 3), workgroup tile 64 DB x 64 CB.
-hipError_t launch_bwdw_real_f16(int T, int DB, int CB, const BwdwArgs& a, unsigned grid, hipStream_t s);
-hipError_t launch_bwdw_real_f32(int T, int DB, int CB, const BwdwArgs& a, unsigned grid, hipStream_t s);
-hipError_t launch_bwdw_pair_f16(int T, int DB, int CB, const BwdwArgs& a, unsigned grid, hipStream_t s);
-hipError_t launch_bwdw_pair_f32(int T, int DB, int CB, const BwdwArgs& a, unsigned grid, hipStream_t s);
+hipError_t launch_bwdw_real_f16(int T, int DB, int CB, int WCN, const BwdwArgs& a, unsigned grid, hipStream_t s);
+hipError_t launch_bwdw_real_f32(int T, int DB, int CB, int WCN, const BwdwArgs& a, unsigned grid, hipStream_t s);
+hipError_t launch_bwdw_pair_f16(int T, int DB, int CB, int WCN, const BwdwArgs& a, unsigned grid, hipStream_t s);
+hipError_t launch_bwdw_pair_f32(int T, int DB, int CB, int WCN, const BwdwArgs& a, unsigned grid, hipStream_t s);
 // Weight gradient with dy's transform fused into the GEMM (T in {1, 2, 4}).
 hipError_t launch_bwdw4(bool f16, int T, int NB, const Bwdw4Args& a, unsigned grid, hipStream_t s);
 // p4m: the tied C_4 weight from w, and the p4m weight gradient from the C_4 one.

@@ -773,3 +773,30 @@ def test_bwd_w_both_paths(path):
     assert len(res) == len(_PATH_CASES)
     for key, (err, nbytes) in res.items():
         assert err <= TOL[key.split("/")[1]], (key, err)
+
+
+# Shapes whose channel axes take 256-wide GEMM tiles on the separate weight-gradient path
+# (ragged tiles on both axes, T with and without complex pairs, both dtypes).
+_WAVE_CASES = [(8, "f16", 600, 200, 500), (8, "f32", 300, 256, 256), (4, "f16", 1000, 256, 400),
+               (6, "f32", 257, 230, 450), (2, "f16", 900, 300, 260)]
+
+
+@pytest.mark.parametrize("waves", ["4", "8"])
+def test_bwd_w_gemm_wave_arrangements(waves):
+    """The separate path's GEMMs on 256-wide tiles with 4 waves (one per SIMD) and with 8
+    (two per SIMD, half the columns each), selected with EQL_BWDW_WAVES in a child process,
+    against the oracle."""
+    import json
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, EQL_BWDW_PATH="separate", EQL_BWDW_WAVES=waves)
+    r = subprocess.run([sys.executable, "-c", _PATH_CHILD, root, json.dumps(_WAVE_CASES)], env=env,
+                       capture_output=True, text=True, timeout=170)
+    print(r.stdout[-3000:], r.stderr[-3000:], flush=True)
+    assert r.returncode == 0
+    res = json.loads([l for l in r.stdout.splitlines() if l.startswith("RESULT ")][-1][7:])
+    assert len(res) == len(_WAVE_CASES)
+    for key, (err, nbytes) in res.items():
+        assert err <= TOL[key.split("/")[1]], (key, err)
