@@ -776,9 +776,11 @@ def test_bwd_w_both_paths(path):
 
 
 # Shapes whose channel axes take 256-wide GEMM tiles on the separate weight-gradient path
-# (ragged tiles on both axes, T with and without complex pairs, both dtypes).
+# (ragged tiles on both axes, T with and without complex pairs, both dtypes, one row, a
+# partial k-step, several row ranges).
 _WAVE_CASES = [(8, "f16", 600, 200, 500), (8, "f32", 300, 256, 256), (4, "f16", 1000, 256, 400),
-               (6, "f32", 257, 230, 450), (2, "f16", 900, 300, 260)]
+               (6, "f32", 257, 230, 450), (2, "f16", 900, 300, 260), (4, "f16", 1, 256, 256),
+               (8, "f32", 15, 300, 210), (3, "f16", 4000, 512, 256)]
 
 
 @pytest.mark.parametrize("waves", ["4", "8"])
