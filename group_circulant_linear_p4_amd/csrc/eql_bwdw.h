@@ -26,8 +26,8 @@
 //      into NS-deep LDS rings by buffer->LDS loads; the loop body is LDS reads and
 //      MFMAs.  Each item writes the fp32 partial spectrum of one row range.
 //   3. eql_bwdw_reduce: sums the partials in a fixed order (deterministic; with long
-//      chains four waves share the splits of 64 outputs, combined in order), applies
-//      the inverse group transform and rounds to the element type.
+//      chains 4 or 16 phases of threads share the splits of 64 or 16 outputs, combined
+//      in order), applies the inverse group transform and rounds to the element type.
 #pragma once
 
 #include <type_traits>
