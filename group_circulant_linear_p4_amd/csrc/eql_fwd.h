@@ -15,8 +15,9 @@
 //     its x straight into registers with narrower bounds-checked loads).  Lane l
 //     takes row l%32 and channel group l/32 (G channels x T group elements) in MFMA
 //     A-operand order; rows past N and channels past C' read as zero.  The group DFT
-//     runs in fp32 registers and rounds once to the element type; the negated Im
-//     planes needed by the real part of each complex product are made by a sign flip;
+//     runs in fp32 registers and rounds once to the element type (p4 fp16: packed
+//     fp16 butterflies, see dft_p4_f16); the negated Im planes needed by the real
+//     part of each complex product are made by a sign flip;
 //   * the packed spectrum of w streams into its own LDS ring, one contiguous run per
 //     32-channel block and stage (see packed_unit);
 //   * per k-step and 32-column block: real planes take one MFMA, a complex pair

@@ -243,9 +243,12 @@ size_t eqlinear_bwd_w_workspace_bytes(int64_t N, int64_t Cp, int64_t Dp, int T, 
  *  - fused (T in {1, 2, 4}, Dp T sizeof(element) a multiple of 16, and fewer than
  *    400 real-product FLOPs per byte of x and dy, i.e. memory-bound shapes): only
  *    x's transform goes to the workspace; the GEMM reads dy's raw rows and forms
- *    their spectrum (rounded once to `dtype`, as on the separate path) as it goes.
+ *    their spectrum as it goes (p4 fp16: with the forward's packed fp16 butterflies,
+ *    which round the two real frequencies twice; otherwise in fp32, rounded once).
  *    The environment variable EQL_BWDW_PATH=fused|separate, read once per process,
- *    overrides the choice among shapes the fused path accepts.
+ *    overrides the choice among shapes the fused path accepts (for measurement), and
+ *    EQL_BWDW_WAVES=4|8 the waves per workgroup of the separate path's GEMMs on
+ *    256-channel tiles (default 8).
  * Both write one fp32 partial per row range of N, then sum the partials in a fixed
  * order (deterministic for a given shape and path), apply the inverse transform and
  * round to `dtype`.  x: [N][Cp*T], dy: [N][Dp*T] read; dw: [Dp][Cp][T] overwritten
