@@ -502,7 +502,7 @@ int eqlinear_bwd_w(const void* x, const void* dy, void* dw, void* workspace, siz
   const int rwaves = reduce_waves(p.real.S * n_real_planes(T) + p.pair.S * (T - n_real_planes(T)), Dp * Cp);
   const int64_t rgrid = ceil_div(Dp * Cp, 256 / rwaves);
   const int64_t fItems = p.fS * p.fDTiles * p.fCTiles;
-  if (p.real.items() > kMaxGrid || p.pair.items() > kMaxGrid || gdy > kMaxGrid || gx > kMaxGrid ||
+  if (p.real.items() > kMaxGrid || p.pair.items() > kMaxGrid || gdy + gx > kMaxGrid ||
       rgrid > kMaxGrid || fItems > kMaxGrid)
     return EQL_EINVAL;
 
@@ -522,6 +522,7 @@ int eqlinear_bwd_w(const void* x, const void* dy, void* dw, void* workspace, siz
     sp.out = ws;
     sp.K = (int)Cp;
     sp.Kpad = (int)p.Cpad;
+    sp.blocks1 = (int)gx;
     hipError_t e = f16 ? launch_spec_f16(T, sp, (unsigned)gx, s) : launch_spec_f32(T, sp, (unsigned)gx, s);
     if (e != hipSuccess) return EQL_EHIP;
     Bwdw4Args a{};
@@ -546,17 +547,17 @@ int eqlinear_bwd_w(const void* x, const void* dy, void* dw, void* workspace, siz
     sp.N = (int)N;
     sp.kgCount = (int)p.kgCount;
     sp.tw = tw;
+    // dy's and x's spectra in one launch: dy's workgroups first, then x's.
     sp.m = dy;
     sp.out = ws;
     sp.K = (int)Dp;
     sp.Kpad = (int)p.Dpad;
-    hipError_t e = f16 ? launch_spec_f16(T, sp, (unsigned)gdy, s) : launch_spec_f32(T, sp, (unsigned)gdy, s);
-    if (e != hipSuccess) return EQL_EHIP;
-    sp.m = x;
-    sp.out = ws + p.dyhBytes;
-    sp.K = (int)Cp;
-    sp.Kpad = (int)p.Cpad;
-    e = f16 ? launch_spec_f16(T, sp, (unsigned)gx, s) : launch_spec_f32(T, sp, (unsigned)gx, s);
+    sp.m2 = x;
+    sp.out2 = ws + p.dyhBytes;
+    sp.K2 = (int)Cp;
+    sp.Kpad2 = (int)p.Cpad;
+    sp.blocks1 = (int)gdy;
+    hipError_t e = f16 ? launch_spec_f16(T, sp, (unsigned)(gdy + gx), s) : launch_spec_f32(T, sp, (unsigned)(gdy + gx), s);
     if (e != hipSuccess) return EQL_EHIP;
 
     for (int pair = 0; pair < 2; ++pair) {

@@ -37,11 +37,16 @@
 
 namespace eql {
 
+// Two matrices of N rows may share one launch: workgroups below `blocks1` transform
+// (m, out, K, Kpad), the others (m2, out2, K2, Kpad2).
 struct SpecArgs {
   const void* m;    // [N][K*T]
   void* out;        // units [kgCount][T][2][Kpad]
   int N, K, Kpad, kgCount;
   Twiddles tw;
+  const void* m2;   // [N][K2*T] or null
+  void* out2;       // units [kgCount][T][2][Kpad2]
+  int K2, Kpad2, blocks1;
 };
 
 // One launch covers either every real plane (PAIR = false: planes 0 .. NR-1) or
@@ -65,10 +70,13 @@ template <int T, typename Elt>
 __global__ void __launch_bounds__(256) eql_spec_kernel(const SpecArgs a) {
   using E = EltT<Elt>;
   constexpr int G = E::kPerUnit;
-  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (size_t)a.kgCount * 2 * a.Kpad) return;
-  const int k = (int)(idx % a.Kpad);
-  const size_t rest = idx / a.Kpad;
+  const bool second = (int)blockIdx.x >= a.blocks1;
+  const Elt* const m = static_cast<const Elt*>(second ? a.m2 : a.m);
+  const int K = second ? a.K2 : a.K, Kpad = second ? a.Kpad2 : a.Kpad;
+  const size_t idx = (size_t)((int)blockIdx.x - (second ? a.blocks1 : 0)) * 256 + threadIdx.x;
+  if (idx >= (size_t)a.kgCount * 2 * Kpad) return;
+  const int k = (int)(idx % Kpad);
+  const size_t rest = idx / Kpad;
   const int half = (int)(rest & 1);
   const int kg = (int)(rest >> 1);
   const int row0 = kg * 2 * G + half * G;
@@ -77,8 +85,8 @@ __global__ void __launch_bounds__(256) eql_spec_kernel(const SpecArgs a) {
   for (int e = 0; e < G; ++e) {
     float v[T], o[T];
     const int row = row0 + e;
-    if (row < a.N && k < a.K) {
-      load_group<T, Elt>(static_cast<const Elt*>(a.m) + ((size_t)row * a.K + k) * T, v);
+    if (row < a.N && k < K) {
+      load_group<T, Elt>(m + ((size_t)row * K + k) * T, v);
     } else {
 #pragma unroll
       for (int h = 0; h < T; ++h) v[h] = 0.0f;
@@ -89,9 +97,9 @@ __global__ void __launch_bounds__(256) eql_spec_kernel(const SpecArgs a) {
   }
   // Non-temporal: the spectra are read back by the GEMMs only after the whole
   // transform, long after they would have left the caches.
-  u32x4* out = static_cast<u32x4*>(a.out) + ((size_t)kg * T * 2 + half) * a.Kpad + k;
+  u32x4* out = static_cast<u32x4*>(second ? a.out2 : a.out) + ((size_t)kg * T * 2 + half) * Kpad + k;
 #pragma unroll
-  for (int p = 0; p < T; ++p) __builtin_nontemporal_store(E::pack(pl[p]), &out[(size_t)p * 2 * a.Kpad]);
+  for (int p = 0; p < T; ++p) __builtin_nontemporal_store(E::pack(pl[p]), &out[(size_t)p * 2 * Kpad]);
 }
 
 template <int T, typename Elt, bool PAIR, int DB, int CB, int WCN>
