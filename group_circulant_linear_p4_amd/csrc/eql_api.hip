@@ -220,14 +220,30 @@ int bwdw_waves() {
 }
 
 constexpr int64_t kMinStepsPerSplit = 16;  // keeps partial-spectrum traffic small
+// Small layers may split down to kMinStepsSmall k-steps per row range while their
+// partials stay within kSmallPartialBytes: few outputs and few rows would otherwise
+// leave a handful of workgroups each walking a long serial chain of stages.
+constexpr int64_t kMinStepsSmall = 2;
+constexpr int64_t kSmallPartialBytes = 1 << 20;
 
-// Row ranges (k-step ranges) of one GEMM launch: enough to give every compute unit
-// one item.
-void plan_splits(GemmPlan& g, int64_t kgCount) {
+// Row ranges of a reduction over kgCount k-steps for `tiles` output items whose
+// partials take partBytesPerSplit bytes per range: enough ranges to give every compute
+// unit one item.
+int64_t split_count(int64_t tiles, int64_t kgCount, int64_t partBytesPerSplit) {
+  const int64_t want = tiles >= kTargetWorkgroups ? 1 : kTargetWorkgroups / tiles;
+  int64_t S = std::min<int64_t>(want, std::max<int64_t>(1, kgCount / kMinStepsPerSplit));
+  if (S < want) {
+    const int64_t S2 = std::min<int64_t>(want, std::max<int64_t>(1, kgCount / kMinStepsSmall));
+    if (S2 * partBytesPerSplit <= kSmallPartialBytes) S = S2;
+  }
+  return S;
+}
+
+// Row ranges (k-step ranges) of one GEMM launch.
+void plan_splits(GemmPlan& g, int64_t kgCount, int64_t partBytesPerSplit) {
   const int64_t tiles = g.groups * g.dTiles * g.cTiles;
   if (tiles == 0 || kgCount == 0) return;
-  int64_t S = tiles >= kTargetWorkgroups ? 1 : kTargetWorkgroups / tiles;
-  S = std::min<int64_t>(S, std::max<int64_t>(1, kgCount / kMinStepsPerSplit));
+  const int64_t S = split_count(tiles, kgCount, partBytesPerSplit);
   g.kgPerSplit = ceil_div(kgCount, S);
   g.S = ceil_div(kgCount, g.kgPerSplit);
 }
@@ -277,8 +293,7 @@ BwdwPlan plan_bwdw(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype) {
     p.fCTiles = ceil_div(Cp, 32 * p.fNB);
     p.Cpad = p.fCTiles * 32 * p.fNB;
     const int64_t tiles = p.fDTiles * p.fCTiles;
-    int64_t S = std::max<int64_t>(1, kTargetWorkgroups / tiles);
-    S = std::min<int64_t>(S, std::max<int64_t>(1, p.kgCount / kMinStepsPerSplit));
+    const int64_t S = split_count(tiles, p.kgCount, (int64_t)T * Dp * Cp * (int64_t)sizeof(float));
     p.fKgPerSplit = ceil_div(p.kgCount, S);
     p.fS = ceil_div(p.kgCount, p.fKgPerSplit);
     p.real.S = p.pair.S = p.fS;
@@ -287,8 +302,8 @@ BwdwPlan plan_bwdw(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype) {
     p.partPBytes = (size_t)p.fS * (T - nr) * (size_t)Dp * (size_t)Cp * sizeof(float);
     return p;
   }
-  plan_splits(p.real, p.kgCount);
-  plan_splits(p.pair, p.kgCount);
+  plan_splits(p.real, p.kgCount, (int64_t)nr * Dp * Cp * (int64_t)sizeof(float));
+  plan_splits(p.pair, p.kgCount, (int64_t)(T - nr) * Dp * Cp * (int64_t)sizeof(float));
   p.dyhBytes = align256((size_t)p.kgCount * T * 2 * (size_t)p.Dpad * 16);
   p.xhBytes = align256((size_t)p.kgCount * T * 2 * (size_t)p.Cpad * 16);
   p.partRBytes = align256((size_t)p.real.S * nr * (size_t)Dp * (size_t)Cp * sizeof(float));
