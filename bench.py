@@ -41,6 +41,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c5", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--step", default="plain", choices=["train", "plain"],
+                    help="train: eqlinear_fwd_train / eqlinear_bwd_x_train / eqlinear_bwd_w_train (the "
+                         "forward and the input gradient leave the spectra in the weight-gradient workspace); "
+                         "plain: eqlinear_fwd / eqlinear_bwd_x / eqlinear_bwd_w")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true", help="skip timing the unrolled dense GEMM comparator")
     ap.add_argument("--no-graph", action="store_true",
@@ -135,13 +139,23 @@ def main():
     sptr = stream.cuda_stream
 
     def make_calls(sp, b=s0):
-        return {
+        calls = {
             "pack": lambda: (eql.eqlinear_pack_weight(b["w"], b["wp"], Dp, Cp, T, code, eql.EQL_PACK_FWD, sp),
                              eql.eqlinear_pack_weight(b["w"], b["wpb"], Dp, Cp, T, code, eql.EQL_PACK_BWDX, sp)),
-            "fwd": lambda: eql.eqlinear_fwd(b["x"], b["wp"], b["y"], N, Cp, Dp, T, code, sp),
-            "bwd_x": lambda: eql.eqlinear_bwd_x(b["dy"], b["wpb"], b["dx"], N, Cp, Dp, T, code, sp),
-            "bwd_w": lambda: eql.eqlinear_bwd_w(b["x"], b["dy"], b["dw"], b["ws"], ws_bytes, N, Cp, Dp, T, code, sp),
         }
+        if args.step == "train":
+            calls["fwd"] = lambda: eql.eqlinear_fwd_train(b["x"], b["wp"], b["y"], b["ws"], ws_bytes, N, Cp, Dp, T,
+                                                          code, sp)
+            calls["bwd_x"] = lambda: eql.eqlinear_bwd_x_train(b["dy"], b["wpb"], b["dx"], b["ws"], ws_bytes, N, Cp,
+                                                              Dp, T, code, sp)
+            calls["bwd_w"] = lambda: eql.eqlinear_bwd_w_train(b["dy"], b["dw"], b["ws"], ws_bytes, N, Cp, Dp, T,
+                                                              code, sp)
+        else:
+            calls["fwd"] = lambda: eql.eqlinear_fwd(b["x"], b["wp"], b["y"], N, Cp, Dp, T, code, sp)
+            calls["bwd_x"] = lambda: eql.eqlinear_bwd_x(b["dy"], b["wpb"], b["dx"], N, Cp, Dp, T, code, sp)
+            calls["bwd_w"] = lambda: eql.eqlinear_bwd_w(b["x"], b["dy"], b["dw"], b["ws"], ws_bytes, N, Cp, Dp, T,
+                                                        code, sp)
+        return calls
 
     set_calls = [make_calls(sptr, b) for b in sets]
     order = ["pack", "fwd", "bwd_x", "bwd_w"]
@@ -303,7 +317,8 @@ def main():
         "data": "synthetic (seeded; x,dy ~ N(0,1), w ~ N(0,1/C)%s)" % (
             ", %g%% of rows x%g" % (100 * wl.hot_rows_frac, wl.hot_rows_scale) if wl.hot_rows_frac else ""),
         "config": {"workload": wl.name, "T": T, "N": N, "C": Cp * T, "D": Dp * T,
-                   "step": "pack(fwd)+pack(bwd_x)+fwd+bwd_x+bwd_w", "buffer_sets": n_sets,
+                   "step": ("pack(fwd)+pack(bwd_x)+fwd_train+bwd_x_train+bwd_w_train" if args.step == "train"
+                            else "pack(fwd)+pack(bwd_x)+fwd+bwd_x+bwd_w"), "buffer_sets": n_sets,
                    "set_mib": round(set_bytes / 2**20, 1)},
         "warm": warm,
         "passes": passes,

@@ -26,6 +26,7 @@ __all__ = [
     "eqlinear_fused_epilogue_bwd_workspace_bytes", "eqlinear_fused_epilogue_bwd",
     "eqlinear_fused_epilogue_bwd_noalloc", "EQL_NOALLOC_SCRATCH_BYTES",
     "eqlinear_bwd_w_workspace_bytes", "eqlinear_bwd_w",
+    "eqlinear_fwd_train", "eqlinear_bwd_x_train", "eqlinear_bwd_w_train",
     "eqlinear_p4m_expand_weight", "eqlinear_p4m_fold_weight_grad",
 ]
 
@@ -87,6 +88,11 @@ def lib() -> ctypes.CDLL:
         L.eqlinear_bwd_w_workspace_bytes.restype = sz
         L.eqlinear_bwd_w.argtypes = [vp, vp, vp, vp, sz, i64, i64, i64, i32, i32, vp]
         L.eqlinear_bwd_w.restype = i32
+        for name in ("eqlinear_fwd_train", "eqlinear_bwd_x_train"):
+            getattr(L, name).argtypes = [vp, vp, vp, vp, sz, i64, i64, i64, i32, i32, vp]
+            getattr(L, name).restype = i32
+        L.eqlinear_bwd_w_train.argtypes = [vp, vp, vp, sz, i64, i64, i64, i32, i32, vp]
+        L.eqlinear_bwd_w_train.restype = i32
         _lib = L
     return _lib
 
@@ -194,6 +200,27 @@ def eqlinear_bwd_w(x, dy, dw, workspace, ws_bytes: int, N: int, Cp: int, Dp: int
                    stream=None) -> None:
     _check(lib().eqlinear_bwd_w(_ptr(x), _ptr(dy), _ptr(dw), _ptr(workspace), ws_bytes, N, Cp, Dp, T,
                                 _dtype(dtype), _stream(stream)), "eqlinear_bwd_w")
+
+
+def eqlinear_fwd_train(x, w_packed, y, workspace, ws_bytes: int, N: int, Cp: int, Dp: int, T: int, dtype,
+                       stream=None) -> None:
+    """eqlinear_fwd that also leaves x's half spectrum in the weight-gradient workspace."""
+    _check(lib().eqlinear_fwd_train(_ptr(x), _ptr(w_packed), _ptr(y), _ptr(workspace), ws_bytes, N, Cp, Dp, T,
+                                    _dtype(dtype), _stream(stream)), "eqlinear_fwd_train")
+
+
+def eqlinear_bwd_x_train(dy, w_packed_bwdx, dx, workspace, ws_bytes: int, N: int, Cp: int, Dp: int, T: int, dtype,
+                         stream=None) -> None:
+    """eqlinear_bwd_x that also leaves dy's half spectrum in the workspace (separate path)."""
+    _check(lib().eqlinear_bwd_x_train(_ptr(dy), _ptr(w_packed_bwdx), _ptr(dx), _ptr(workspace), ws_bytes, N, Cp,
+                                      Dp, T, _dtype(dtype), _stream(stream)), "eqlinear_bwd_x_train")
+
+
+def eqlinear_bwd_w_train(dy, dw, workspace, ws_bytes: int, N: int, Cp: int, Dp: int, T: int, dtype,
+                         stream=None) -> None:
+    """Weight gradient from the spectra the two calls above left in the workspace."""
+    _check(lib().eqlinear_bwd_w_train(_ptr(dy), _ptr(dw), _ptr(workspace), ws_bytes, N, Cp, Dp, T, _dtype(dtype),
+                                      _stream(stream)), "eqlinear_bwd_w_train")
 
 
 def eqlinear_p4m_expand_weight(w, w_c4, Dp: int, Cp: int, dtype, stream=None) -> None:

@@ -31,6 +31,7 @@ SOURCES = [
     "eql_fwd_f32.hip",
     "eql_fwd_fused_f16.hip",
     "eql_fwd_fused_f32.hip",
+    "eql_fwd_spec.hip",
     "eql_bwdw_f16.hip",
     "eql_bwdw_f32.hip",
     "eql_bwdw_real_f16.hip",

@@ -82,9 +82,44 @@ int device_cus() {
 // Shared by the forward pass and the input gradient: out = in * W^T for the packed
 // weight with (out, in) channel counts (Dout, Cin).
 // epi: the fused epilogue (bias, act, res); otherwise those are ignored.
+// Relative cost of a forward tile that also stores its transformed input (the stores
+// and the transposes), in percent of a plain tile's; EQL_SPEC_COST overrides it (for
+// measurement).
+int spec_cost_pct() {
+  static const int v = [] {
+    const char* e = std::getenv("EQL_SPEC_COST");
+    const int p = e ? std::atoi(e) : 0;
+    return p >= 50 && p <= 400 ? p : 175;
+  }();
+  return v;
+}
+
+// Workgroups of the spectrum-storing forward launch that take column 0's row tiles: a
+// multiple of 8 (one per XCD each), so that both parts keep the XCD-aware tile order,
+// chosen to balance rounds of column-0 tiles (weighted by spec_cost_pct) against rounds
+// of the other columns on the remaining compute units.
+int spec_grid(int64_t rowTiles, int64_t colTiles, int cus) {
+  const int64_t plain = rowTiles * (colTiles - 1);
+  const int maxGs = std::max(8, cus / 8 * 8);
+  if (plain == 0) return (int)std::min<int64_t>(ceil_div(rowTiles, 8) * 8, maxGs);
+  int best = 8;
+  int64_t bestCost = -1;
+  for (int gs = 8; gs < maxGs; gs += 8) {
+    const int gp = cus - gs;
+    const int64_t cost = std::max(ceil_div(rowTiles, gs) * spec_cost_pct(), ceil_div(plain, gp) * 100);
+    if (bestCost < 0 || cost < bestCost) {
+      bestCost = cost;
+      best = gs;
+    }
+  }
+  return best;
+}
+
+// spec: also store the transformed input as weight-gradient operand units into this
+// section of specBytes bytes, channel axis padded to specKpad (fwd_spec_ok must hold).
 int run_fwd(const void* x, const void* wp, void* y, int64_t N, int64_t Cin, int64_t Dout, int T,
             int dtype, void* stream, bool epi = false, const void* bias = nullptr, const void* res = nullptr,
-            int act = 0, void* pre = nullptr) {
+            int act = 0, void* pre = nullptr, void* spec = nullptr, int64_t specKpad = 0, size_t specBytes = 0) {
   int st = check_sizes(N, Cin, Dout, T, dtype);
   if (st != EQL_OK) return st;
   if (N == 0) return EQL_OK;
@@ -139,13 +174,28 @@ int run_fwd(const void* x, const void* wp, void* y, int64_t N, int64_t Cin, int6
     a.y = static_cast<char*>(y) + (size_t)r0 * outRow;
     a.res = res ? static_cast<const char*>(res) + (size_t)r0 * outRow : nullptr;
     a.pre = pre ? static_cast<char*>(pre) + (size_t)r0 * outRow : nullptr;
+    if (spec) {
+      // r0 is a multiple of the row tile, so of the 16 rows of one k-step.
+      const size_t skip = (size_t)(r0 / 16) * (size_t)T * 2 * (size_t)specKpad * 16;
+      a.spec = static_cast<char*>(spec) + skip;
+      a.specBytes = (uint32_t)(specBytes - skip);
+      a.specKpad = (int)specKpad;
+    }
     a.N = (int)rows;
-    a.numTiles = (int)(ceil_div(rows, kFwdRows) * colTiles);
-    const unsigned grid = (unsigned)std::min<int64_t>(a.numTiles, cus);
-    const hipError_t e = epi ? (dtype == EQL_F16 ? launch_fwd_fused_f16(T, nb, a, grid, s)
-                                                 : launch_fwd_fused_f32(T, nb, a, grid, s))
-                             : (dtype == EQL_F16 ? launch_fwd_f16(T, nb, a, grid, s)
-                                                 : launch_fwd_f32(T, nb, a, grid, s));
+    const int64_t rowTiles = ceil_div(rows, kFwdRows);
+    a.numTiles = (int)(rowTiles * colTiles);
+    hipError_t e;
+    if (spec) {
+      const int gs = spec_grid(rowTiles, colTiles, cus);
+      a.specGrid = gs;
+      const int64_t plain = rowTiles * (colTiles - 1);
+      const unsigned grid = (unsigned)(gs + std::min<int64_t>(plain, std::max(cus - gs, 8)));
+      e = launch_fwd_spec_f16(nb, a, grid, s);
+    } else {
+      const unsigned grid = (unsigned)std::min<int64_t>(a.numTiles, cus);
+      e = epi ? (dtype == EQL_F16 ? launch_fwd_fused_f16(T, nb, a, grid, s) : launch_fwd_fused_f32(T, nb, a, grid, s))
+              : (dtype == EQL_F16 ? launch_fwd_f16(T, nb, a, grid, s) : launch_fwd_f32(T, nb, a, grid, s));
+    }
     if (e != hipSuccess) return EQL_EHIP;
   }
   return EQL_OK;
@@ -311,6 +361,35 @@ BwdwPlan plan_bwdw(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype) {
   return p;
 }
 
+// Whether the forward kernel itself can store the transformed input (Cin channels)
+// as weight-gradient operand units into a section of `bytes` bytes with the channel
+// axis padded to Kpad: p4 fp16 with 16-byte rows (the ring kernel), and the section
+// plus the last row tile's overhang (at most 8 k-steps past it) within 31-bit
+// offsets.
+bool fwd_spec_ok(int64_t Cin, int T, int dtype, size_t bytes, int64_t Kpad) {
+  if (T != 4 || dtype != EQL_F16 || (Cin * T * elt_bytes(dtype)) % 16 != 0) return false;
+  return (double)bytes + 8.0 * T * 2 * (double)Kpad * 16 < 2147483648.0;
+}
+
+// The group transform of one N x K matrix (x or dy) into operand units [kg][T][2][Kpad]
+// by eql_spec_kernel.
+int run_spec(const void* m, void* out, int64_t N, int64_t K, int64_t Kpad, int64_t kgCount, int T, int dtype,
+             hipStream_t s) {
+  const int64_t grid = ceil_div(kgCount * 2 * Kpad, 256);
+  if (grid > kMaxGrid) return EQL_EINVAL;
+  SpecArgs sp{};
+  sp.N = (int)N;
+  sp.kgCount = (int)kgCount;
+  sp.tw = make_twiddles(T);
+  sp.m = m;
+  sp.out = out;
+  sp.K = (int)K;
+  sp.Kpad = (int)Kpad;
+  sp.blocks1 = (int)grid;
+  return status_of(dtype == EQL_F16 ? launch_spec_f16(T, sp, (unsigned)grid, s)
+                                    : launch_spec_f32(T, sp, (unsigned)grid, s));
+}
+
 // Launch shape of the epilogue backward: chunk width W (the widest power of two, up
 // to 16 bytes, dividing a row), 64 chunks across per workgroup, and rows per
 // workgroup halved from 1024 (down to 16) until the grid has 2048 workgroups (eight
@@ -408,11 +487,120 @@ int epilogue_bwd(const void* dy, const void* pre, void* dpre, void* dbias, void*
   return EQL_OK;
 }
 
+// Body of the weight-gradient entry points.  spectra: the workspace already holds x's
+// spectrum and, on the separate path, dy's (written by the training forward and
+// input gradient); only the GEMMs and the reduce run, and x is not read.
+int run_bwdw(const void* x, const void* dy, void* dw, void* workspace, size_t ws_bytes, int64_t N, int64_t Cp,
+             int64_t Dp, int T, int dtype, void* stream, bool spectra) {
+  int st = check_sizes(N, Cp, Dp, T, dtype);
+  if (st != EQL_OK) return st;
+  const BwdwPlan p = plan_bwdw(N, Cp, Dp, T, dtype);
+  const bool needX = !spectra, needDy = !spectra || p.fused;
+  if (!dw || (N > 0 && ((needX && !x) || (needDy && !dy) || !workspace))) return EQL_EINVAL;
+  if (ws_bytes < p.total()) return EQL_EINVAL;
+  if (!aligned16(dw) || (N > 0 && ((needX && !aligned16(x)) || (needDy && !aligned16(dy)) || !aligned16(workspace))))
+    return EQL_EALIGN;
+  const int64_t gdy = ceil_div(p.kgCount * 2 * p.Dpad, 256);
+  const int64_t gx = ceil_div(p.kgCount * 2 * p.Cpad, 256);
+  const int rwaves = reduce_waves(p.real.S * n_real_planes(T) + p.pair.S * (T - n_real_planes(T)), Dp * Cp);
+  const int64_t rgrid = ceil_div(Dp * Cp, 256 / rwaves);
+  const int64_t fItems = p.fS * p.fDTiles * p.fCTiles;
+  if (p.real.items() > kMaxGrid || p.pair.items() > kMaxGrid || gdy + gx > kMaxGrid ||
+      rgrid > kMaxGrid || fItems > kMaxGrid)
+    return EQL_EINVAL;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Twiddles tw = make_twiddles(T);
+  char* ws = static_cast<char*>(workspace);
+  float* partR = reinterpret_cast<float*>(ws + p.dyhBytes + p.xhBytes);
+  float* partP = reinterpret_cast<float*>(ws + p.dyhBytes + p.xhBytes + p.partRBytes);
+  const bool f16 = dtype == EQL_F16;
+  if (N > 0 && p.fused) {
+    // x's spectrum only; dy is transformed inside the GEMM.
+    if (!spectra) {
+      st = run_spec(x, ws, N, Cp, p.Cpad, p.kgCount, T, dtype, s);
+      if (st != EQL_OK) return st;
+    }
+    Bwdw4Args a{};
+    a.dy = dy;
+    a.xh = ws;
+    a.wsR = partR;
+    a.wsP = partP;
+    a.N = (int)N;
+    a.Dp = (int)Dp;
+    a.Cp = (int)Cp;
+    a.Cpad = (int)p.Cpad;
+    a.kgCount = (int)p.kgCount;
+    a.kgPerSplit = (int)p.fKgPerSplit;
+    a.dTiles = (int)p.fDTiles;
+    a.cTiles = (int)p.fCTiles;
+    a.numItems = (int)fItems;
+    a.tw = tw;
+    if (launch_bwdw4(f16, T, p.fNB, a, (unsigned)fItems, s) != hipSuccess) return EQL_EHIP;
+  } else if (N > 0) {
+    hipError_t e = hipSuccess;
+    if (!spectra) {
+      // dy's and x's spectra in one launch: dy's workgroups first, then x's.
+      SpecArgs sp{};
+      sp.N = (int)N;
+      sp.kgCount = (int)p.kgCount;
+      sp.tw = tw;
+      sp.m = dy;
+      sp.out = ws;
+      sp.K = (int)Dp;
+      sp.Kpad = (int)p.Dpad;
+      sp.m2 = x;
+      sp.out2 = ws + p.dyhBytes;
+      sp.K2 = (int)Cp;
+      sp.Kpad2 = (int)p.Cpad;
+      sp.blocks1 = (int)gdy;
+      e = f16 ? launch_spec_f16(T, sp, (unsigned)(gdy + gx), s) : launch_spec_f32(T, sp, (unsigned)(gdy + gx), s);
+      if (e != hipSuccess) return EQL_EHIP;
+    }
+    for (int pair = 0; pair < 2; ++pair) {
+      const GemmPlan& g = pair ? p.pair : p.real;
+      if (g.items() == 0) continue;
+      BwdwArgs a{};
+      a.dyh = ws;
+      a.xh = ws + p.dyhBytes;
+      a.ws = pair ? partP : partR;
+      a.Dp = (int)Dp;
+      a.Cp = (int)Cp;
+      a.Dpad = (int)p.Dpad;
+      a.Cpad = (int)p.Cpad;
+      a.kgCount = (int)p.kgCount;
+      a.kgPerSplit = (int)g.kgPerSplit;
+      a.groups = (int)g.groups;
+      a.dTiles = (int)g.dTiles;
+      a.cTiles = (int)g.cTiles;
+      a.numItems = (int)g.items();
+      if (pair)
+        e = f16 ? launch_bwdw_pair_f16(T, g.DB, g.CB, g.WCN, a, (unsigned)a.numItems, s)
+                : launch_bwdw_pair_f32(T, g.DB, g.CB, g.WCN, a, (unsigned)a.numItems, s);
+      else
+        e = f16 ? launch_bwdw_real_f16(T, g.DB, g.CB, g.WCN, a, (unsigned)a.numItems, s)
+                : launch_bwdw_real_f32(T, g.DB, g.CB, g.WCN, a, (unsigned)a.numItems, s);
+      if (e != hipSuccess) return EQL_EHIP;
+    }
+  }
+  BwdwReduceArgs r{};
+  r.wsR = partR;
+  r.wsP = partP;
+  r.dw = dw;
+  r.SR = (int)p.real.S;
+  r.SP = (int)p.pair.S;
+  r.Dp = (int)Dp;
+  r.Cp = (int)Cp;
+  r.tw = tw;
+  return status_of(f16 ? launch_bwdw_reduce_f16(T, rwaves, r, (unsigned)rgrid, s)
+                       : launch_bwdw_reduce_f32(T, rwaves, r, (unsigned)rgrid, s));
+}
+
 }  // namespace
 
 extern "C" {
 
-int eqlinear_abi_version(void) { return 202; }
+int eqlinear_abi_version(void) { return 203; }
 
 const char* eqlinear_status_string(int status) {
   switch (status) {
@@ -505,115 +693,48 @@ size_t eqlinear_bwd_w_workspace_bytes(int64_t N, int64_t Cp, int64_t Dp, int T, 
 
 int eqlinear_bwd_w(const void* x, const void* dy, void* dw, void* workspace, size_t ws_bytes,
                    int64_t N, int64_t Cp, int64_t Dp, int T, int dtype, void* stream) {
-  int st = check_sizes(N, Cp, Dp, T, dtype);
-  if (st != EQL_OK) return st;
-  const BwdwPlan p = plan_bwdw(N, Cp, Dp, T, dtype);
-  if (!dw || (N > 0 && (!x || !dy || !workspace))) return EQL_EINVAL;
-  if (ws_bytes < p.total()) return EQL_EINVAL;
-  if (!aligned16(dw) || (N > 0 && (!aligned16(x) || !aligned16(dy) || !aligned16(workspace))))
-    return EQL_EALIGN;
-  const int64_t gdy = ceil_div(p.kgCount * 2 * p.Dpad, 256);
-  const int64_t gx = ceil_div(p.kgCount * 2 * p.Cpad, 256);
-  const int rwaves = reduce_waves(p.real.S * n_real_planes(T) + p.pair.S * (T - n_real_planes(T)), Dp * Cp);
-  const int64_t rgrid = ceil_div(Dp * Cp, 256 / rwaves);
-  const int64_t fItems = p.fS * p.fDTiles * p.fCTiles;
-  if (p.real.items() > kMaxGrid || p.pair.items() > kMaxGrid || gdy + gx > kMaxGrid ||
-      rgrid > kMaxGrid || fItems > kMaxGrid)
-    return EQL_EINVAL;
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const Twiddles tw = make_twiddles(T);
-  char* ws = static_cast<char*>(workspace);
-  float* partR = reinterpret_cast<float*>(ws + p.dyhBytes + p.xhBytes);
-  float* partP = reinterpret_cast<float*>(ws + p.dyhBytes + p.xhBytes + p.partRBytes);
-  const bool f16 = dtype == EQL_F16;
-  if (N > 0 && p.fused) {
-    // x's spectrum only; dy is transformed inside the GEMM.
-    SpecArgs sp{};
-    sp.N = (int)N;
-    sp.kgCount = (int)p.kgCount;
-    sp.tw = tw;
-    sp.m = x;
-    sp.out = ws;
-    sp.K = (int)Cp;
-    sp.Kpad = (int)p.Cpad;
-    sp.blocks1 = (int)gx;
-    hipError_t e = f16 ? launch_spec_f16(T, sp, (unsigned)gx, s) : launch_spec_f32(T, sp, (unsigned)gx, s);
-    if (e != hipSuccess) return EQL_EHIP;
-    Bwdw4Args a{};
-    a.dy = dy;
-    a.xh = ws;
-    a.wsR = partR;
-    a.wsP = partP;
-    a.N = (int)N;
-    a.Dp = (int)Dp;
-    a.Cp = (int)Cp;
-    a.Cpad = (int)p.Cpad;
-    a.kgCount = (int)p.kgCount;
-    a.kgPerSplit = (int)p.fKgPerSplit;
-    a.dTiles = (int)p.fDTiles;
-    a.cTiles = (int)p.fCTiles;
-    a.numItems = (int)fItems;
-    a.tw = tw;
-    e = launch_bwdw4(f16, T, p.fNB, a, (unsigned)fItems, s);
-    if (e != hipSuccess) return EQL_EHIP;
-  } else if (N > 0) {
-    SpecArgs sp{};
-    sp.N = (int)N;
-    sp.kgCount = (int)p.kgCount;
-    sp.tw = tw;
-    // dy's and x's spectra in one launch: dy's workgroups first, then x's.
-    sp.m = dy;
-    sp.out = ws;
-    sp.K = (int)Dp;
-    sp.Kpad = (int)p.Dpad;
-    sp.m2 = x;
-    sp.out2 = ws + p.dyhBytes;
-    sp.K2 = (int)Cp;
-    sp.Kpad2 = (int)p.Cpad;
-    sp.blocks1 = (int)gdy;
-    hipError_t e = f16 ? launch_spec_f16(T, sp, (unsigned)(gdy + gx), s) : launch_spec_f32(T, sp, (unsigned)(gdy + gx), s);
-    if (e != hipSuccess) return EQL_EHIP;
-
-    for (int pair = 0; pair < 2; ++pair) {
-      const GemmPlan& g = pair ? p.pair : p.real;
-      if (g.items() == 0) continue;
-      BwdwArgs a{};
-      a.dyh = ws;
-      a.xh = ws + p.dyhBytes;
-      a.ws = pair ? partP : partR;
-      a.Dp = (int)Dp;
-      a.Cp = (int)Cp;
-      a.Dpad = (int)p.Dpad;
-      a.Cpad = (int)p.Cpad;
-      a.kgCount = (int)p.kgCount;
-      a.kgPerSplit = (int)g.kgPerSplit;
-      a.groups = (int)g.groups;
-      a.dTiles = (int)g.dTiles;
-      a.cTiles = (int)g.cTiles;
-      a.numItems = (int)g.items();
-      if (pair)
-        e = f16 ? launch_bwdw_pair_f16(T, g.DB, g.CB, g.WCN, a, (unsigned)a.numItems, s)
-                : launch_bwdw_pair_f32(T, g.DB, g.CB, g.WCN, a, (unsigned)a.numItems, s);
-      else
-        e = f16 ? launch_bwdw_real_f16(T, g.DB, g.CB, g.WCN, a, (unsigned)a.numItems, s)
-                : launch_bwdw_real_f32(T, g.DB, g.CB, g.WCN, a, (unsigned)a.numItems, s);
-      if (e != hipSuccess) return EQL_EHIP;
-    }
-  }
-  BwdwReduceArgs r{};
-  r.wsR = partR;
-  r.wsP = partP;
-  r.dw = dw;
-  r.SR = (int)p.real.S;
-  r.SP = (int)p.pair.S;
-  r.Dp = (int)Dp;
-  r.Cp = (int)Cp;
-  r.tw = tw;
-  return status_of(f16 ? launch_bwdw_reduce_f16(T, rwaves, r, (unsigned)rgrid, s)
-                       : launch_bwdw_reduce_f32(T, rwaves, r, (unsigned)rgrid, s));
+  return run_bwdw(x, dy, dw, workspace, ws_bytes, N, Cp, Dp, T, dtype, stream, false);
 }
 
+int eqlinear_fwd_train(const void* x, const void* w_packed, void* y, void* workspace, size_t ws_bytes,
+                       int64_t N, int64_t Cp, int64_t Dp, int T, int dtype, void* stream) {
+  int st = check_sizes(N, Cp, Dp, T, dtype);
+  if (st != EQL_OK) return st;
+  if (N == 0) return EQL_OK;
+  const BwdwPlan p = plan_bwdw(N, Cp, Dp, T, dtype);
+  if (!workspace || ws_bytes < p.total()) return EQL_EINVAL;
+  if (!aligned16(workspace)) return EQL_EALIGN;
+  void* xh = static_cast<char*>(workspace) + p.dyhBytes;
+  if (fwd_spec_ok(Cp, T, dtype, p.xhBytes, p.Cpad))
+    return run_fwd(x, w_packed, y, N, Cp, Dp, T, dtype, stream, false, nullptr, nullptr, 0, nullptr, xh, p.Cpad,
+                   p.xhBytes);
+  st = run_fwd(x, w_packed, y, N, Cp, Dp, T, dtype, stream);
+  if (st != EQL_OK) return st;
+  return run_spec(x, xh, N, Cp, p.Cpad, p.kgCount, T, dtype, static_cast<hipStream_t>(stream));
+}
+
+int eqlinear_bwd_x_train(const void* dy, const void* w_packed_bwdx, void* dx, void* workspace, size_t ws_bytes,
+                         int64_t N, int64_t Cp, int64_t Dp, int T, int dtype, void* stream) {
+  int st = check_sizes(N, Cp, Dp, T, dtype);
+  if (st != EQL_OK) return st;
+  if (N == 0) return EQL_OK;
+  const BwdwPlan p = plan_bwdw(N, Cp, Dp, T, dtype);
+  if (!workspace || ws_bytes < p.total()) return EQL_EINVAL;
+  if (!aligned16(workspace)) return EQL_EALIGN;
+  // The fused weight-gradient path reads dy itself: nothing to keep.
+  if (p.fused) return run_fwd(dy, w_packed_bwdx, dx, N, Dp, Cp, T, dtype, stream);
+  if (fwd_spec_ok(Dp, T, dtype, p.dyhBytes, p.Dpad))
+    return run_fwd(dy, w_packed_bwdx, dx, N, Dp, Cp, T, dtype, stream, false, nullptr, nullptr, 0, nullptr,
+                   workspace, p.Dpad, p.dyhBytes);
+  st = run_fwd(dy, w_packed_bwdx, dx, N, Dp, Cp, T, dtype, stream);
+  if (st != EQL_OK) return st;
+  return run_spec(dy, workspace, N, Dp, p.Dpad, p.kgCount, T, dtype, static_cast<hipStream_t>(stream));
+}
+
+int eqlinear_bwd_w_train(const void* dy, void* dw, void* workspace, size_t ws_bytes, int64_t N, int64_t Cp,
+                         int64_t Dp, int T, int dtype, void* stream) {
+  return run_bwdw(nullptr, dy, dw, workspace, ws_bytes, N, Cp, Dp, T, dtype, stream, true);
+}
 
 // p4m (dihedral D4) through the C_4 layer on 2C' x 2D' channels (eql_p4m.h).
 static int p4m_map(const void* src, void* dst, int64_t Dp, int64_t Cp, int dtype, void* stream, bool expand) {

@@ -53,6 +53,15 @@ struct FwdArgs {
   const void* res;   // [N][Dout*T] or null (may equal y)
   void* pre;         // [N][Dout*T] or null: receives x W^T + bias (the activation's input)
   int act;           // 0 none, 1 GELU
+  // Spectrum side output (eql_fwd4_kernel with SPEC = 1): the tiles of output column 0
+  // also store the transformed input as weight-gradient operand units, unit
+  // (kg, p, half, k) = plane p of input channel k for rows 16 kg + 8 half .. +7, at
+  // byte ((kg T + p) 2 + half) specKpad 16 + 16 k; stores at or past specBytes are
+  // dropped.
+  void* spec;
+  uint32_t specBytes;
+  int specKpad;
+  int specGrid;      // workgroups that take column 0's tiles (a multiple of 8)
 };
 
 constexpr int kFwdRows = 128;   // rows per workgroup (4 waves x 32)
@@ -88,6 +97,41 @@ __device__ __forceinline__ void dft_p4_f16(const uint32_t (&raw)[16], u32x4 (&ou
     out[3][q] = nxi ^ 0x80008000u;
     out[4][q] = nxi;
   }
+}
+
+// Transposes, in each aligned group of 8 lanes, the 8 x 8 block of 16-bit values
+// held as four words per lane: on entry lane j holds row j (word q = elements 2q and
+// 2q+1), on return column j (word q = rows 2q and 2q+1).  Three exchange rounds by
+// DPP: lanes j and j^4 swap 4 x 4 blocks (row shifts by 4 lanes, each written only to
+// the banks of 4 lanes that receive it), then inside each quad lanes r and r^2 swap
+// 2 x 2 blocks and lanes r and r^1 swap 16-bit halves.  hi2: bit 1 of the lane index;
+// sel: the last round's byte selector (0x05040100 on even lanes, 0x03020706 on odd).
+__device__ __forceinline__ u32x4 transpose8_b16(const u32x4& v, bool hi2, uint32_t sel) {
+  // Lanes 4-7 of each group take words 2, 3 of lane j-4 as their words 0, 1; lanes
+  // 0-3 take words 0, 1 of lane j+4 as their words 2, 3.
+  const uint32_t n0 = (uint32_t)__builtin_amdgcn_update_dpp((int)v[0], (int)v[2], 0x114, 0xf, 0xa, false);
+  const uint32_t n1 = (uint32_t)__builtin_amdgcn_update_dpp((int)v[1], (int)v[3], 0x114, 0xf, 0xa, false);
+  const uint32_t n2 = (uint32_t)__builtin_amdgcn_update_dpp((int)v[2], (int)v[0], 0x104, 0xf, 0x5, false);
+  const uint32_t n3 = (uint32_t)__builtin_amdgcn_update_dpp((int)v[3], (int)v[1], 0x104, 0xf, 0x5, false);
+  // A 4 x 4 block of one quad, lane r holding row r as words (a, b).
+  auto quad = [&](uint32_t a, uint32_t b, uint32_t& oa, uint32_t& ob) __attribute__((always_inline)) {
+    const uint32_t pa = (uint32_t)__builtin_amdgcn_mov_dpp((int)a, 0x4E, 0xf, 0xf, false);  // lane r^2
+    const uint32_t pb = (uint32_t)__builtin_amdgcn_mov_dpp((int)b, 0x4E, 0xf, 0xf, false);
+    const uint32_t a2 = hi2 ? pb : a, b2 = hi2 ? b : pa;
+    const uint32_t qa = (uint32_t)__builtin_amdgcn_mov_dpp((int)a2, 0xB1, 0xf, 0xf, false);  // lane r^1
+    const uint32_t qb = (uint32_t)__builtin_amdgcn_mov_dpp((int)b2, 0xB1, 0xf, 0xf, false);
+    oa = __builtin_amdgcn_perm(qa, a2, sel);
+    ob = __builtin_amdgcn_perm(qb, b2, sel);
+  };
+  u32x4 o;
+  uint32_t o0, o1, o2, o3;
+  quad(n0, n1, o0, o1);
+  quad(n2, n3, o2, o3);
+  o[0] = o0;
+  o[1] = o1;
+  o[2] = o2;
+  o[3] = o3;
+  return o;
 }
 #endif
 
@@ -610,9 +654,21 @@ __host__ __device__ constexpr int fwd4_waves(int T, int NB) { return NB >= 2 && 
 //     wait for this wave's loads of stage g+1, barrier, issue stage g+3, read x of
 //     stage g+1, then per column block: next block's fragments, the block's MFMAs,
 //     and after block 0 the transform of x stage g+1 into the other fragment buffer.
-template <int T, typename Elt, int NB, int LOAD, int EPI>
-__global__ void __launch_bounds__(64 * fwd4_waves(T, NB)) eql_fwd4_kernel(const FwdArgs a) {
+//   * SPEC = 1 (p4 fp16, plain epilogue): in the tiles of output column 0 each wave also
+//     transposes its transformed x fragments (8 rows x 8 channels per 8 lanes, by DPP)
+//     and stores them as weight-gradient operand units (FwdArgs::spec), two planes per
+//     wave with 8 waves, at the end of each stage.  Vector-memory loads (LDS DMA
+//     included) and stores retire in issue order on this counter, so each stage's
+//     wait leaves the previous stage's stores outstanding as well as the next stage's
+//     loads.
 #if defined(__HIP_DEVICE_COMPILE__)
+// One workgroup's persistent loop of eql_fwd4_kernel: workgroup b0 of `grid` takes the
+// tiles xcd_remap(b0 + k grid) of `numTiles`, which cover output column tiles
+// colTile0 .. colTile0 + colTiles - 1 of every row tile; LDS rings at byte addresses
+// ldsB (weight) and ldsX (x).  SPEC: also store the transformed x (see above).
+template <int T, typename Elt, int NB, int LOAD, int EPI, bool SPEC>
+__device__ __forceinline__ void fwd4_body(const FwdArgs& a, uint32_t ldsB, uint32_t ldsX, int b0, int grid,
+                                          int numTiles, int colTile0, int colTiles) {
   using E = EltT<Elt>;
   constexpr int WAVES = fwd4_waves(T, NB);
   constexpr int G = E::kPerUnit;
@@ -643,14 +699,10 @@ __global__ void __launch_bounds__(64 * fwd4_waves(T, NB)) eql_fwd4_kernel(const 
   constexpr int WAIT_TOP = (DIST - 2) * (IPW + IPWX);
   constexpr int WAIT_PRO = (DIST - 1) * (IPW + IPWX);
   static_assert(WAIT_PRO < 64, "vmcnt range");
+  static_assert(!SPEC || (T == 4 && ELT == 2 && EPI == 0), "spectrum side output: p4 fp16, plain epilogue");
 
-  __shared__ u32x4 ringB[NS][BSLOT / 16];
-  __shared__ u32x4 ringX[NS][XSLOT / 16];
-
-  // Persistent schedule as eql_fwd_kernel: workgroup b takes tiles xcd_remap(b + k grid).
-  const int b0 = blockIdx.x, grid = gridDim.x;
-  if (b0 >= a.numTiles) return;
-  const int myTiles = (a.numTiles - b0 + grid - 1) / grid;
+  if (b0 >= numTiles) return;
+  const int myTiles = (numTiles - b0 + grid - 1) / grid;
   const int nst = a.Jpad / 2;
   const int nblk = (a.Dout + 31) >> 5;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -663,7 +715,7 @@ __global__ void __launch_bounds__(64 * fwd4_waves(T, NB)) eql_fwd4_kernel(const 
   const uint64_t chunkStride = (uint64_t)T * 1024;
   const uint64_t blockStride = (uint64_t)nst * chunkStride;
 
-  auto tile_of = [&](int k) __attribute__((always_inline)) { return xcd_remap(b0 + k * grid, a.numTiles); };
+  auto tile_of = [&](int k) __attribute__((always_inline)) { return xcd_remap(b0 + k * grid, numTiles); };
 
   // Lane-derived values, re-derived after every epilogue (none is live there; see
   // eql_fwd_kernel).
@@ -678,15 +730,15 @@ __global__ void __launch_bounds__(64 * fwd4_waves(T, NB)) eql_fwd4_kernel(const 
     // Weight fragment (block 0, plane 0) of this lane: channel lrow of the block, group
     // khalf of the stage (packed_unit's order within a chunk).
     const uint32_t bl = (uint32_t)(lrow * 32 + ((khalf ^ ((lrow >> 3) & 1)) * 16));
-    bRdA = lds_addr(&ringB[0][0]) + pa * BSLOT + bl;
-    bRdB = lds_addr(&ringB[0][0]) + pb * BSLOT + bl;
+    bRdA = ldsB + pa * BSLOT + bl;
+    bRdB = ldsB + pb * BSLOT + bl;
     const int row = rb * 32 + lrow;
 #pragma unroll
     for (int v = 0; v < T; ++v) {
       const int u = khalf * T + v;
       const uint32_t xl = (uint32_t)((row * RP + (u ^ ring_swz<RP>(row))) * 16);
-      xRdA[v] = lds_addr(&ringX[0][0]) + pa * XSLOT + xl;
-      xRdB[v] = lds_addr(&ringX[0][0]) + pb * XSLOT + xl;
+      xRdA[v] = ldsX + pa * XSLOT + xl;
+      xRdB[v] = ldsX + pb * XSLOT + xl;
     }
     // x DMA: ring position P = (wave IPWX + i) 64 + lane holds unit (P % RP) ^ swz of
     // row P / RP (padding units past 2T load an arbitrary unit of the row).
@@ -709,8 +761,8 @@ __global__ void __launch_bounds__(64 * fwd4_waves(T, NB)) eql_fwd4_kernel(const 
   auto tile_state = [&](int k, uint64_t& bc, uint32_t& bl, uint64_t& xc, uint32_t& xl) __attribute__((always_inline)) {
     if (k < myTiles) {
       const int t = tile_of(k);
-      const int rt = t / a.colTiles;
-      const int row0 = rt * kFwdRows, col0 = (t - rt * a.colTiles) * BN;
+      const int rt = t / colTiles;
+      const int row0 = rt * kFwdRows, col0 = (colTile0 + t - rt * colTiles) * BN;
       const int ob = (col0 >> 5) + cw;
       bc = reinterpret_cast<uint64_t>(a.wp) + (uint64_t)ob * blockStride + (uint64_t)kbw * 1024;
       bl = ob < nblk ? (uint32_t)(IPW * 1024) : 0u;
@@ -725,10 +777,10 @@ __global__ void __launch_bounds__(64 * fwd4_waves(T, NB)) eql_fwd4_kernel(const 
   uint32_t bDmaA, bDmaB, xDmaA, xDmaB;
   auto ring_setup = [&]() __attribute__((always_inline)) {
     const uint32_t pa = (uint32_t)phase, pb = (uint32_t)((phase + 2) & 3);
-    bDmaA = lds_addr(&ringB[0][0]) + pa * BSLOT + (uint32_t)qw * 1024u;
-    bDmaB = lds_addr(&ringB[0][0]) + pb * BSLOT + (uint32_t)qw * 1024u;
-    xDmaA = lds_addr(&ringX[0][0]) + pa * XSLOT + (uint32_t)(wave * IPWX * 1024);
-    xDmaB = lds_addr(&ringX[0][0]) + pb * XSLOT + (uint32_t)(wave * IPWX * 1024);
+    bDmaA = ldsB + pa * BSLOT + (uint32_t)qw * 1024u;
+    bDmaB = ldsB + pb * BSLOT + (uint32_t)qw * 1024u;
+    xDmaA = ldsX + pa * XSLOT + (uint32_t)(wave * IPWX * 1024);
+    xDmaB = ldsX + pb * XSLOT + (uint32_t)(wave * IPWX * 1024);
   };
   ring_setup();
   auto issue = [&](auto slotTag) __attribute__((always_inline)) {
@@ -797,6 +849,40 @@ __global__ void __launch_bounds__(64 * fwd4_waves(T, NB)) eql_fwd4_kernel(const 
     }
   };
 
+  // Spectrum side output state (SPEC = 1, tiles of column 0 only; dead outside them).
+  uint32_t specCur = 0, specSel = 0;
+  bool specHi2 = false;
+  constexpr int PPW = WAVES == 8 ? T / 2 : T;  // planes stored per wave
+  const uint32_t specRow = (uint32_t)a.specKpad * 16u;  // bytes of one (kg, p, half) run
+  auto spec_setup = [&](int rt) __attribute__((always_inline)) {
+    const int lane = lane_index();
+    const int lrow = lane & 31;
+    const int rbase = rt * kFwdRows + rb * 32 + (lrow & 24);  // first row of the lane's 8-row group
+    specCur = ((uint32_t)(rbase >> 4) * (2u * T) + (uint32_t)((rbase >> 3) & 1)) * specRow +
+              (uint32_t)((lane >> 5) * 8 + (lrow & 7)) * 16u;
+    specHi2 = (lane & 2) != 0;
+    specSel = (lane & 1) ? 0x03020706u : 0x05040100u;
+  };
+  auto store_spec = [&](const u32x4 (&f)[T + NP]) __attribute__((always_inline)) {
+    if constexpr (SPEC) {
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(a.spec, a.specBytes);
+#pragma unroll
+      for (int i = 0; i < PPW; ++i) {
+        u32x4 v;
+        if constexpr (PPW == T) {
+          v = f[i];
+        } else {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) v[w] = cb ? f[PPW + i][w] : f[i][w];
+        }
+        const int p = cb * PPW + i;
+        __builtin_amdgcn_raw_buffer_store_b128(transpose8_b16(v, specHi2, specSel), r, specCur,
+                                               (int)((uint32_t)p * 2u * specRow), kStoreNT);
+      }
+      specCur += 2u * G * 16u;  // the next stage's 16 channels
+    }
+  };
+
   f32x16 acc[T][NBW];
   auto zero_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -814,7 +900,10 @@ __global__ void __launch_bounds__(64 * fwd4_waves(T, NB)) eql_fwd4_kernel(const 
     u32x4 bf[2][T];
 #pragma unroll
     for (int p = 0; p < T; ++p) bf[0][p] = rd(S < 2 ? bRdA : bRdB, (S & 1) * BSLOT + (cb * NBW * T + p) * 1024);
-    wait_vmcnt<WAIT_TOP>();
+    // With the spectrum side output the previous stage's PPW stores were issued after
+    // this stage's look-ahead loads; vector-memory operations retire in issue order, so
+    // leaving them outstanding still means that stage g+1's loads have landed.
+    wait_vmcnt<SPEC ? WAIT_TOP + PPW : WAIT_TOP>();
     // Plain barrier (no fence): the ring reads of stage g-1 are consumed, and a fence
     // would also wait for the loads in flight.
     __builtin_amdgcn_s_barrier();
@@ -840,6 +929,7 @@ __global__ void __launch_bounds__(64 * fwd4_waves(T, NB)) eql_fwd4_kernel(const 
       }
       if (nb == 0) transform(Nxt{});  // x stage g+1; overlaps the MFMA chains
     }
+    if constexpr (SPEC) store_spec(af[cur]);  // x stage g, as weight-gradient units
   };
 
   using I0 = std::integral_constant<int, 0>;
@@ -857,11 +947,14 @@ __global__ void __launch_bounds__(64 * fwd4_waves(T, NB)) eql_fwd4_kernel(const 
   __builtin_amdgcn_s_barrier();
   read_x(I0{});
   transform(I0{});
+  // The first stage's wait counts stores that were never issued: wait for stage 1 here.
+  if constexpr (SPEC) wait_vmcnt<WAIT_TOP>();
 
   for (int k = 0; k < myTiles; ++k) {
     // During this tile's nst stages the issue side crosses exactly one tile boundary.
     tile_state(issK + 1, nbCur, nbLen, nxCur, nxLeft);
     zero_acc();
+    if constexpr (SPEC) spec_setup(tile_of(k) / colTiles);
     int st = 0;
     for (; st + 4 <= nst; st += 4) {
       stage(I0{});
@@ -876,13 +969,41 @@ __global__ void __launch_bounds__(64 * fwd4_waves(T, NB)) eql_fwd4_kernel(const 
     phase = (phase + nst) & 3;
     ring_setup();
     const int t = tile_of(k);
-    const int rt = t / a.colTiles;
-    fwd_epilogue<T, Elt, NBW, EPI>(a, acc, rt * kFwdRows, rb * 32, (t - rt * a.colTiles) * BN + cb * NBW * 32);
+    const int rt = t / colTiles;
+    fwd_epilogue<T, Elt, NBW, EPI>(a, acc, rt * kFwdRows, rb * 32,
+                                   (colTile0 + t - rt * colTiles) * BN + cb * NBW * 32);
     lane_setup();
   }
   // Drain the look-ahead loads (all out of range) before the workgroup's LDS can be
   // reused.
   wait_vmcnt<0>();
+}
+#endif  // __HIP_DEVICE_COMPILE__
+
+template <int T, typename Elt, int NB, int LOAD, int EPI, int SPEC = 0>
+__global__ void __launch_bounds__(64 * fwd4_waves(T, NB)) eql_fwd4_kernel(const FwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int NS = 4;
+  constexpr int BSLOT = NB * T * 1024;
+  constexpr int XSLOT = kFwdRows * 8 * 16;
+  __shared__ u32x4 ringB[NS][BSLOT / 16];
+  __shared__ u32x4 ringX[NS][XSLOT / 16];
+  const uint32_t lb = lds_addr(&ringB[0][0]), lx = lds_addr(&ringX[0][0]);
+  const int b = blockIdx.x;
+  if constexpr (SPEC) {
+    // Workgroups below specGrid (a multiple of the 8 XCDs, as is the rest) take column
+    // 0's tiles and store the spectrum; the others take the remaining columns.  Each
+    // part walks its own tiles in the XCD-aware order, and both visit the row tiles in
+    // the same order, so the two parts of an XCD read the same rows of x.
+    const int rowTiles = a.numTiles / a.colTiles;
+    if (b < a.specGrid)
+      fwd4_body<T, Elt, NB, LOAD, EPI, true>(a, lb, lx, b, a.specGrid, rowTiles, 0, 1);
+    else
+      fwd4_body<T, Elt, NB, LOAD, EPI, false>(a, lb, lx, b - a.specGrid, (int)gridDim.x - a.specGrid,
+                                              rowTiles * (a.colTiles - 1), 1, a.colTiles - 1);
+  } else {
+    fwd4_body<T, Elt, NB, LOAD, EPI, false>(a, lb, lx, b, (int)gridDim.x, a.numTiles, 0, a.colTiles);
+  }
 #endif  // __HIP_DEVICE_COMPILE__
 }
 

@@ -260,6 +260,41 @@ int eqlinear_bwd_w(const void* x, const void* dy, void* dw, void* workspace, siz
                    int64_t N, int64_t Cp, int64_t Dp, int T, int dtype, void* stream);
 
 /*
+ * A training step's three passes sharing one weight-gradient workspace, so that the
+ * group transforms of x and dy are taken where the forward and the input gradient
+ * already compute them, instead of by a separate pass over x and dy in the weight
+ * gradient ("Resumo Tecnico: Flash EQ-Linear", "Implementacao": fused data flows with
+ * no intermediate re-reads of the activations).  Arguments, results and errors as
+ * eqlinear_fwd, eqlinear_bwd_x and eqlinear_bwd_w, plus `workspace` of at least
+ * eqlinear_bwd_w_workspace_bytes(N, Cp, Dp, T, dtype) bytes, 16-byte aligned
+ * (EQL_EINVAL if ws_bytes is smaller or workspace is NULL with N > 0):
+ *  - eqlinear_fwd_train writes y exactly as eqlinear_fwd, and x's half spectrum into
+ *    the workspace (the operand units of the weight-gradient GEMM).  At p4 fp16 with
+ *    16-byte rows the forward kernel stores the transform it has formed for its MFMAs
+ *    (packed fp16 butterflies: X0 and X2 rounded twice, as in the forward); otherwise,
+ *    after the forward, the weight gradient's own transform (fp32, rounded once).
+ *  - eqlinear_bwd_x_train writes dx exactly as eqlinear_bwd_x and, when the shape takes
+ *    the separate weight-gradient path, dy's half spectrum likewise; on the fused path
+ *    (which reads dy itself) it only computes dx.
+ *  - eqlinear_bwd_w_train writes dw from those spectra: the weight gradient's GEMMs and
+ *    reduce without its transforms.  dy is read on the fused path only (it may be NULL
+ *    on the separate path); x is not needed.
+ * Contract: eqlinear_bwd_w_train's workspace must hold what eqlinear_fwd_train (for
+ * this x) and eqlinear_bwd_x_train (for this dy) wrote there, for the same N, Cp, Dp,
+ * T and dtype, ordered before it on the stream, with nothing else writing that memory
+ * in between; the library cannot check this.  Each call's own result is complete when
+ * it returns (y, dx) or completes on the stream (dw).  The spectra cover every row and
+ * every channel of the layer; padding units past the channel count may hold stale
+ * values and only reach gradient entries that are discarded.
+ */
+int eqlinear_fwd_train(const void* x, const void* w_packed, void* y, void* workspace, size_t ws_bytes,
+                       int64_t N, int64_t Cp, int64_t Dp, int T, int dtype, void* stream);
+int eqlinear_bwd_x_train(const void* dy, const void* w_packed_bwdx, void* dx, void* workspace, size_t ws_bytes,
+                         int64_t N, int64_t Cp, int64_t Dp, int T, int dtype, void* stream);
+int eqlinear_bwd_w_train(const void* dy, void* dw, void* workspace, size_t ws_bytes, int64_t N, int64_t Cp,
+                         int64_t Dp, int T, int dtype, void* stream);
+
+/*
  * The layer over p4m's point group (dihedral D4: four rotations r^a and four
  * reflections r^a s; r^4 = s^2 = e, s r s = r^-1).  "Resumo Tecnico: Flash EQ-Linear",
  * "Limitacoes e Trabalho Futuro", names other groups, reflection groups among them, as
@@ -296,7 +331,9 @@ const char* eqlinear_status_string(int status);
 
 /* ABI version of this header (major * 100 + minor).  2.00: the blocked packed-weight
  * layout above (1.xx stored ((o * Jin + i / G) * T + p) * G + i % G).  2.01:
- * eqlinear_fused_epilogue_bwd_noalloc and EQL_ESCRATCH.  2.02: the p4m entry points. */
+ * eqlinear_fused_epilogue_bwd_noalloc and EQL_ESCRATCH.  2.02: the p4m entry points.
+ * 2.03: the training-step entry points (eqlinear_fwd_train, eqlinear_bwd_x_train,
+ * eqlinear_bwd_w_train). */
 int eqlinear_abi_version(void);
 
 #ifdef __cplusplus

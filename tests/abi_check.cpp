@@ -35,7 +35,7 @@ void* const MIS2 = reinterpret_cast<void*>(uintptr_t{0x10002});
 constexpr int F16 = EQL_F16, F32 = EQL_F32;
 
 void sizes() {
-  CHECK(eqlinear_abi_version() == 202);
+  CHECK(eqlinear_abi_version() == 203);
   for (int s = -3; s < 12; ++s) CHECK(eqlinear_status_string(s) != nullptr && std::strlen(eqlinear_status_string(s)) > 0);
   // Packed weight: out channels padded to 32, input 16-byte groups padded per stage.
   CHECK(eqlinear_packed_weight_bytes(3, 5, 4, F16) == 32u * 4 * 16 * 4);
@@ -116,6 +116,32 @@ void validation() {
   CHECK(eqlinear_bwd_w(A, B, C, D, ws, 300, 5, 7, 0, F16, nullptr) == EQL_EINVAL);
   CHECK(eqlinear_bwd_w(A, B, C, D, ws, 300, 5, 7, 4, 3, nullptr) == EQL_EINVAL);
   CHECK(eqlinear_bwd_w(A, B, C, D, SIZE_MAX, INT64_MAX, 5, 7, 4, F16, nullptr) == EQL_EINVAL);
+  // Training-step entry points (share the weight-gradient workspace).  (300, 8, 8, 4)
+  // takes the fused weight-gradient path, (300, 5, 7, 4) the separate one.
+  const size_t wf = eqlinear_bwd_w_workspace_bytes(300, 8, 8, 4, F16);
+  CHECK(wf > 0);
+  CHECK(eqlinear_fwd_train(A, B, C, D, ws - 1, 300, 5, 7, 4, F16, nullptr) == EQL_EINVAL);
+  CHECK(eqlinear_fwd_train(A, B, C, nullptr, ws, 300, 5, 7, 4, F16, nullptr) == EQL_EINVAL);
+  CHECK(eqlinear_fwd_train(A, B, C, MIS, ws, 300, 5, 7, 4, F16, nullptr) == EQL_EALIGN);
+  CHECK(eqlinear_fwd_train(MIS, B, C, D, wf, 300, 8, 8, 4, F16, nullptr) == EQL_EALIGN);
+  CHECK(eqlinear_fwd_train(nullptr, B, C, D, wf, 300, 8, 8, 4, F16, nullptr) == EQL_EINVAL);
+  CHECK(eqlinear_fwd_train(A, B, C, D, ws, 300, 5, 7, 0, F16, nullptr) == EQL_EINVAL);
+  CHECK(eqlinear_fwd_train(A, B, C, D, ws, 300, 5, 7, 20, F16, nullptr) == EQL_EUNSUPPORTED);
+  CHECK(eqlinear_fwd_train(A, B, C, D, SIZE_MAX, INT64_MAX, 5, 7, 4, F16, nullptr) == EQL_EINVAL);
+  CHECK(eqlinear_fwd_train(nullptr, nullptr, nullptr, nullptr, 0, 0, 5, 7, 4, F16, nullptr) == EQL_OK);
+  CHECK(eqlinear_bwd_x_train(A, B, C, D, ws - 1, 300, 5, 7, 4, F16, nullptr) == EQL_EINVAL);
+  CHECK(eqlinear_bwd_x_train(A, B, C, nullptr, ws, 300, 5, 7, 4, F16, nullptr) == EQL_EINVAL);
+  CHECK(eqlinear_bwd_x_train(A, B, C, MIS, ws, 300, 5, 7, 4, F16, nullptr) == EQL_EALIGN);
+  CHECK(eqlinear_bwd_x_train(MIS, B, C, D, ws, 300, 5, 7, 4, F16, nullptr) == EQL_EALIGN);
+  CHECK(eqlinear_bwd_x_train(MIS, B, C, D, wf, 300, 8, 8, 4, F16, nullptr) == EQL_EALIGN);
+  CHECK(eqlinear_bwd_x_train(nullptr, nullptr, nullptr, nullptr, 0, 0, 5, 7, 4, F16, nullptr) == EQL_OK);
+  CHECK(eqlinear_bwd_w_train(B, C, D, ws - 1, 300, 5, 7, 4, F16, nullptr) == EQL_EINVAL);
+  CHECK(eqlinear_bwd_w_train(B, nullptr, D, ws, 300, 5, 7, 4, F16, nullptr) == EQL_EINVAL);
+  CHECK(eqlinear_bwd_w_train(B, C, nullptr, ws, 300, 5, 7, 4, F16, nullptr) == EQL_EINVAL);
+  CHECK(eqlinear_bwd_w_train(B, C, MIS, ws, 300, 5, 7, 4, F16, nullptr) == EQL_EALIGN);
+  CHECK(eqlinear_bwd_w_train(nullptr, C, D, wf, 300, 8, 8, 4, F16, nullptr) == EQL_EINVAL);  // fused: dy read
+  CHECK(eqlinear_bwd_w_train(MIS, C, D, wf, 300, 8, 8, 4, F16, nullptr) == EQL_EALIGN);
+  CHECK(eqlinear_bwd_w_train(B, C, D, ws, 300, 5, 7, 4, 3, nullptr) == EQL_EINVAL);
   // Epilogue backward, with and without a workspace.
   const size_t es = eqlinear_fused_epilogue_bwd_workspace_bytes(300, 5, 4, F16);
   CHECK(es == 19u * 20 * 4);
