@@ -4,8 +4,12 @@
 
 One step = one pass of the whole path over one batch of resident synthetic input:
 pack the weight spectrum (forward and input-gradient packings), forward, input
-gradient, weight gradient.  The default workload is the p4 (T=4) fp16 large square
-layer, N=65536 rows, C=D=4096 (C'=D'=1024), forward + backward.
+gradient, weight gradient.  By default (--step train) the three passes are the
+training-step entry points, which share the weight-gradient workspace: the forward
+and the input gradient leave the half spectra of x and dy there and the weight
+gradient runs its GEMMs on them; the same step through the plain entry points is
+timed beside it (`plain_step`).  The default workload is the p4 (T=4) fp16 large
+square layer, N=65536 rows, C=D=4096 (C'=D'=1024), forward + backward.
 
 Prints ONE JSON line.  `value` is the dense-equivalent throughput of the step,
 3 passes x 2*N*D*C FLOPs per step time.  `roofline` covers the step's dominant
@@ -41,7 +45,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="c5", choices=sorted(W.WORKLOADS))
-    ap.add_argument("--step", default="plain", choices=["train", "plain"],
+    ap.add_argument("--step", default="train", choices=["train", "plain"],
                     help="train: eqlinear_fwd_train / eqlinear_bwd_x_train / eqlinear_bwd_w_train (the "
                          "forward and the input gradient leave the spectra in the weight-gradient workspace); "
                          "plain: eqlinear_fwd / eqlinear_bwd_x / eqlinear_bwd_w")
@@ -63,6 +67,15 @@ def parse():
                     help="after timing, run a plain device copy of this size (a reference for "
                          "profiler traffic counters)")
     return ap.parse_args()
+
+
+def bwdw_fused_path(N, Cp, Dp, T, elt) -> bool:
+    """Whether the library's weight gradient takes its fused path for this shape (the
+    rule include/eqlinear.h documents for eqlinear_bwd_w)."""
+    if N == 0 or T not in (1, 2, 4) or (Dp * T * elt) % 16 or N * Dp * T * elt >= 2**32:
+        return False
+    planes = {1: 1, 2: 2, 4: 6}[T]
+    return 2.0 * planes * N * Dp * Cp / (elt * T * N * (Cp + Dp)) < 400.0
 
 
 def kernel_source_hash() -> str:
@@ -138,12 +151,13 @@ def main():
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
 
-    def make_calls(sp, b=s0):
+    def make_calls(sp, b=s0, mode=None):
+        mode = mode or args.step
         calls = {
             "pack": lambda: (eql.eqlinear_pack_weight(b["w"], b["wp"], Dp, Cp, T, code, eql.EQL_PACK_FWD, sp),
                              eql.eqlinear_pack_weight(b["w"], b["wpb"], Dp, Cp, T, code, eql.EQL_PACK_BWDX, sp)),
         }
-        if args.step == "train":
+        if mode == "train":
             calls["fwd"] = lambda: eql.eqlinear_fwd_train(b["x"], b["wp"], b["y"], b["ws"], ws_bytes, N, Cp, Dp, T,
                                                           code, sp)
             calls["bwd_x"] = lambda: eql.eqlinear_bwd_x_train(b["dy"], b["wpb"], b["dx"], b["ws"], ws_bytes, N, Cp,
@@ -187,6 +201,15 @@ def main():
         return wall * 1e3 / args.steps, per, step_dev
 
     ms_per_step, per, step_dev = timed(lambda i: set_calls[i % n_sets])
+    plain_step = None
+    if args.step == "train":
+        # The same step through the plain entry points (each pass on its own inputs; the
+        # weight gradient transforms x and dy itself), for comparison.
+        plain_calls = [make_calls(sptr, b, "plain") for b in sets]
+        pms, pper, _ = timed(lambda i: plain_calls[i % n_sets])
+        plain_step = {"ms_per_step": round(pms, 4), "passes_ms": {k: round(v, 4) for k, v in pper.items()},
+                      "kind": "pack(fwd)+pack(bwd_x)+eqlinear_fwd+eqlinear_bwd_x+eqlinear_bwd_w on the same buffers"}
+        del plain_calls
     warm = None
     if n_sets > 1:
         wms, wper, _ = timed(lambda i: set_calls[0])
@@ -202,6 +225,13 @@ def main():
         "bwd_x": elt * (N * Dp * T + N * Cp * T + Dp * Cp * T),
         "bwd_w": elt * (N * Cp * T + N * Dp * T + Dp * Cp * T),
     }
+    if args.step == "train":
+        # The training forward also writes x's half spectrum (the size of x); the training
+        # input gradient writes dy's where the weight gradient takes the separate path.  The
+        # weight gradient then reads the spectra instead of x and dy (the same bytes).
+        bytes_pass["fwd"] += elt * N * Cp * T
+        if not bwdw_fused_path(N, Cp, Dp, T, elt):
+            bytes_pass["bwd_x"] += elt * N * Dp * T
     passes = {}
     for k in ("fwd", "bwd_x", "bwd_w"):
         t = per[k] * 1e-3
@@ -221,6 +251,8 @@ def main():
         else "eql_fwd_kernel"
     if fwd_kernel_ms >= per["bwd_w"]:
         dom, kname, t_dom = "fwd", fwd_name, 0.5 * fwd_kernel_ms * 1e-3
+        if args.step == "train" and fwd_name == "eql_fwd4_kernel" and T == 4 and elt == 2:
+            kname = "eql_fwd4_kernel_spec"  # the launch whose column-0 tiles store the spectrum
     else:
         dom, kname, t_dom = "bwd_w", "eqlinear_bwd_w", per["bwd_w"] * 1e-3
     flop_bound = actual / MFMA_PEAK[wl.dtype] / 1e12 >= bytes_pass[dom] / HBM_PEAK / 1e9
@@ -234,8 +266,9 @@ def main():
     roofline["traffic"] = traffic_for(kname, wl.key)
     roofline["kernel"] = kname
     roofline["ms_per_launch"] = round(t_dom * 1e3, 4)
-    roofline["algorithmic"] = ("%.4g FLOP (%s real GEMMs of N x D' x C') and %.4g bytes (x, y, weight) per launch"
-                               % (actual, (2 * T - 2) if T % 2 == 0 else (2 * T - 1), bytes_pass[dom]))
+    roofline["algorithmic"] = ("%.4g FLOP (%s real GEMMs of N x D' x C') and %.4g bytes (x, y, weight%s) per launch"
+                               % (actual, (2 * T - 2) if T % 2 == 0 else (2 * T - 1), bytes_pass[dom],
+                                  ", x's spectrum" if args.step == "train" and dom == "fwd" else ""))
 
     # The same step captured once in a HIP graph and replayed (the library records only
     # kernel launches on the caller's stream).  Reported beside the eager figure.
@@ -284,6 +317,12 @@ def main():
         dense["speedup_bwd_w"] = round(dense["bwd_w_ms"] / per["bwd_w"], 3)
         total = dense["fwd_ms"] + dense["bwd_x_ms"] + dense["bwd_w_ms"]
         dense["speedup_fwd_bwd"] = round(total / (per["fwd"] + per["bwd_x"] + per["bwd_w"]), 3)
+        if plain_step is not None:
+            pp = plain_step["passes_ms"]
+            dense["plain_speedup_fwd"] = round(dense["fwd_ms"] / pp["fwd"], 3)
+            dense["plain_speedup_bwd_x"] = round(dense["bwd_x_ms"] / pp["bwd_x"], 3)
+            dense["plain_speedup_bwd_w"] = round(dense["bwd_w_ms"] / pp["bwd_w"], 3)
+            dense["plain_speedup_fwd_bwd"] = round(total / (pp["fwd"] + pp["bwd_x"] + pp["bwd_w"]), 3)
 
     fused = None
     if not args.no_fused:
@@ -325,6 +364,7 @@ def main():
         "pack_ms": round(per["pack"], 4),
         "mfma_frac_step": round(n_passes * actual / (ms_per_step * 1e-3) / 1e12 / MFMA_PEAK[wl.dtype], 4),
         "roofline": roofline,
+        "plain_step": plain_step,
         "graph_step": graph,
         "dense_baseline": dense,
         "fused_epilogue": fused,
