@@ -4,7 +4,10 @@ weight can be used as is ("Implementacao" in "Resumo Tecnico: Flash EQ-Linear":
 training-free, plug-and-play replacement).
 
 Forward packs the half spectrum of w and runs eqlinear_fwd; backward runs
-eqlinear_bwd_x on the conjugate-transposed packing and eqlinear_bwd_w.  EQLinearP4M is the
+eqlinear_bwd_x on the conjugate-transposed packing and eqlinear_bwd_w.  When the weight
+needs a gradient, the three passes are the training entry points instead
+(eqlinear_fwd_train, eqlinear_bwd_x_train, eqlinear_bwd_w_train): the forward keeps the
+weight-gradient workspace, holding x's half spectrum, alive until the backward.  EQLinearP4M is the
 layer over p4m's point group (rotations and reflections), run through the same kernels on
 the C_4 view described in include/eqlinear.h.  With a bias,
 GELU or a residual, the forward is eqlinear_fwd_fused and the backward starts with
@@ -18,7 +21,8 @@ import math
 import torch
 
 from . import (EQL_ACT_GELU, EQL_ACT_NONE, EQL_PACK_BWDX, EQL_PACK_FWD, eqlinear_bwd_w,
-               eqlinear_bwd_w_workspace_bytes, eqlinear_bwd_x, eqlinear_fused_epilogue_bwd,
+               eqlinear_bwd_w_train, eqlinear_bwd_w_workspace_bytes, eqlinear_bwd_x,
+               eqlinear_bwd_x_train, eqlinear_fused_epilogue_bwd, eqlinear_fwd_train,
                eqlinear_fused_epilogue_bwd_workspace_bytes, eqlinear_fwd, eqlinear_fwd_fused,
                eqlinear_p4m_expand_weight, eqlinear_p4m_fold_weight_grad, eqlinear_pack_weight,
                eqlinear_packed_weight_bytes)
@@ -46,27 +50,40 @@ class EQLinearFunction(torch.autograd.Function):
         x2 = x.reshape(-1, Cp * T).contiguous()
         N = x2.shape[0]
         y = torch.empty((N, Dp * T), dtype=x.dtype, device=x.device)
-        eqlinear_fwd(x2, _packed(w, EQL_PACK_FWD), y, N, Cp, Dp, T, x.dtype)
-        ctx.save_for_backward(x2, w)
+        ws_bytes = eqlinear_bwd_w_workspace_bytes(N, Cp, Dp, T, x.dtype)
+        if ctx.needs_input_grad[1]:
+            # The weight gradient will follow: keep x's spectrum in its workspace.
+            ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=x.device)
+            eqlinear_fwd_train(x2, _packed(w, EQL_PACK_FWD), y, ws, ws_bytes, N, Cp, Dp, T, x.dtype)
+        else:
+            ws = None
+            eqlinear_fwd(x2, _packed(w, EQL_PACK_FWD), y, N, Cp, Dp, T, x.dtype)
+        ctx.save_for_backward(x2, w, ws)
+        ctx.ws_bytes = ws_bytes
         ctx.lead_shape = x.shape[:-1]
         return y.reshape(*x.shape[:-1], Dp * T)
 
     @staticmethod
     def backward(ctx, dy: torch.Tensor):
-        x2, w = ctx.saved_tensors
+        x2, w, ws = ctx.saved_tensors
         Dp, Cp, T = w.shape
         N = x2.shape[0]
         dy2 = dy.reshape(-1, Dp * T).to(x2.dtype).contiguous()
         dx = dw = None
-        if ctx.needs_input_grad[0]:
+        need_dx, need_dw = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        if need_dx:
             dx = torch.empty((N, Cp * T), dtype=x2.dtype, device=x2.device)
-            eqlinear_bwd_x(dy2, _packed(w, EQL_PACK_BWDX), dx, N, Cp, Dp, T, x2.dtype)
+            if need_dw:  # also leaves dy's spectrum where the weight gradient reads it
+                eqlinear_bwd_x_train(dy2, _packed(w, EQL_PACK_BWDX), dx, ws, ctx.ws_bytes, N, Cp, Dp, T, x2.dtype)
+            else:
+                eqlinear_bwd_x(dy2, _packed(w, EQL_PACK_BWDX), dx, N, Cp, Dp, T, x2.dtype)
             dx = dx.reshape(*ctx.lead_shape, Cp * T)
-        if ctx.needs_input_grad[1]:
-            ws_bytes = eqlinear_bwd_w_workspace_bytes(N, Cp, Dp, T, x2.dtype)
-            ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=x2.device)
+        if need_dw:
             dw = torch.empty_like(w)
-            eqlinear_bwd_w(x2, dy2, dw, ws, ws_bytes, N, Cp, Dp, T, x2.dtype)
+            if need_dx:
+                eqlinear_bwd_w_train(dy2, dw, ws, ctx.ws_bytes, N, Cp, Dp, T, x2.dtype)
+            else:
+                eqlinear_bwd_w(x2, dy2, dw, ws, ctx.ws_bytes, N, Cp, Dp, T, x2.dtype)
         return dx, dw
 
 

@@ -216,3 +216,28 @@ def test_train_full_size(key):
     cmp = Compare(TOL[wl.dtype], "%s bwd_w_train" % key)
     cmp.add(dw.reshape(wl.Dp, -1), oracle.bwd_w(x, dy, wl.T).reshape(wl.Dp, -1))
     cmp.check()
+
+
+@pytest.mark.parametrize("grads", ["both", "w_only", "x_only"])
+def test_layer_autograd_through_training_entry_points(grads):
+    """EQLinearFunction: with a weight gradient the forward keeps the workspace and the
+    backward runs the training entry points (with only one gradient, the plain ones)."""
+    from group_circulant_linear_p4_amd.layer import eqlinear
+    T, N, Cp, Dp = 4, 333, 256, 520
+    wl = W.Workload("t", "test", T, N, Cp, Dp, "f16", ("fwd", "bwd_x", "bwd_w"), seed=91)
+    x_h, w_h, dy_h = W.make_x(wl), W.make_w(wl), W.make_dy(wl)
+    x = torch.from_numpy(x_h).to(DEV).reshape(3, 111, Cp * T).requires_grad_(grads != "w_only")
+    w = torch.from_numpy(w_h).to(DEV).requires_grad_(grads != "x_only")
+    print("case layer %s" % grads, flush=True)
+    y = eqlinear(x, w)
+    y.backward(torch.from_numpy(dy_h).to(DEV).reshape(3, 111, Dp * T))
+    torch.cuda.synchronize()
+    assert rel_err(y.detach().cpu().numpy().reshape(N, -1), oracle.fwd(x_h, w_h)) <= TOL["f16"]
+    if grads != "w_only":
+        assert rel_err(x.grad.cpu().numpy().reshape(N, -1), oracle.bwd_x(dy_h, w_h)) <= TOL["f16"]
+    else:
+        assert x.grad is None
+    if grads != "x_only":
+        assert rel_err(w.grad.cpu().numpy(), oracle.bwd_w(x_h, dy_h, T)) <= TOL["f16"]
+    else:
+        assert w.grad is None
