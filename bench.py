@@ -663,7 +663,18 @@ def bench_p4m(args, torch, eql, wl):
         "bwd_w": lambda: (eql.eqlinear_bwd_w(x, dy, dw4, ws, ws_bytes, N, 2 * Cp, 2 * Dp, 4, code, sp),
                           eql.eqlinear_p4m_fold_weight_grad(dw4, dw, Dp, Cp, code, sp)),
     }
+    if args.step == "train":
+        calls["fwd"] = lambda: eql.eqlinear_fwd_train(x, wp, y, ws, ws_bytes, N, 2 * Cp, 2 * Dp, 4, code, sp)
+        calls["bwd_x"] = lambda: eql.eqlinear_bwd_x_train(dy, wpb, dx, ws, ws_bytes, N, 2 * Cp, 2 * Dp, 4, code, sp)
+        calls["bwd_w"] = lambda: (eql.eqlinear_bwd_w_train(dy, dw4, ws, ws_bytes, N, 2 * Cp, 2 * Dp, 4, code, sp),
+                                  eql.eqlinear_p4m_fold_weight_grad(dw4, dw, Dp, Cp, code, sp))
     order = ["pack", "fwd", "bwd_x", "bwd_w"]
+    t_burn = time.perf_counter()
+    while args.burn_in_ms > 0 and time.perf_counter() - t_burn < args.burn_in_ms * 1e-3:
+        for _ in range(8):
+            for k in order:
+                calls[k]()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         for k in order:
             calls[k]()
@@ -693,7 +704,9 @@ def bench_p4m(args, torch, eql, wl):
         roofline = {"bound": "hbm", "achieved": round(bytes_pass / t_dom / 1e9, 1), "peak": HBM_PEAK, "unit": "GB/s"}
     roofline["frac"] = round(roofline["achieved"] / roofline["peak"], 4)
     roofline["traffic"] = None
-    roofline["kernel"] = "eql_fwd4_kernel (C_4 view)"
+    roofline["kernel"] = ("eql_fwd4_kernel (C_4 view; in the training step the forward's launch also stores x's "
+                          "spectrum, the input gradient's is the plain kernel where the weight gradient reads dy itself)"
+                          if args.step == "train" else "eql_fwd4_kernel (C_4 view)")
     roofline["ms_per_launch"] = round(t_dom * 1e3, 4)
     cpu = None
     if not args.no_cpu_baseline:
@@ -718,7 +731,9 @@ def bench_p4m(args, torch, eql, wl):
             "dtype": wl.dtype, "data": "synthetic (seeded; x, dy ~ N(0,1), w ~ N(0,1/C))",
             "config": {"workload": "p4m layer on %s's widths: N=%d, C=%d (C'=%d x 8), D=%d (D'=%d x 8)"
                                    % (wl.key, N, C, Cp, D, Dp),
-                       "group": "p4m (D4)", "step": "expand+pack x2, fwd, bwd_x, bwd_w+fold"},
+                       "group": "p4m (D4)",
+                       "step": ("expand+pack x2, fwd_train, bwd_x_train, bwd_w_train+fold" if args.step == "train"
+                                else "expand+pack x2, fwd, bwd_x, bwd_w+fold")},
             "passes": passes, "pack_ms": round(per["pack"], 4), "roofline": roofline, "cpu_baseline": cpu}
     print(json.dumps(line), flush=True)
 

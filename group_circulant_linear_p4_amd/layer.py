@@ -231,28 +231,42 @@ class EQLinearP4MFunction(torch.autograd.Function):
         x2 = x.reshape(-1, Cp * 8).contiguous()
         N = x2.shape[0]
         y = torch.empty((N, Dp * 8), dtype=x.dtype, device=x.device)
-        eqlinear_fwd(x2, _packed(w4, EQL_PACK_FWD), y, N, 2 * Cp, 2 * Dp, 4, x.dtype)
-        ctx.save_for_backward(x2, w4)
+        ws_bytes = eqlinear_bwd_w_workspace_bytes(N, 2 * Cp, 2 * Dp, 4, x.dtype)
+        if ctx.needs_input_grad[1]:
+            # As EQLinearFunction: keep x's spectrum for the weight gradient.
+            ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=x.device)
+            eqlinear_fwd_train(x2, _packed(w4, EQL_PACK_FWD), y, ws, ws_bytes, N, 2 * Cp, 2 * Dp, 4, x.dtype)
+        else:
+            ws = None
+            eqlinear_fwd(x2, _packed(w4, EQL_PACK_FWD), y, N, 2 * Cp, 2 * Dp, 4, x.dtype)
+        ctx.save_for_backward(x2, w4, ws)
+        ctx.ws_bytes = ws_bytes
         ctx.lead_shape = x.shape[:-1]
         ctx.p4m_shape = (Dp, Cp)
         return y.reshape(*x.shape[:-1], Dp * 8)
 
     @staticmethod
     def backward(ctx, dy: torch.Tensor):
-        x2, w4 = ctx.saved_tensors
+        x2, w4, ws = ctx.saved_tensors
         Dp, Cp = ctx.p4m_shape
         N = x2.shape[0]
         dy2 = dy.reshape(-1, Dp * 8).to(x2.dtype).contiguous()
         dx = dw = None
-        if ctx.needs_input_grad[0]:
+        need_dx, need_dw = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        if need_dx:
             dx = torch.empty((N, Cp * 8), dtype=x2.dtype, device=x2.device)
-            eqlinear_bwd_x(dy2, _packed(w4, EQL_PACK_BWDX), dx, N, 2 * Cp, 2 * Dp, 4, x2.dtype)
+            if need_dw:
+                eqlinear_bwd_x_train(dy2, _packed(w4, EQL_PACK_BWDX), dx, ws, ctx.ws_bytes, N, 2 * Cp, 2 * Dp, 4,
+                                     x2.dtype)
+            else:
+                eqlinear_bwd_x(dy2, _packed(w4, EQL_PACK_BWDX), dx, N, 2 * Cp, 2 * Dp, 4, x2.dtype)
             dx = dx.reshape(*ctx.lead_shape, Cp * 8)
-        if ctx.needs_input_grad[1]:
-            ws_bytes = eqlinear_bwd_w_workspace_bytes(N, 2 * Cp, 2 * Dp, 4, x2.dtype)
-            ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=x2.device)
+        if need_dw:
             dw4 = torch.empty_like(w4)
-            eqlinear_bwd_w(x2, dy2, dw4, ws, ws_bytes, N, 2 * Cp, 2 * Dp, 4, x2.dtype)
+            if need_dx:
+                eqlinear_bwd_w_train(dy2, dw4, ws, ctx.ws_bytes, N, 2 * Cp, 2 * Dp, 4, x2.dtype)
+            else:
+                eqlinear_bwd_w(x2, dy2, dw4, ws, ctx.ws_bytes, N, 2 * Cp, 2 * Dp, 4, x2.dtype)
             dw = torch.empty((Dp, Cp, 8), dtype=x2.dtype, device=x2.device)
             eqlinear_p4m_fold_weight_grad(dw4, dw, Dp, Cp, x2.dtype)
         return dx, dw
