@@ -257,16 +257,21 @@ bool bwdw_fused(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype) {
   return flops / bytes < kFusedIntensity;
 }
 
-// Waves per workgroup of the separate path's GEMMs on 256-wide tiles.
-// EQL_BWDW_WAVES=4|8 overrides the choice (for measurement).
-int bwdw_waves() {
+// Waves per workgroup of the separate path's GEMMs on 256-wide tiles, for the real-plane
+// GEMM (pair = false) and the complex-pair GEMM.  EQL_BWDW_WAVES=4|8 overrides both,
+// EQL_BWDW_WAVES=<real>,<pair> (e.g. 4,8) each (for measurement).
+int bwdw_waves(bool pair) {
   static const int forced = [] {
     const char* v = std::getenv("EQL_BWDW_WAVES");
-    if (v && std::strcmp(v, "4") == 0) return 4;
-    if (v && std::strcmp(v, "8") == 0) return 8;
+    if (!v) return 0;
+    if (std::strcmp(v, "4") == 0) return 44;
+    if (std::strcmp(v, "8") == 0) return 88;
+    if (std::strcmp(v, "4,8") == 0) return 48;
+    if (std::strcmp(v, "8,4") == 0) return 84;
     return 0;
   }();
-  return forced ? forced : 8;
+  if (!forced) return 8;
+  return pair ? forced % 10 : forced / 10;
 }
 
 constexpr int64_t kMinStepsPerSplit = 16;  // keeps partial-spectrum traffic small
@@ -312,11 +317,15 @@ BwdwPlan plan_bwdw(int64_t N, int64_t Cp, int64_t Dp, int T, int dtype) {
   p.pair.CB = wc == 256 ? 2 : 1;
   // 256 x 256 (real) and 256 x 128 (pair) tiles: 8 waves, two per SIMD, each with half
   // the columns of the 4-wave arrangement.
-  if (bwdw_waves() == 8 && wd == 256 && wc == 256) {
-    p.real.CB = 2;
-    p.real.WCN = 4;
-    p.pair.CB = 1;
-    p.pair.WCN = 4;
+  if (wd == 256 && wc == 256) {
+    if (bwdw_waves(false) == 8) {
+      p.real.CB = 2;
+      p.real.WCN = 4;
+    }
+    if (bwdw_waves(true) == 8) {
+      p.pair.CB = 1;
+      p.pair.WCN = 4;
+    }
   }
   p.real.groups = nr;
   p.real.dTiles = p.Dpad / wd;

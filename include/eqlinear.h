@@ -247,8 +247,8 @@ size_t eqlinear_bwd_w_workspace_bytes(int64_t N, int64_t Cp, int64_t Dp, int T, 
  *    which round the two real frequencies twice; otherwise in fp32, rounded once).
  *    The environment variable EQL_BWDW_PATH=fused|separate, read once per process,
  *    overrides the choice among shapes the fused path accepts (for measurement), and
- *    EQL_BWDW_WAVES=4|8 the waves per workgroup of the separate path's GEMMs on
- *    256-channel tiles (default 8).
+ *    EQL_BWDW_WAVES=4|8 (or <real>,<pair>, e.g. 4,8) the waves per workgroup of the
+ *    separate path's GEMMs on 256-channel tiles (default 8 for both).
  * Both write one fp32 partial per row range of N, then sum the partials in a fixed
  * order (deterministic for a given shape and path), apply the inverse transform and
  * round to `dtype`.  x: [N][Cp*T], dy: [N][Dp*T] read; dw: [Dp][Cp][T] overwritten
