@@ -654,7 +654,9 @@ __host__ __device__ constexpr int fwd4_waves(int T, int NB) { return NB >= 2 && 
 //     wait for this wave's loads of stage g+1, barrier, issue stage g+3, read x of
 //     stage g+1, then per column block: next block's fragments, the block's MFMAs,
 //     and after block 0 the transform of x stage g+1 into the other fragment buffer.
-//   * SPEC = 1 (p4 fp16, plain epilogue): in the tiles of output column 0 each wave also
+//   * SPEC = 1 (p4 fp16, plain epilogue): the workgroups below FwdArgs::specGrid take the
+//     tiles of output column 0 and run the loop with the spectrum side output; the others
+//     take the remaining columns with the plain loop.  In the storing loop each wave also
 //     transposes its transformed x fragments (8 rows x 8 channels per 8 lanes, by DPP)
 //     and stores them as weight-gradient operand units (FwdArgs::spec), two planes per
 //     wave with 8 waves, at the end of each stage.  Vector-memory loads (LDS DMA
@@ -849,7 +851,7 @@ __device__ __forceinline__ void fwd4_body(const FwdArgs& a, uint32_t ldsB, uint3
     }
   };
 
-  // Spectrum side output state (SPEC = 1, tiles of column 0 only; dead outside them).
+  // Spectrum side output state (SPEC: set at each tile's start, dead before its epilogue).
   uint32_t specCur = 0, specSel = 0;
   bool specHi2 = false;
   constexpr int PPW = WAVES == 8 ? T / 2 : T;  // planes stored per wave
