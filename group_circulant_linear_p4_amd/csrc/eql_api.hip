@@ -63,6 +63,9 @@ int status_of(hipError_t e) { return e == hipSuccess ? EQL_OK : EQL_EHIP; }
 
 // Fixed per-stage cost of a forward tile in units of one 32-column block's MFMAs.
 constexpr int64_t kFwdStageFixed = 5;
+// A tile's epilogue (inverse transform and stores, not overlapped with MFMAs) per
+// 32-column block, in the same units.
+constexpr int64_t kFwdEpilogueBlock = 21;
 
 // Compute units of the current device (cached per device; 256 on MI355X).  The
 // persistent kernels launch one workgroup per compute unit.
@@ -132,14 +135,23 @@ int run_fwd(const void* x, const void* wp, void* y, int64_t N, int64_t Cin, int6
   const int cus = device_cus();
   // Tile width (32-column blocks): the persistent grid takes ceil(tiles / CUs) rounds,
   // and a tile costs about kFwdStageFixed + nb block-units per K stage (the stage's
-  // barrier, x load and transform measure about five blocks' MFMA time).  Fewest
-  // estimated units wins; ties go to the wider tile, which moves fewer bytes per FLOP.
+  // barrier, x load and transform measure about five blocks' MFMA time) plus
+  // kFwdEpilogueBlock per block for its epilogue, which weighs in on short K (c2's
+  // forward, 6 stages: 64-column tiles 8% faster than 128-column ones, as this predicts).
+  // Fewest estimated units wins; ties go to the wider tile, which moves fewer bytes per
+  // FLOP.  EQL_FWD_NB=1|2|4 forces the width where it applies (for measurement).
   int nb = 1;
   if (rowsAligned) {
     int64_t best = -1;
+    static const int forcedNb = [] {
+      const char* v = std::getenv("EQL_FWD_NB");
+      return v && (std::strcmp(v, "1") == 0 || std::strcmp(v, "2") == 0 || std::strcmp(v, "4") == 0) ? std::atoi(v) : 0;
+    }();
     for (int cand = nbm; cand >= 1; cand /= 2) {
+      if (forcedNb && cand != forcedNb && forcedNb <= nbm) continue;
       const int64_t rounds = ceil_div(rowTiles * ceil_div(Dout, 32 * cand), (int64_t)cus);
-      const int64_t cost = rounds * (kFwdStageFixed + cand);
+      const int64_t nst = padded_groups(Cin, dtype) / 2;
+      const int64_t cost = rounds * (nst * (kFwdStageFixed + cand) + kFwdEpilogueBlock * cand);
       if (best < 0 || cost < best) {
         best = cost;
         nb = cand;

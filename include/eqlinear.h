@@ -124,7 +124,10 @@ int eqlinear_pack_weight(const void* w, void* w_packed, int64_t Dp, int64_t Cp, 
  * One fused kernel: group DFT of x in the GEMM prologue, per-frequency MFMA
  * GEMMs, inverse DFT (with its 1/T scaling) in the epilogue; no intermediate
  * global writes ("Implementacao": fused data flow, Fourier fragments held in
- * registers and shared memory).
+ * registers and shared memory).  The output tile width (32, 64 or 128 channels) is
+ * chosen per shape; the environment variable EQL_FWD_NB=1|2|4, read once per process,
+ * forces it where the shape allows (for measurement; it applies to every forward-kernel
+ * launch, the input gradient's included).
  */
 int eqlinear_fwd(const void* x, const void* w_packed, void* y, int64_t N, int64_t Cp,
                  int64_t Dp, int T, int dtype, void* stream);
