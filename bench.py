@@ -362,7 +362,8 @@ def main():
                                reps=max(5, min(args.steps, 20)))
         fused["plain_fwd_ms"] = round(per["fwd"], 4)
         fused["mlp_train_step"] = mlp_train_step(torch, eql, x, w, wp, wpb, b, dy, y, dx, dw, ws, ws_bytes,
-                                                 N, Cp, Dp, T, code, sptr, reps=max(5, min(args.steps, 20)))
+                                                 N, Cp, Dp, T, code, sptr, reps=max(5, min(args.steps, 20)),
+                                                 train=args.step == "train")
         del b
 
     cpu = None
@@ -473,10 +474,12 @@ def fused_epilogue(torch, eql, x, wp, b, r, y, N, Cp, Dp, T, code, sptr, reps):
     return res
 
 
-def mlp_train_step(torch, eql, x, w, wp, wpb, b, dy, y, dx, dw, ws, ws_bytes, N, Cp, Dp, T, code, sptr, reps):
+def mlp_train_step(torch, eql, x, w, wp, wpb, b, dy, y, dx, dw, ws, ws_bytes, N, Cp, Dp, T, code, sptr, reps,
+                   train=True):
     """One training step of the layer as an MLP expansion, y = GELU(x W^T + b): the
     library's pack (both forms), fused forward keeping pre, epilogue backward (dpre,
-    dbias), input and weight gradients on dpre; against the unrolled dense layer in
+    dbias), input and weight gradients on dpre (train: through eqlinear_fwd_fused_train,
+    eqlinear_bwd_x_train and eqlinear_bwd_w_train); against the unrolled dense layer in
     torch (F.linear with the repeated bias, F.gelu, gelu_backward, the bias sum, the two
     gradient matmuls, and the fold of the dense weight gradient onto the T tied entries
     of each (d, c)).  Both produce y, dx, dw and db."""
@@ -496,10 +499,18 @@ def mlp_train_step(torch, eql, x, w, wp, wpb, b, dy, y, dx, dw, ws, ws_bytes, N,
     def lib_step():
         eql.eqlinear_pack_weight(w, wp, Dp, Cp, T, code, eql.EQL_PACK_FWD, sptr)
         eql.eqlinear_pack_weight(w, wpb, Dp, Cp, T, code, eql.EQL_PACK_BWDX, sptr)
-        eql.eqlinear_fwd_fused(x, wp, b, None, y, pre, N, Cp, Dp, T, code, eql.EQL_ACT_GELU, sptr)
+        if train:
+            eql.eqlinear_fwd_fused_train(x, wp, b, None, y, pre, ws, ws_bytes, N, Cp, Dp, T, code, eql.EQL_ACT_GELU,
+                                         sptr)
+        else:
+            eql.eqlinear_fwd_fused(x, wp, b, None, y, pre, N, Cp, Dp, T, code, eql.EQL_ACT_GELU, sptr)
         eql.eqlinear_fused_epilogue_bwd(dy, pre, dpre, db, ews, ebytes, N, Dp, T, code, eql.EQL_ACT_GELU, sptr)
-        eql.eqlinear_bwd_x(dpre, wpb, dx, N, Cp, Dp, T, code, sptr)
-        eql.eqlinear_bwd_w(x, dpre, dw, ws, ws_bytes, N, Cp, Dp, T, code, sptr)
+        if train:
+            eql.eqlinear_bwd_x_train(dpre, wpb, dx, ws, ws_bytes, N, Cp, Dp, T, code, sptr)
+            eql.eqlinear_bwd_w_train(dpre, dw, ws, ws_bytes, N, Cp, Dp, T, code, sptr)
+        else:
+            eql.eqlinear_bwd_x(dpre, wpb, dx, N, Cp, Dp, T, code, sptr)
+            eql.eqlinear_bwd_w(x, dpre, dw, ws, ws_bytes, N, Cp, Dp, T, code, sptr)
 
     def torch_step():
         pre_t = F.linear(x, Wd, bb)
@@ -525,9 +536,11 @@ def mlp_train_step(torch, eql, x, w, wp, wpb, b, dy, y, dx, dw, ws, ws_bytes, N,
 
     res = {"lib_ms": round(timeit(lib_step), 4), "torch_dense_ms": round(timeit(torch_step), 4)}
     res["speedup"] = round(res["torch_dense_ms"] / res["lib_ms"], 3)
-    res["kind"] = ("pack x2 + eqlinear_fwd_fused(bias, GELU, pre) + eqlinear_fused_epilogue_bwd + bwd_x + bwd_w, "
-                   "vs torch on the unrolled dense weight (F.linear, F.gelu, gelu_backward, bias sum, mm x2, "
-                   "weight-gradient fold)")
+    lib_kind = ("pack x2 + eqlinear_fwd_fused_train(bias, GELU, pre) + eqlinear_fused_epilogue_bwd + "
+                "bwd_x_train + bwd_w_train" if train else
+                "pack x2 + eqlinear_fwd_fused(bias, GELU, pre) + eqlinear_fused_epilogue_bwd + bwd_x + bwd_w")
+    res["kind"] = lib_kind + (", vs torch on the unrolled dense weight (F.linear, F.gelu, gelu_backward, bias sum, "
+                              "mm x2, weight-gradient fold)")
     del Wd, pre, dpre, ews
     torch.cuda.empty_cache()
     return res

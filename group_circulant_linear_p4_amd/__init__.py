@@ -26,7 +26,7 @@ __all__ = [
     "eqlinear_fused_epilogue_bwd_workspace_bytes", "eqlinear_fused_epilogue_bwd",
     "eqlinear_fused_epilogue_bwd_noalloc", "EQL_NOALLOC_SCRATCH_BYTES",
     "eqlinear_bwd_w_workspace_bytes", "eqlinear_bwd_w",
-    "eqlinear_fwd_train", "eqlinear_bwd_x_train", "eqlinear_bwd_w_train",
+    "eqlinear_fwd_train", "eqlinear_fwd_fused_train", "eqlinear_bwd_x_train", "eqlinear_bwd_w_train",
     "eqlinear_p4m_expand_weight", "eqlinear_p4m_fold_weight_grad",
 ]
 
@@ -91,6 +91,8 @@ def lib() -> ctypes.CDLL:
         for name in ("eqlinear_fwd_train", "eqlinear_bwd_x_train"):
             getattr(L, name).argtypes = [vp, vp, vp, vp, sz, i64, i64, i64, i32, i32, vp]
             getattr(L, name).restype = i32
+        L.eqlinear_fwd_fused_train.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i32, i32, i32, vp]
+        L.eqlinear_fwd_fused_train.restype = i32
         L.eqlinear_bwd_w_train.argtypes = [vp, vp, vp, sz, i64, i64, i64, i32, i32, vp]
         L.eqlinear_bwd_w_train.restype = i32
         _lib = L
@@ -207,6 +209,14 @@ def eqlinear_fwd_train(x, w_packed, y, workspace, ws_bytes: int, N: int, Cp: int
     """eqlinear_fwd that also leaves x's half spectrum in the weight-gradient workspace."""
     _check(lib().eqlinear_fwd_train(_ptr(x), _ptr(w_packed), _ptr(y), _ptr(workspace), ws_bytes, N, Cp, Dp, T,
                                     _dtype(dtype), _stream(stream)), "eqlinear_fwd_train")
+
+
+def eqlinear_fwd_fused_train(x, w_packed, bias, residual, y, pre_out, workspace, ws_bytes: int, N: int, Cp: int,
+                             Dp: int, T: int, dtype, act: int, stream=None) -> None:
+    """eqlinear_fwd_fused that also leaves x's half spectrum in the weight-gradient workspace."""
+    _check(lib().eqlinear_fwd_fused_train(_ptr(x), _ptr(w_packed), _ptr(bias), _ptr(residual), _ptr(y), _ptr(pre_out),
+                                          _ptr(workspace), ws_bytes, N, Cp, Dp, T, _dtype(dtype), int(act),
+                                          _stream(stream)), "eqlinear_fwd_fused_train")
 
 
 def eqlinear_bwd_x_train(dy, w_packed_bwdx, dx, workspace, ws_bytes: int, N: int, Cp: int, Dp: int, T: int, dtype,

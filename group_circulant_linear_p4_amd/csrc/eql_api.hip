@@ -202,7 +202,7 @@ int run_fwd(const void* x, const void* wp, void* y, int64_t N, int64_t Cin, int6
       a.specGrid = gs;
       const int64_t plain = rowTiles * (colTiles - 1);
       const unsigned grid = (unsigned)(gs + std::min<int64_t>(plain, std::max(cus - gs, 8)));
-      e = launch_fwd_spec_f16(nb, a, grid, s);
+      e = launch_fwd_spec_f16(nb, epi, a, grid, s);
     } else {
       const unsigned grid = (unsigned)std::min<int64_t>(a.numTiles, cus);
       e = epi ? (dtype == EQL_F16 ? launch_fwd_fused_f16(T, nb, a, grid, s) : launch_fwd_fused_f32(T, nb, a, grid, s))
@@ -621,7 +621,7 @@ int run_bwdw(const void* x, const void* dy, void* dw, void* workspace, size_t ws
 
 extern "C" {
 
-int eqlinear_abi_version(void) { return 203; }
+int eqlinear_abi_version(void) { return 204; }
 
 const char* eqlinear_status_string(int status) {
   switch (status) {
@@ -730,6 +730,27 @@ int eqlinear_fwd_train(const void* x, const void* w_packed, void* y, void* works
     return run_fwd(x, w_packed, y, N, Cp, Dp, T, dtype, stream, false, nullptr, nullptr, 0, nullptr, xh, p.Cpad,
                    p.xhBytes);
   st = run_fwd(x, w_packed, y, N, Cp, Dp, T, dtype, stream);
+  if (st != EQL_OK) return st;
+  return run_spec(x, xh, N, Cp, p.Cpad, p.kgCount, T, dtype, static_cast<hipStream_t>(stream));
+}
+
+int eqlinear_fwd_fused_train(const void* x, const void* w_packed, const void* bias, const void* residual, void* y,
+                             void* pre_out, void* workspace, size_t ws_bytes, int64_t N, int64_t Cp, int64_t Dp, int T,
+                             int dtype, int act, void* stream) {
+  if (act != EQL_ACT_NONE && act != EQL_ACT_GELU) return EQL_EINVAL;
+  int st = check_sizes(N, Cp, Dp, T, dtype);
+  if (st != EQL_OK) return st;
+  if (N == 0) return EQL_OK;
+  const BwdwPlan p = plan_bwdw(N, Cp, Dp, T, dtype);
+  if (!workspace || ws_bytes < p.total()) return EQL_EINVAL;
+  if (!aligned16(workspace)) return EQL_EALIGN;
+  if (bias && (reinterpret_cast<uintptr_t>(bias) % (uintptr_t)elt_bytes(dtype)) != 0) return EQL_EALIGN;
+  if ((residual && !aligned16(residual)) || (pre_out && !aligned16(pre_out))) return EQL_EALIGN;
+  void* xh = static_cast<char*>(workspace) + p.dyhBytes;
+  if (fwd_spec_ok(Cp, T, dtype, p.xhBytes, p.Cpad))
+    return run_fwd(x, w_packed, y, N, Cp, Dp, T, dtype, stream, true, bias, residual, act, pre_out, xh, p.Cpad,
+                   p.xhBytes);
+  st = run_fwd(x, w_packed, y, N, Cp, Dp, T, dtype, stream, true, bias, residual, act, pre_out);
   if (st != EQL_OK) return st;
   return run_spec(x, xh, N, Cp, p.Cpad, p.kgCount, T, dtype, static_cast<hipStream_t>(stream));
 }

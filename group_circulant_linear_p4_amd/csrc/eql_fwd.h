@@ -654,7 +654,7 @@ __host__ __device__ constexpr int fwd4_waves(int T, int NB) { return NB >= 2 && 
 //     wait for this wave's loads of stage g+1, barrier, issue stage g+3, read x of
 //     stage g+1, then per column block: next block's fragments, the block's MFMAs,
 //     and after block 0 the transform of x stage g+1 into the other fragment buffer.
-//   * SPEC = 1 (p4 fp16, plain epilogue): the workgroups below FwdArgs::specGrid take the
+//   * SPEC = 1 (p4 fp16, either epilogue): the workgroups below FwdArgs::specGrid take the
 //     tiles of output column 0 and run the loop with the spectrum side output; the others
 //     take the remaining columns with the plain loop.  In the storing loop each wave also
 //     transposes its transformed x fragments (8 rows x 8 channels per 8 lanes, by DPP)
@@ -701,7 +701,7 @@ __device__ __forceinline__ void fwd4_body(const FwdArgs& a, uint32_t ldsB, uint3
   constexpr int WAIT_TOP = (DIST - 2) * (IPW + IPWX);
   constexpr int WAIT_PRO = (DIST - 1) * (IPW + IPWX);
   static_assert(WAIT_PRO < 64, "vmcnt range");
-  static_assert(!SPEC || (T == 4 && ELT == 2 && EPI == 0), "spectrum side output: p4 fp16, plain epilogue");
+  static_assert(!SPEC || (T == 4 && ELT == 2), "spectrum side output: p4 fp16");
 
   if (b0 >= numTiles) return;
   const int myTiles = (numTiles - b0 + grid - 1) / grid;

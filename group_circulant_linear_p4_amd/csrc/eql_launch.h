@@ -30,8 +30,9 @@ hipError_t launch_fwd_f32(int T, int NB, const FwdArgs& a, unsigned grid, hipStr
 hipError_t launch_fwd_fused_f16(int T, int NB, const FwdArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_fwd_fused_f32(int T, int NB, const FwdArgs& a, unsigned grid, hipStream_t s);
 // The forward kernel that also stores the transformed input of the column-0 tiles
-// as weight-gradient operand units (p4 fp16, 16-byte rows; FwdArgs::spec).
-hipError_t launch_fwd_spec_f16(int NB, const FwdArgs& a, unsigned grid, hipStream_t s);
+// as weight-gradient operand units (p4 fp16, 16-byte rows; FwdArgs::spec), with the
+// plain or (epi) the fused epilogue.
+hipError_t launch_fwd_spec_f16(int NB, bool epi, const FwdArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_spec_f16(int T, const SpecArgs& a, unsigned grid, hipStream_t s);
 hipError_t launch_spec_f32(int T, const SpecArgs& a, unsigned grid, hipStream_t s);
 // Weight-gradient GEMMs: the real planes' (DB, CB in {4, 1}) and the complex pairs'

@@ -10,8 +10,8 @@ needs a gradient, the three passes are the training entry points instead
 weight-gradient workspace, holding x's half spectrum, alive until the backward.  EQLinearP4M is the
 layer over p4m's point group (rotations and reflections), run through the same kernels on
 the C_4 view described in include/eqlinear.h.  With a bias,
-GELU or a residual, the forward is eqlinear_fwd_fused and the backward starts with
-eqlinear_fused_epilogue_bwd.  Torch only allocates the buffers; every arithmetic step
+GELU or a residual, the forward is eqlinear_fwd_fused (eqlinear_fwd_fused_train when the
+weight needs a gradient) and the backward starts with eqlinear_fused_epilogue_bwd.  Torch only allocates the buffers; every arithmetic step
 runs in the HIP library.
 """
 from __future__ import annotations
@@ -22,7 +22,7 @@ import torch
 
 from . import (EQL_ACT_GELU, EQL_ACT_NONE, EQL_PACK_BWDX, EQL_PACK_FWD, eqlinear_bwd_w,
                eqlinear_bwd_w_train, eqlinear_bwd_w_workspace_bytes, eqlinear_bwd_x,
-               eqlinear_bwd_x_train, eqlinear_fused_epilogue_bwd, eqlinear_fwd_train,
+               eqlinear_bwd_x_train, eqlinear_fused_epilogue_bwd, eqlinear_fwd_fused_train, eqlinear_fwd_train,
                eqlinear_fused_epilogue_bwd_workspace_bytes, eqlinear_fwd, eqlinear_fwd_fused,
                eqlinear_p4m_expand_weight, eqlinear_p4m_fold_weight_grad, eqlinear_pack_weight,
                eqlinear_packed_weight_bytes)
@@ -136,16 +136,25 @@ class EQLinearFusedFunction(torch.autograd.Function):
         # pre is kept only when a backward can follow.
         keep = code == EQL_ACT_GELU and grad_mode and any(ctx.needs_input_grad[:3])
         pre = torch.empty_like(y) if keep else None
-        eqlinear_fwd_fused(x2, _packed(w, EQL_PACK_FWD), b.contiguous() if b is not None else None, r2, y, pre,
-                           N, Cp, Dp, T, x.dtype, code)
-        ctx.save_for_backward(x2, w, pre)
+        bc = b.contiguous() if b is not None else None
+        ws_bytes = eqlinear_bwd_w_workspace_bytes(N, Cp, Dp, T, x.dtype)
+        if grad_mode and ctx.needs_input_grad[1]:
+            # The weight gradient will follow: keep x's spectrum in its workspace.
+            wsw = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=x.device)
+            eqlinear_fwd_fused_train(x2, _packed(w, EQL_PACK_FWD), bc, r2, y, pre, wsw, ws_bytes, N, Cp, Dp, T,
+                                     x.dtype, code)
+        else:
+            wsw = None
+            eqlinear_fwd_fused(x2, _packed(w, EQL_PACK_FWD), bc, r2, y, pre, N, Cp, Dp, T, x.dtype, code)
+        ctx.save_for_backward(x2, w, pre, wsw)
+        ctx.ws_bytes = ws_bytes
         ctx.code, ctx.has_bias, ctx.lead_shape = code, b is not None, x.shape[:-1]
         ctx.res_shape = r.shape if r is not None else None
         return y.reshape(*x.shape[:-1], Dp * T)
 
     @staticmethod
     def backward(ctx, dy: torch.Tensor):
-        x2, w, pre = ctx.saved_tensors
+        x2, w, pre, wsw = ctx.saved_tensors
         Dp, Cp, T = w.shape
         N = x2.shape[0]
         dy2 = dy.reshape(-1, Dp * T).to(x2.dtype).contiguous()
@@ -161,15 +170,24 @@ class EQLinearFusedFunction(torch.autograd.Function):
             ws_bytes = eqlinear_fused_epilogue_bwd_workspace_bytes(N, Dp, T, x2.dtype)
             ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=x2.device)
             eqlinear_fused_epilogue_bwd(dy2, pre, dpre, db, ws, ws_bytes, N, Dp, T, x2.dtype, ctx.code)
+        # With a weight gradient the training entry points run on dpre: the input gradient
+        # leaves dpre's spectrum beside x's (from the forward) in the workspace.
+        train = wsw is not None and ctx.needs_input_grad[1]
         if ctx.needs_input_grad[0]:
             dx = torch.empty((N, Cp * T), dtype=x2.dtype, device=x2.device)
-            eqlinear_bwd_x(dpre, _packed(w, EQL_PACK_BWDX), dx, N, Cp, Dp, T, x2.dtype)
+            if train:
+                eqlinear_bwd_x_train(dpre, _packed(w, EQL_PACK_BWDX), dx, wsw, ctx.ws_bytes, N, Cp, Dp, T, x2.dtype)
+            else:
+                eqlinear_bwd_x(dpre, _packed(w, EQL_PACK_BWDX), dx, N, Cp, Dp, T, x2.dtype)
             dx = dx.reshape(*ctx.lead_shape, Cp * T)
         if ctx.needs_input_grad[1]:
-            wsw = eqlinear_bwd_w_workspace_bytes(N, Cp, Dp, T, x2.dtype)
-            wsb = torch.empty(max(wsw, 16), dtype=torch.uint8, device=x2.device)
             dw = torch.empty_like(w)
-            eqlinear_bwd_w(x2, dpre, dw, wsb, wsw, N, Cp, Dp, T, x2.dtype)
+            if train and ctx.needs_input_grad[0]:
+                eqlinear_bwd_w_train(dpre, dw, wsw, ctx.ws_bytes, N, Cp, Dp, T, x2.dtype)
+            else:
+                wsb = wsw if wsw is not None else torch.empty(max(ctx.ws_bytes, 16), dtype=torch.uint8,
+                                                              device=x2.device)
+                eqlinear_bwd_w(x2, dpre, dw, wsb, ctx.ws_bytes, N, Cp, Dp, T, x2.dtype)
         return dx, dw, db, dr, None, None
 
 

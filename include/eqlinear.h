@@ -294,6 +294,18 @@ int eqlinear_fwd_train(const void* x, const void* w_packed, void* y, void* works
                        int64_t N, int64_t Cp, int64_t Dp, int T, int dtype, void* stream);
 int eqlinear_bwd_x_train(const void* dy, const void* w_packed_bwdx, void* dx, void* workspace, size_t ws_bytes,
                          int64_t N, int64_t Cp, int64_t Dp, int T, int dtype, void* stream);
+
+/*
+ * eqlinear_fwd_fused with the training forward's side output: y and pre_out exactly as
+ * eqlinear_fwd_fused (arguments, results and errors as there), and x's half spectrum in
+ * the weight-gradient workspace as eqlinear_fwd_train leaves it (workspace and ws_bytes
+ * as there).  For a layer with the fused epilogue the training step is then this call,
+ * eqlinear_fused_epilogue_bwd (dpre), and eqlinear_bwd_x_train / eqlinear_bwd_w_train on
+ * dpre, with the same contract as above.
+ */
+int eqlinear_fwd_fused_train(const void* x, const void* w_packed, const void* bias, const void* residual, void* y,
+                             void* pre_out, void* workspace, size_t ws_bytes, int64_t N, int64_t Cp, int64_t Dp, int T,
+                             int dtype, int act, void* stream);
 int eqlinear_bwd_w_train(const void* dy, void* dw, void* workspace, size_t ws_bytes, int64_t N, int64_t Cp,
                          int64_t Dp, int T, int dtype, void* stream);
 
@@ -336,7 +348,7 @@ const char* eqlinear_status_string(int status);
  * layout above (1.xx stored ((o * Jin + i / G) * T + p) * G + i % G).  2.01:
  * eqlinear_fused_epilogue_bwd_noalloc and EQL_ESCRATCH.  2.02: the p4m entry points.
  * 2.03: the training-step entry points (eqlinear_fwd_train, eqlinear_bwd_x_train,
- * eqlinear_bwd_w_train). */
+ * eqlinear_bwd_w_train).  2.04: eqlinear_fwd_fused_train. */
 int eqlinear_abi_version(void);
 
 #ifdef __cplusplus

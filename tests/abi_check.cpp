@@ -35,7 +35,7 @@ void* const MIS2 = reinterpret_cast<void*>(uintptr_t{0x10002});
 constexpr int F16 = EQL_F16, F32 = EQL_F32;
 
 void sizes() {
-  CHECK(eqlinear_abi_version() == 203);
+  CHECK(eqlinear_abi_version() == 204);
   for (int s = -3; s < 12; ++s) CHECK(eqlinear_status_string(s) != nullptr && std::strlen(eqlinear_status_string(s)) > 0);
   // Packed weight: out channels padded to 32, input 16-byte groups padded per stage.
   CHECK(eqlinear_packed_weight_bytes(3, 5, 4, F16) == 32u * 4 * 16 * 4);
@@ -129,6 +129,17 @@ void validation() {
   CHECK(eqlinear_fwd_train(A, B, C, D, ws, 300, 5, 7, 20, F16, nullptr) == EQL_EUNSUPPORTED);
   CHECK(eqlinear_fwd_train(A, B, C, D, SIZE_MAX, INT64_MAX, 5, 7, 4, F16, nullptr) == EQL_EINVAL);
   CHECK(eqlinear_fwd_train(nullptr, nullptr, nullptr, nullptr, 0, 0, 5, 7, 4, F16, nullptr) == EQL_OK);
+  CHECK(eqlinear_fwd_fused_train(A, B, nullptr, nullptr, C, nullptr, D, ws - 1, 300, 5, 7, 4, F16, 0, nullptr) == EQL_EINVAL);
+  CHECK(eqlinear_fwd_fused_train(A, B, nullptr, nullptr, C, nullptr, nullptr, ws, 300, 5, 7, 4, F16, 0, nullptr) == EQL_EINVAL);
+  CHECK(eqlinear_fwd_fused_train(A, B, nullptr, nullptr, C, nullptr, MIS, ws, 300, 5, 7, 4, F16, 0, nullptr) == EQL_EALIGN);
+  CHECK(eqlinear_fwd_fused_train(A, B, nullptr, nullptr, C, nullptr, D, ws, 300, 5, 7, 4, F16, 7, nullptr) == EQL_EINVAL);
+  CHECK(eqlinear_fwd_fused_train(A, B, MIS2, nullptr, C, nullptr, D, eqlinear_bwd_w_workspace_bytes(300, 5, 7, 4, F32),
+                                 300, 5, 7, 4, F32, 1, nullptr) == EQL_EALIGN);
+  CHECK(eqlinear_fwd_fused_train(A, B, nullptr, MIS, C, nullptr, D, ws, 300, 5, 7, 4, F16, 1, nullptr) == EQL_EALIGN);
+  CHECK(eqlinear_fwd_fused_train(A, B, nullptr, nullptr, C, MIS, D, ws, 300, 5, 7, 4, F16, 1, nullptr) == EQL_EALIGN);
+  CHECK(eqlinear_fwd_fused_train(MIS, B, nullptr, nullptr, C, nullptr, D, wf, 300, 8, 8, 4, F16, 1, nullptr) == EQL_EALIGN);
+  CHECK(eqlinear_fwd_fused_train(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0, 5, 7, 4, F16, 1,
+                                 nullptr) == EQL_OK);
   CHECK(eqlinear_bwd_x_train(A, B, C, D, ws - 1, 300, 5, 7, 4, F16, nullptr) == EQL_EINVAL);
   CHECK(eqlinear_bwd_x_train(A, B, C, nullptr, ws, 300, 5, 7, 4, F16, nullptr) == EQL_EINVAL);
   CHECK(eqlinear_bwd_x_train(A, B, C, MIS, ws, 300, 5, 7, 4, F16, nullptr) == EQL_EALIGN);

@@ -241,3 +241,50 @@ def test_layer_autograd_through_training_entry_points(grads):
         assert rel_err(w.grad.cpu().numpy(), oracle.bwd_w(x_h, dy_h, T)) <= TOL["f16"]
     else:
         assert w.grad is None
+
+
+FUSED_TRAIN_CASES = [(4, "f16", 1000, 600, 600), (4, "f16", 300, 96, 384), (4, "f16", 500, 601, 600),
+                     (3, "f32", 257, 33, 41), (8, "f16", 200, 130, 70)]
+
+
+@pytest.mark.parametrize("case", FUSED_TRAIN_CASES, ids=lambda c: "T%d_%s_N%d_C%d_D%d" % c)
+def test_fused_train_step(case):
+    """eqlinear_fwd_fused_train (bias, GELU, residual, pre kept): y and pre bit-identical to
+    eqlinear_fwd_fused, x's spectrum as the separate transform leaves it; then the epilogue
+    backward and the training input and weight gradients on dpre against the oracle."""
+    T, dtype, N, Cp, Dp = case
+    code = DT[dtype]
+    wl = W.Workload("t", "test", T, N, Cp, Dp, dtype, ("fwd", "bwd_x", "bwd_w"), seed=80 + T)
+    x, w, dy, b, r = W.make_x(wl), W.make_w(wl), W.make_dy(wl), W.make_bias(wl), W.make_residual(wl)
+    xd, wd, dyd, bd, rd = (torch.from_numpy(a).to(DEV) for a in (x, w, dy, b, r))
+    wp = torch.empty(eql.eqlinear_packed_weight_bytes(Dp, Cp, T, code), dtype=torch.uint8, device=DEV)
+    wpb = torch.empty(eql.eqlinear_packed_weight_bytes(Cp, Dp, T, code), dtype=torch.uint8, device=DEV)
+    eql.eqlinear_pack_weight(wd, wp, Dp, Cp, T, code, eql.EQL_PACK_FWD)
+    eql.eqlinear_pack_weight(wd, wpb, Dp, Cp, T, code, eql.EQL_PACK_BWDX)
+    nbytes = eql.eqlinear_bwd_w_workspace_bytes(N, Cp, Dp, T, code)
+    ws = torch.full((max(nbytes, 16),), 0xFF, dtype=torch.uint8, device=DEV)
+    ws_ref = torch.empty_like(ws)
+    y, pre, y0, pre0, dpre = (torch.empty((N, Dp * T), dtype=xd.dtype, device=DEV) for _ in range(5))
+    dx = torch.empty((N, Cp * T), dtype=xd.dtype, device=DEV)
+    dw, dw0 = torch.empty((Dp, Cp, T), dtype=xd.dtype, device=DEV), torch.empty((Dp, Cp, T), dtype=xd.dtype,
+                                                                                 device=DEV)
+    db = torch.empty(Dp, dtype=xd.dtype, device=DEV)
+    ebytes = eql.eqlinear_fused_epilogue_bwd_workspace_bytes(N, Dp, T, code)
+    ews = torch.empty(max(ebytes, 16), dtype=torch.uint8, device=DEV)
+    print("case fused train T=%d %s N=%d C'=%d D'=%d" % case, flush=True)
+    eql.eqlinear_fwd_fused_train(xd, wp, bd, rd, y, pre, ws, nbytes, N, Cp, Dp, T, code, eql.EQL_ACT_GELU)
+    torch.cuda.synchronize()
+    ws_after = ws.clone()
+    eql.eqlinear_fused_epilogue_bwd(dyd, pre, dpre, db, ews, ebytes, N, Dp, T, code, eql.EQL_ACT_GELU)
+    eql.eqlinear_bwd_x_train(dpre, wpb, dx, ws, nbytes, N, Cp, Dp, T, code)
+    eql.eqlinear_bwd_w_train(dpre, dw, ws, nbytes, N, Cp, Dp, T, code)
+    eql.eqlinear_fwd_fused(xd, wp, bd, rd, y0, pre0, N, Cp, Dp, T, code, eql.EQL_ACT_GELU)
+    eql.eqlinear_bwd_w(xd, dpre, dw0, ws_ref, nbytes, N, Cp, Dp, T, code)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y0) and torch.equal(pre, pre0), "eqlinear_fwd_fused_train changed y or pre"
+    _, xs = spectrum_sections(N, Cp, Dp, T, xd.element_size())
+    check_spectra(planes_of(ws_after, xs, N, T, dtype), planes_of(ws_ref, xs, N, T, dtype), x, T, dtype,
+                  "x spectrum (fused forward)")
+    dpre_h = dpre.cpu().numpy()
+    assert rel_err(dx.cpu().numpy(), oracle.bwd_x(dpre_h, w)) <= TOL[dtype]
+    assert rel_err(dw.cpu().numpy(), oracle.bwd_w(x, dpre_h, T)) <= TOL[dtype]
