@@ -574,16 +574,19 @@ def test_fused_epilogue_bwd_empty_and_pre_out():
     assert rel_err(host(y), oracle.fwd_fused(x, w, bias=b, act="gelu")) <= TOL[dtype]
 
 
-@pytest.mark.parametrize("fused", [False, True], ids=["plain", "fused_bias_gelu"])
-def test_graph_replay_matches_eager(fused):
+@pytest.mark.parametrize("mode", ["plain", "fused_bias_gelu", "train", "fused_train"])
+def test_graph_replay_matches_eager(mode):
     """One training step captured in a HIP graph and replayed three times: pack, forward,
     input gradient and weight gradient; with `fused`, the forward with bias + GELU that
-    keeps pre, the epilogue's backward (dpre, dbias), and both gradients on dpre.
+    keeps pre, the epilogue's backward (dpre, dbias), and both gradients on dpre; with
+    `train`, the training entry points (spectra kept in the workspace between the passes,
+    on a shape whose weight gradient takes the separate path).
     Between replays the inputs are rewritten in place and other eager work runs; every
     replay must equal the eager result for the same inputs bit for bit (the library
     allocates nothing and records no memset, so the captured step is the eager one)."""
-    T, N, Cp, Dp, dtype = 4, 700, 72, 96, "f16"
-    print("case graph replay fused=%d" % fused, flush=True)
+    fused, train = mode.startswith("fused"), mode.endswith("train")
+    T, N, Cp, Dp, dtype = (4, 700, 600, 520, "f16") if train else (4, 700, 72, 96, "f16")
+    print("case graph replay %s" % mode, flush=True)
     code = DT[dtype]
     bufs = [inputs(T, N, Cp, Dp, dtype, seed=60 + i) for i in range(4)]
     biases = [W.make_bias(W.Workload("t", "test", T, N, Cp, Dp, dtype, ("fwd",), seed=70 + i)) for i in range(4)]
@@ -605,14 +608,25 @@ def test_graph_replay_matches_eager(fused):
         eql.eqlinear_pack_weight(w_d, wp, Dp, Cp, T, code, eql.EQL_PACK_FWD)
         eql.eqlinear_pack_weight(w_d, wpb, Dp, Cp, T, code, eql.EQL_PACK_BWDX)
         if fused:
-            eql.eqlinear_fwd_fused(x_d, wp, b_d, None, y, pre, N, Cp, Dp, T, code, eql.EQL_ACT_GELU)
+            if train:
+                eql.eqlinear_fwd_fused_train(x_d, wp, b_d, None, y, pre, ws, nbytes, N, Cp, Dp, T, code,
+                                             eql.EQL_ACT_GELU)
+            else:
+                eql.eqlinear_fwd_fused(x_d, wp, b_d, None, y, pre, N, Cp, Dp, T, code, eql.EQL_ACT_GELU)
             eql.eqlinear_fused_epilogue_bwd(dy_d, pre, dpre, db, ews, ebytes, N, Dp, T, code, eql.EQL_ACT_GELU)
             g_out = dpre
         else:
-            eql.eqlinear_fwd(x_d, wp, y, N, Cp, Dp, T, code)
+            if train:
+                eql.eqlinear_fwd_train(x_d, wp, y, ws, nbytes, N, Cp, Dp, T, code)
+            else:
+                eql.eqlinear_fwd(x_d, wp, y, N, Cp, Dp, T, code)
             g_out = dy_d
-        eql.eqlinear_bwd_x(g_out, wpb, dx, N, Cp, Dp, T, code)
-        eql.eqlinear_bwd_w(x_d, g_out, dw, ws, nbytes, N, Cp, Dp, T, code)
+        if train:
+            eql.eqlinear_bwd_x_train(g_out, wpb, dx, ws, nbytes, N, Cp, Dp, T, code)
+            eql.eqlinear_bwd_w_train(g_out, dw, ws, nbytes, N, Cp, Dp, T, code)
+        else:
+            eql.eqlinear_bwd_x(g_out, wpb, dx, N, Cp, Dp, T, code)
+            eql.eqlinear_bwd_w(x_d, g_out, dw, ws, nbytes, N, Cp, Dp, T, code)
 
     outs = (y, dx, dw) + ((pre, dpre, db) if fused else ())
     side = torch.cuda.Stream()
