@@ -163,6 +163,7 @@ def main():
                              eql.eqlinear_pack_weight(b["w"], b["wpb"], Dp, Cp, T, code, eql.EQL_PACK_BWDX, sp)),
         }
         if mode == "train":
+            calls["pack"] = lambda: eql.eqlinear_pack_weight_both(b["w"], b["wp"], b["wpb"], Dp, Cp, T, code, sp)
             calls["fwd"] = lambda: eql.eqlinear_fwd_train(b["x"], b["wp"], b["y"], b["ws"], ws_bytes, N, Cp, Dp, T,
                                                           code, sp)
             calls["bwd_x"] = lambda: eql.eqlinear_bwd_x_train(b["dy"], b["wpb"], b["dx"], b["ws"], ws_bytes, N, Cp,
@@ -389,7 +390,7 @@ def main():
         "data": "synthetic (seeded; x,dy ~ N(0,1), w ~ N(0,1/C)%s)" % (
             ", %g%% of rows x%g" % (100 * wl.hot_rows_frac, wl.hot_rows_scale) if wl.hot_rows_frac else ""),
         "config": {"workload": wl.name, "T": T, "N": N, "C": Cp * T, "D": Dp * T,
-                   "step": ("pack(fwd)+pack(bwd_x)+fwd_train+bwd_x_train+bwd_w_train" if args.step == "train"
+                   "step": ("pack_both+fwd_train+bwd_x_train+bwd_w_train" if args.step == "train"
                             else "pack(fwd)+pack(bwd_x)+fwd+bwd_x+bwd_w"), "buffer_sets": n_sets,
                    "set_mib": round(set_bytes / 2**20, 1)},
         "warm": warm,
@@ -497,9 +498,11 @@ def mlp_train_step(torch, eql, x, w, wp, wpb, b, dy, y, dx, dw, ws, ws_bytes, N,
     ews = torch.empty(max(ebytes, 16), dtype=torch.uint8, device=y.device)
 
     def lib_step():
-        eql.eqlinear_pack_weight(w, wp, Dp, Cp, T, code, eql.EQL_PACK_FWD, sptr)
-        eql.eqlinear_pack_weight(w, wpb, Dp, Cp, T, code, eql.EQL_PACK_BWDX, sptr)
+        if not train:
+            eql.eqlinear_pack_weight(w, wp, Dp, Cp, T, code, eql.EQL_PACK_FWD, sptr)
+            eql.eqlinear_pack_weight(w, wpb, Dp, Cp, T, code, eql.EQL_PACK_BWDX, sptr)
         if train:
+            eql.eqlinear_pack_weight_both(w, wp, wpb, Dp, Cp, T, code, sptr)
             eql.eqlinear_fwd_fused_train(x, wp, b, None, y, pre, ws, ws_bytes, N, Cp, Dp, T, code, eql.EQL_ACT_GELU,
                                          sptr)
         else:
@@ -536,7 +539,7 @@ def mlp_train_step(torch, eql, x, w, wp, wpb, b, dy, y, dx, dw, ws, ws_bytes, N,
 
     res = {"lib_ms": round(timeit(lib_step), 4), "torch_dense_ms": round(timeit(torch_step), 4)}
     res["speedup"] = round(res["torch_dense_ms"] / res["lib_ms"], 3)
-    lib_kind = ("pack x2 + eqlinear_fwd_fused_train(bias, GELU, pre) + eqlinear_fused_epilogue_bwd + "
+    lib_kind = ("pack_both + eqlinear_fwd_fused_train(bias, GELU, pre) + eqlinear_fused_epilogue_bwd + "
                 "bwd_x_train + bwd_w_train" if train else
                 "pack x2 + eqlinear_fwd_fused(bias, GELU, pre) + eqlinear_fused_epilogue_bwd + bwd_x + bwd_w")
     res["kind"] = lib_kind + (", vs torch on the unrolled dense weight (F.linear, F.gelu, gelu_backward, bias sum, "
@@ -677,6 +680,8 @@ def bench_p4m(args, torch, eql, wl):
                           eql.eqlinear_p4m_fold_weight_grad(dw4, dw, Dp, Cp, code, sp)),
     }
     if args.step == "train":
+        calls["pack"] = lambda: (eql.eqlinear_p4m_expand_weight(w, w4, Dp, Cp, code, sp),
+                                 eql.eqlinear_pack_weight_both(w4, wp, wpb, 2 * Dp, 2 * Cp, 4, code, sp))
         calls["fwd"] = lambda: eql.eqlinear_fwd_train(x, wp, y, ws, ws_bytes, N, 2 * Cp, 2 * Dp, 4, code, sp)
         calls["bwd_x"] = lambda: eql.eqlinear_bwd_x_train(dy, wpb, dx, ws, ws_bytes, N, 2 * Cp, 2 * Dp, 4, code, sp)
         calls["bwd_w"] = lambda: (eql.eqlinear_bwd_w_train(dy, dw4, ws, ws_bytes, N, 2 * Cp, 2 * Dp, 4, code, sp),
@@ -745,7 +750,7 @@ def bench_p4m(args, torch, eql, wl):
             "config": {"workload": "p4m layer on %s's widths: N=%d, C=%d (C'=%d x 8), D=%d (D'=%d x 8)"
                                    % (wl.key, N, C, Cp, D, Dp),
                        "group": "p4m (D4)",
-                       "step": ("expand+pack x2, fwd_train, bwd_x_train, bwd_w_train+fold" if args.step == "train"
+                       "step": ("expand+pack_both, fwd_train, bwd_x_train, bwd_w_train+fold" if args.step == "train"
                                 else "expand+pack x2, fwd, bwd_x, bwd_w+fold")},
             "passes": passes, "pack_ms": round(per["pack"], 4), "roofline": roofline, "cpu_baseline": cpu}
     print(json.dumps(line), flush=True)

@@ -22,7 +22,7 @@ __all__ = [
     "EQL_F32", "EQL_F16", "EQL_PACK_FWD", "EQL_PACK_BWDX", "EQL_ACT_NONE", "EQL_ACT_GELU", "EQL_MAX_T",
     "EqlError",
     "lib", "library_path", "eqlinear_abi_version", "eqlinear_status_string",
-    "eqlinear_packed_weight_bytes", "eqlinear_pack_weight", "eqlinear_fwd", "eqlinear_fwd_fused", "eqlinear_bwd_x",
+    "eqlinear_packed_weight_bytes", "eqlinear_pack_weight", "eqlinear_pack_weight_both", "eqlinear_fwd", "eqlinear_fwd_fused", "eqlinear_bwd_x",
     "eqlinear_fused_epilogue_bwd_workspace_bytes", "eqlinear_fused_epilogue_bwd",
     "eqlinear_fused_epilogue_bwd_noalloc", "EQL_NOALLOC_SCRATCH_BYTES",
     "eqlinear_bwd_w_workspace_bytes", "eqlinear_bwd_w",
@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.eqlinear_packed_weight_bytes.restype = sz
         L.eqlinear_pack_weight.argtypes = [vp, vp, i64, i64, i32, i32, i32, vp]
         L.eqlinear_pack_weight.restype = i32
+        L.eqlinear_pack_weight_both.argtypes = [vp, vp, vp, i64, i64, i32, i32, vp]
+        L.eqlinear_pack_weight_both.restype = i32
         L.eqlinear_fwd.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, vp]
         L.eqlinear_fwd.restype = i32
         L.eqlinear_fwd_fused.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, i32, i32, vp]
@@ -154,6 +156,12 @@ def eqlinear_packed_weight_bytes(out_ch: int, in_ch: int, T: int, dtype) -> int:
 def eqlinear_pack_weight(w, w_packed, Dp: int, Cp: int, T: int, dtype, mode: int, stream=None) -> None:
     _check(lib().eqlinear_pack_weight(_ptr(w), _ptr(w_packed), Dp, Cp, T, _dtype(dtype), mode, _stream(stream)),
            "eqlinear_pack_weight")
+
+
+def eqlinear_pack_weight_both(w, w_packed, w_packed_bwdx, Dp: int, Cp: int, T: int, dtype, stream=None) -> None:
+    """Both packings (forward and input-gradient) in one launch."""
+    _check(lib().eqlinear_pack_weight_both(_ptr(w), _ptr(w_packed), _ptr(w_packed_bwdx), Dp, Cp, T, _dtype(dtype),
+                                           _stream(stream)), "eqlinear_pack_weight_both")
 
 
 def eqlinear_fwd(x, w_packed, y, N: int, Cp: int, Dp: int, T: int, dtype, stream=None) -> None:

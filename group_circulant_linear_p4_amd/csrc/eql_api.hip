@@ -621,7 +621,7 @@ int run_bwdw(const void* x, const void* dy, void* dw, void* workspace, size_t ws
 
 extern "C" {
 
-int eqlinear_abi_version(void) { return 204; }
+int eqlinear_abi_version(void) { return 205; }
 
 const char* eqlinear_status_string(int status) {
   switch (status) {
@@ -663,6 +663,33 @@ int eqlinear_pack_weight(const void* w, void* w_packed, int64_t Dp, int64_t Cp, 
   hipStream_t s = static_cast<hipStream_t>(stream);
   return status_of(dtype == EQL_F16 ? launch_pack_f16(T, a, (unsigned)grid, s)
                                     : launch_pack_f32(T, a, (unsigned)grid, s));
+}
+
+int eqlinear_pack_weight_both(const void* w, void* w_packed, void* w_packed_bwdx, int64_t Dp, int64_t Cp, int T,
+                              int dtype, void* stream) {
+  int st = check_sizes(0, Cp, Dp, T, dtype);
+  if (st != EQL_OK) return st;
+  if (!w || !w_packed || !w_packed_bwdx) return EQL_EINVAL;
+  if (!aligned16(w) || !aligned16(w_packed) || !aligned16(w_packed_bwdx)) return EQL_EALIGN;
+  PackArgs a{};
+  a.w = w;
+  a.wp = w_packed;
+  a.wp2 = w_packed_bwdx;
+  a.Dp = (int)Dp;
+  a.Cp = (int)Cp;
+  a.transposed = 0;
+  a.outCh = (int)Dp;
+  a.inCh = (int)Cp;
+  a.Jin = (int)padded_groups(Cp, dtype);
+  a.Jin2 = (int)padded_groups(Dp, dtype);
+  a.tw = make_twiddles(T);
+  const int64_t g1 = ceil_div(padded_out(Dp) * a.Jin * group_channels(dtype), 256);
+  const int64_t g2 = ceil_div(padded_out(Cp) * a.Jin2 * group_channels(dtype), 256);
+  if (g1 + g2 > kMaxGrid) return EQL_EINVAL;
+  a.blocks1 = (int)g1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return status_of(dtype == EQL_F16 ? launch_pack_f16(T, a, (unsigned)(g1 + g2), s)
+                                    : launch_pack_f32(T, a, (unsigned)(g1 + g2), s));
 }
 
 int eqlinear_fwd(const void* x, const void* w_packed, void* y, int64_t N, int64_t Cp, int64_t Dp,

@@ -8,7 +8,7 @@
 // transforms them in fp32 (p4: butterflies only), divides each plane by its share
 // of the inverse transform's scale and rounds it once to the element type.  In the input-gradient mode the weight is the transposed,
 // group-reversed w~[c][d][t] = w[d][c][(-t) mod T]; its spectrum is the conjugate,
-// so the Im planes change sign.
+// so the Im planes change sign.  One launch may write both packings (PackArgs::wp2).
 #pragma once
 
 #include "eql_device.h"
@@ -20,6 +20,10 @@ struct PackArgs {
   void* wp;         // packed: packed_unit(o, i / G, p) * G + i % G
   int Dp, Cp, outCh, inCh, Jin, transposed;
   Twiddles tw;
+  // Both packings in one launch: workgroups from blocks1 on write the input-gradient
+  // packing (transposed) into wp2, whose input axis has Jin2 groups; 0 = one packing.
+  void* wp2;
+  int Jin2, blocks1;
 };
 
 // Output channels per block of the packed weight.
@@ -40,18 +44,22 @@ template <int T, typename Elt>
 __global__ void __launch_bounds__(256) eql_pack_kernel(const PackArgs a) {
   constexpr int G = EltT<Elt>::kPerUnit;
   constexpr int NR = n_real_planes(T);
-  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-  const size_t row = (size_t)a.Jin * G;
-  const int outPad = (a.outCh + kPackBlock - 1) / kPackBlock * kPackBlock;
+  const bool second = a.blocks1 > 0 && (int)blockIdx.x >= a.blocks1;
+  const int transposed = second ? 1 : a.transposed;
+  const int outCh = second ? a.inCh : a.outCh, inCh = second ? a.outCh : a.inCh;
+  const int Jin = second ? a.Jin2 : a.Jin;
+  const size_t idx = (size_t)((int)blockIdx.x - (second ? a.blocks1 : 0)) * 256 + threadIdx.x;
+  const size_t row = (size_t)Jin * G;
+  const int outPad = (outCh + kPackBlock - 1) / kPackBlock * kPackBlock;
   if (idx >= (size_t)outPad * row) return;
   const int o = (int)(idx / row);
   const int i = (int)(idx - (size_t)o * row);
   float pl[T];
 #pragma unroll
   for (int p = 0; p < T; ++p) pl[p] = 0.0f;
-  if (i < a.inCh && o < a.outCh) {
-    const int d = a.transposed ? i : o;
-    const int c = a.transposed ? o : i;
+  if (i < inCh && o < outCh) {
+    const int d = transposed ? i : o;
+    const int c = transposed ? o : i;
     float v[T];
     load_group<T, Elt>(static_cast<const Elt*>(a.w) + ((size_t)d * a.Cp + c) * T, v);
     Dft<T>::run(v, pl, a.tw);
@@ -60,14 +68,14 @@ __global__ void __launch_bounds__(256) eql_pack_kernel(const PackArgs a) {
     // power-of-two T), so the kernels that consume the packing multiply by nothing.
 #pragma unroll
     for (int p = 0; p < T; ++p) pl[p] = (p < NR ? pl[p] : 2.0f * pl[p]) / (float)T;
-    if (a.transposed) {
+    if (transposed) {
 #pragma unroll
       for (int p = NR + 1; p < T; p += 2) pl[p] = -pl[p];
     }
   }
-  Elt* out = static_cast<Elt*>(a.wp);
+  Elt* out = static_cast<Elt*>(second ? a.wp2 : a.wp);
 #pragma unroll
-  for (int p = 0; p < T; ++p) out[packed_unit(o, i / G, p, T, a.Jin / 2) * G + (i % G)] = (Elt)pl[p];
+  for (int p = 0; p < T; ++p) out[packed_unit(o, i / G, p, T, Jin / 2) * G + (i % G)] = (Elt)pl[p];
 }
 
 }  // namespace eql

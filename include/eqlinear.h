@@ -119,6 +119,15 @@ int eqlinear_pack_weight(const void* w, void* w_packed, int64_t Dp, int64_t Cp, 
                          int dtype, int mode, void* stream);
 
 /*
+ * Both packings of w in one launch: w_packed receives the EQL_PACK_FWD packing and
+ * w_packed_bwdx the EQL_PACK_BWDX one, bit-identical to two eqlinear_pack_weight calls
+ * (sizes as there; all three pointers device memory, 16-byte aligned, no overlap).  For a
+ * training step, which needs both.
+ */
+int eqlinear_pack_weight_both(const void* w, void* w_packed, void* w_packed_bwdx, int64_t Dp, int64_t Cp, int T,
+                              int dtype, void* stream);
+
+/*
  * Forward: y = x W^T ("Insight Central").  x: [N][Cp*T] read; w_packed: the
  * EQL_PACK_FWD packing of w[Dp][Cp][T]; y: [N][Dp*T] overwritten.
  * One fused kernel: group DFT of x in the GEMM prologue, per-frequency MFMA
@@ -348,7 +357,7 @@ const char* eqlinear_status_string(int status);
  * layout above (1.xx stored ((o * Jin + i / G) * T + p) * G + i % G).  2.01:
  * eqlinear_fused_epilogue_bwd_noalloc and EQL_ESCRATCH.  2.02: the p4m entry points.
  * 2.03: the training-step entry points (eqlinear_fwd_train, eqlinear_bwd_x_train,
- * eqlinear_bwd_w_train).  2.04: eqlinear_fwd_fused_train. */
+ * eqlinear_bwd_w_train).  2.04: eqlinear_fwd_fused_train.  2.05: eqlinear_pack_weight_both. */
 int eqlinear_abi_version(void);
 
 #ifdef __cplusplus

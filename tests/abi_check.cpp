@@ -35,7 +35,7 @@ void* const MIS2 = reinterpret_cast<void*>(uintptr_t{0x10002});
 constexpr int F16 = EQL_F16, F32 = EQL_F32;
 
 void sizes() {
-  CHECK(eqlinear_abi_version() == 204);
+  CHECK(eqlinear_abi_version() == 205);
   for (int s = -3; s < 12; ++s) CHECK(eqlinear_status_string(s) != nullptr && std::strlen(eqlinear_status_string(s)) > 0);
   // Packed weight: out channels padded to 32, input 16-byte groups padded per stage.
   CHECK(eqlinear_packed_weight_bytes(3, 5, 4, F16) == 32u * 4 * 16 * 4);
@@ -104,6 +104,12 @@ void validation() {
   CHECK(eqlinear_pack_weight(A, B, 4, 4, 20, F16, 0, nullptr) == EQL_EUNSUPPORTED);
   CHECK(eqlinear_pack_weight(A, B, 0, 4, 4, F16, 0, nullptr) == EQL_EINVAL);
   CHECK(eqlinear_pack_weight(A, B, INT64_MAX, INT64_MAX, 4, F16, 0, nullptr) == EQL_EINVAL);
+  CHECK(eqlinear_pack_weight_both(A, B, nullptr, 4, 4, 4, F16, nullptr) == EQL_EINVAL);
+  CHECK(eqlinear_pack_weight_both(nullptr, B, C, 4, 4, 4, F16, nullptr) == EQL_EINVAL);
+  CHECK(eqlinear_pack_weight_both(A, B, MIS, 4, 4, 4, F16, nullptr) == EQL_EALIGN);
+  CHECK(eqlinear_pack_weight_both(A, B, C, 4, 4, 20, F16, nullptr) == EQL_EUNSUPPORTED);
+  CHECK(eqlinear_pack_weight_both(A, B, C, 0, 4, 4, F16, nullptr) == EQL_EINVAL);
+  CHECK(eqlinear_pack_weight_both(A, B, C, INT64_MAX, INT64_MAX, 4, F16, nullptr) == EQL_EINVAL);
   // Weight gradient.
   const size_t ws = eqlinear_bwd_w_workspace_bytes(300, 5, 7, 4, F16);
   CHECK(ws > 0);

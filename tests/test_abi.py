@@ -26,14 +26,14 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_function():
     L = eql.lib()
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     for n in names:
         assert hasattr(L, n), "missing export %s" % n
         assert hasattr(eql, n), "binding lacks %s" % n
 
 
 def test_version_and_status_strings():
-    assert eql.eqlinear_abi_version() == 204
+    assert eql.eqlinear_abi_version() == 205
     for s in range(5):
         assert eql.eqlinear_status_string(s)
     assert eql.eqlinear_status_string(99) == "unknown status"

@@ -288,3 +288,23 @@ def test_fused_train_step(case):
     dpre_h = dpre.cpu().numpy()
     assert rel_err(dx.cpu().numpy(), oracle.bwd_x(dpre_h, w)) <= TOL[dtype]
     assert rel_err(dw.cpu().numpy(), oracle.bwd_w(x, dpre_h, T)) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+@pytest.mark.parametrize("T", [1, 3, 4, 8])
+@pytest.mark.parametrize("shape", [(5, 3), (96, 384), (600, 520), (1024, 1024)], ids=lambda s: "D%d_C%d" % s)
+def test_pack_weight_both_matches_two_packs(T, dtype, shape):
+    """eqlinear_pack_weight_both: both packings bit-identical to two eqlinear_pack_weight calls."""
+    Dp, Cp = shape
+    code = DT[dtype]
+    wl = W.Workload("t", "test", T, 1, Cp, Dp, dtype, ("fwd",), seed=5)
+    wd = torch.from_numpy(W.make_w(wl)).to(DEV)
+    nf = eql.eqlinear_packed_weight_bytes(Dp, Cp, T, code)
+    nb = eql.eqlinear_packed_weight_bytes(Cp, Dp, T, code)
+    a, b = torch.full((nf,), 0xAB, dtype=torch.uint8, device=DEV), torch.full((nb,), 0xAB, dtype=torch.uint8, device=DEV)
+    a0, b0 = torch.empty_like(a), torch.empty_like(b)
+    eql.eqlinear_pack_weight_both(wd, a, b, Dp, Cp, T, code)
+    eql.eqlinear_pack_weight(wd, a0, Dp, Cp, T, code, eql.EQL_PACK_FWD)
+    eql.eqlinear_pack_weight(wd, b0, Dp, Cp, T, code, eql.EQL_PACK_BWDX)
+    torch.cuda.synchronize()
+    assert torch.equal(a, a0) and torch.equal(b, b0)
