@@ -361,7 +361,8 @@ def main():
         b = torch.from_numpy(W.make_bias(wl)).to(dev)
         fused = fused_epilogue(torch, eql, x, wp, b, dy, y, N, Cp, Dp, T, code, sptr,
                                reps=max(5, min(args.steps, 20)))
-        fused["plain_fwd_ms"] = round(per["fwd"], 4)
+        # The plain forward (eqlinear_fwd) the fused epilogue is compared with.
+        fused["plain_fwd_ms"] = round(plain_step["passes_ms"]["fwd"] if plain_step is not None else per["fwd"], 4)
         fused["mlp_train_step"] = mlp_train_step(torch, eql, x, w, wp, wpb, b, dy, y, dx, dw, ws, ws_bytes,
                                                  N, Cp, Dp, T, code, sptr, reps=max(5, min(args.steps, 20)),
                                                  train=args.step == "train")
