@@ -40,7 +40,7 @@ class EQLinearFunction(torch.autograd.Function):
     """y[..., D'*T] = x[..., C'*T] W^T with W[d*T+g, c*T+h] = w[d, c, (g-h) mod T]."""
 
     @staticmethod
-    def forward(ctx, x: torch.Tensor, w: torch.Tensor):
+    def forward(ctx, x: torch.Tensor, w: torch.Tensor, keep_spectra: bool = True):
         Dp, Cp, T = w.shape
         if x.shape[-1] != Cp * T:
             raise ValueError("x has %d features, the weight expects C'*T = %d" % (x.shape[-1], Cp * T))
@@ -51,7 +51,7 @@ class EQLinearFunction(torch.autograd.Function):
         N = x2.shape[0]
         y = torch.empty((N, Dp * T), dtype=x.dtype, device=x.device)
         ws_bytes = eqlinear_bwd_w_workspace_bytes(N, Cp, Dp, T, x.dtype)
-        if ctx.needs_input_grad[1]:
+        if keep_spectra and ctx.needs_input_grad[1]:
             # The weight gradient will follow: keep x's spectrum in its workspace.
             ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=x.device)
             eqlinear_fwd_train(x2, _packed(w, EQL_PACK_FWD), y, ws, ws_bytes, N, Cp, Dp, T, x.dtype)
@@ -71,24 +71,30 @@ class EQLinearFunction(torch.autograd.Function):
         dy2 = dy.reshape(-1, Dp * T).to(x2.dtype).contiguous()
         dx = dw = None
         need_dx, need_dw = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        train = ws is not None
         if need_dx:
             dx = torch.empty((N, Cp * T), dtype=x2.dtype, device=x2.device)
-            if need_dw:  # also leaves dy's spectrum where the weight gradient reads it
+            if train and need_dw:  # also leaves dy's spectrum where the weight gradient reads it
                 eqlinear_bwd_x_train(dy2, _packed(w, EQL_PACK_BWDX), dx, ws, ctx.ws_bytes, N, Cp, Dp, T, x2.dtype)
             else:
                 eqlinear_bwd_x(dy2, _packed(w, EQL_PACK_BWDX), dx, N, Cp, Dp, T, x2.dtype)
             dx = dx.reshape(*ctx.lead_shape, Cp * T)
         if need_dw:
             dw = torch.empty_like(w)
-            if need_dx:
+            if train and need_dx:
                 eqlinear_bwd_w_train(dy2, dw, ws, ctx.ws_bytes, N, Cp, Dp, T, x2.dtype)
             else:
+                if ws is None:
+                    ws = torch.empty(max(ctx.ws_bytes, 16), dtype=torch.uint8, device=x2.device)
                 eqlinear_bwd_w(x2, dy2, dw, ws, ctx.ws_bytes, N, Cp, Dp, T, x2.dtype)
-        return dx, dw
+        return dx, dw, None
 
 
-def eqlinear(x: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
-    return EQLinearFunction.apply(x, w)
+def eqlinear(x: torch.Tensor, w: torch.Tensor, keep_spectra: bool = True) -> torch.Tensor:
+    """keep_spectra: with a weight gradient, run the training entry points (the forward keeps
+    the weight-gradient workspace, about the size of x and dy plus fp32 partials, until the
+    backward); False runs the plain passes and keeps only x."""
+    return EQLinearFunction.apply(x, w, keep_spectra)
 
 
 def _act_code(act):
@@ -109,7 +115,7 @@ class EQLinearFusedFunction(torch.autograd.Function):
     and eqlinear_bwd_w on dpre; the residual's gradient is dy."""
 
     @staticmethod
-    def forward(ctx, x: torch.Tensor, w: torch.Tensor, b, r, act, grad_mode: bool):
+    def forward(ctx, x: torch.Tensor, w: torch.Tensor, b, r, act, grad_mode: bool, keep_spectra: bool = True):
         Dp, Cp, T = w.shape
         if x.shape[-1] != Cp * T:
             raise ValueError("x has %d features, the weight expects C'*T = %d" % (x.shape[-1], Cp * T))
@@ -138,7 +144,7 @@ class EQLinearFusedFunction(torch.autograd.Function):
         pre = torch.empty_like(y) if keep else None
         bc = b.contiguous() if b is not None else None
         ws_bytes = eqlinear_bwd_w_workspace_bytes(N, Cp, Dp, T, x.dtype)
-        if grad_mode and ctx.needs_input_grad[1]:
+        if keep_spectra and grad_mode and ctx.needs_input_grad[1]:
             # The weight gradient will follow: keep x's spectrum in its workspace.
             wsw = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=x.device)
             eqlinear_fwd_fused_train(x2, _packed(w, EQL_PACK_FWD), bc, r2, y, pre, wsw, ws_bytes, N, Cp, Dp, T,
@@ -161,7 +167,7 @@ class EQLinearFusedFunction(torch.autograd.Function):
         dr = dy2.reshape(ctx.res_shape) if ctx.res_shape is not None and ctx.needs_input_grad[3] else None
         dx = dw = db = None
         if not any(ctx.needs_input_grad[:3]):
-            return dx, dw, db, dr, None, None
+            return dx, dw, db, dr, None, None, None
         # Without an activation dpre = dy: the call then only sums the bias gradient.
         dpre = torch.empty_like(dy2) if ctx.code == EQL_ACT_GELU else dy2
         if ctx.has_bias and ctx.needs_input_grad[2]:
@@ -188,26 +194,30 @@ class EQLinearFusedFunction(torch.autograd.Function):
                 wsb = wsw if wsw is not None else torch.empty(max(ctx.ws_bytes, 16), dtype=torch.uint8,
                                                               device=x2.device)
                 eqlinear_bwd_w(x2, dpre, dw, wsb, ctx.ws_bytes, N, Cp, Dp, T, x2.dtype)
-        return dx, dw, db, dr, None, None
+        return dx, dw, db, dr, None, None, None
 
 
 def eqlinear_fused(x: torch.Tensor, w: torch.Tensor, bias: torch.Tensor | None = None,
-                   residual: torch.Tensor | None = None, act: str = "none") -> torch.Tensor:
+                   residual: torch.Tensor | None = None, act: str = "none", keep_spectra: bool = True) -> torch.Tensor:
     """act(x W^T + bias) + residual with the epilogue fused into the forward kernel
     (eqlinear_fwd_fused), the MLP-block epilogue of the networks the layer is built into
     ("Nivel de Rede").  bias has one value per output channel (shared by its T group
     elements); act is "none" or "gelu"; residual has the output's shape.  Differentiable
-    in x, w, bias and residual."""
-    return EQLinearFusedFunction.apply(x, w, bias, residual, act, torch.is_grad_enabled())
+    in x, w, bias and residual.  keep_spectra as for eqlinear."""
+    return EQLinearFusedFunction.apply(x, w, bias, residual, act, torch.is_grad_enabled(), keep_spectra)
 
 
 class EQLinear(torch.nn.Module):
     """Equivariant linear layer over C_T: in_channels*T -> out_channels*T features."""
 
     def __init__(self, in_channels: int, out_channels: int, group_order: int = 4, bias: bool = False,
-                 activation: str | None = None, device=None, dtype=None):
+                 activation: str | None = None, device=None, dtype=None, keep_spectra: bool = True):
         super().__init__()
         self.in_channels, self.out_channels, self.group_order = in_channels, out_channels, group_order
+        # Training through the training entry points holds the weight-gradient workspace
+        # from the forward to the backward (see eqlinear); False trades that memory for the
+        # weight gradient's own transforms.
+        self.keep_spectra = keep_spectra
         _act_code(activation)
         self.activation = activation
         self.weight = torch.nn.Parameter(torch.empty(out_channels, in_channels, group_order, device=device,
@@ -220,9 +230,9 @@ class EQLinear(torch.nn.Module):
     def forward(self, x: torch.Tensor, residual: torch.Tensor | None = None) -> torch.Tensor:
         """y = act(x W^T + bias) + residual (the parts not configured are skipped)."""
         if self.bias is None and self.activation in (None, "none") and residual is None:
-            return EQLinearFunction.apply(x, self.weight)
+            return EQLinearFunction.apply(x, self.weight, self.keep_spectra)
         return EQLinearFusedFunction.apply(x, self.weight, self.bias, residual, self.activation,
-                                           torch.is_grad_enabled())
+                                           torch.is_grad_enabled(), self.keep_spectra)
 
     def extra_repr(self) -> str:
         return "in_channels=%d, out_channels=%d, group_order=%d, bias=%s, activation=%s" % (
@@ -236,7 +246,7 @@ class EQLinearP4MFunction(torch.autograd.Function):
     the weight gradient is the C_4 one folded back onto the shared parameters."""
 
     @staticmethod
-    def forward(ctx, x: torch.Tensor, w: torch.Tensor):
+    def forward(ctx, x: torch.Tensor, w: torch.Tensor, keep_spectra: bool = True):
         Dp, Cp, G = w.shape
         if G != 8:
             raise ValueError("a p4m weight has 8 group elements per (out, in) pair, got %d" % G)
@@ -250,7 +260,7 @@ class EQLinearP4MFunction(torch.autograd.Function):
         N = x2.shape[0]
         y = torch.empty((N, Dp * 8), dtype=x.dtype, device=x.device)
         ws_bytes = eqlinear_bwd_w_workspace_bytes(N, 2 * Cp, 2 * Dp, 4, x.dtype)
-        if ctx.needs_input_grad[1]:
+        if keep_spectra and ctx.needs_input_grad[1]:
             # As EQLinearFunction: keep x's spectrum for the weight gradient.
             ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=x.device)
             eqlinear_fwd_train(x2, _packed(w4, EQL_PACK_FWD), y, ws, ws_bytes, N, 2 * Cp, 2 * Dp, 4, x.dtype)
@@ -271,9 +281,10 @@ class EQLinearP4MFunction(torch.autograd.Function):
         dy2 = dy.reshape(-1, Dp * 8).to(x2.dtype).contiguous()
         dx = dw = None
         need_dx, need_dw = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        train = ws is not None
         if need_dx:
             dx = torch.empty((N, Cp * 8), dtype=x2.dtype, device=x2.device)
-            if need_dw:
+            if train and need_dw:
                 eqlinear_bwd_x_train(dy2, _packed(w4, EQL_PACK_BWDX), dx, ws, ctx.ws_bytes, N, 2 * Cp, 2 * Dp, 4,
                                      x2.dtype)
             else:
@@ -281,31 +292,35 @@ class EQLinearP4MFunction(torch.autograd.Function):
             dx = dx.reshape(*ctx.lead_shape, Cp * 8)
         if need_dw:
             dw4 = torch.empty_like(w4)
-            if need_dx:
+            if train and need_dx:
                 eqlinear_bwd_w_train(dy2, dw4, ws, ctx.ws_bytes, N, 2 * Cp, 2 * Dp, 4, x2.dtype)
             else:
+                if ws is None:
+                    ws = torch.empty(max(ctx.ws_bytes, 16), dtype=torch.uint8, device=x2.device)
                 eqlinear_bwd_w(x2, dy2, dw4, ws, ctx.ws_bytes, N, 2 * Cp, 2 * Dp, 4, x2.dtype)
             dw = torch.empty((Dp, Cp, 8), dtype=x2.dtype, device=x2.device)
             eqlinear_p4m_fold_weight_grad(dw4, dw, Dp, Cp, x2.dtype)
-        return dx, dw
+        return dx, dw, None
 
 
-def eqlinear_p4m(x: torch.Tensor, w: torch.Tensor) -> torch.Tensor:
-    return EQLinearP4MFunction.apply(x, w)
+def eqlinear_p4m(x: torch.Tensor, w: torch.Tensor, keep_spectra: bool = True) -> torch.Tensor:
+    """keep_spectra as for eqlinear."""
+    return EQLinearP4MFunction.apply(x, w, keep_spectra)
 
 
 class EQLinearP4M(torch.nn.Module):
     """Equivariant linear layer over p4m's point group: in_channels*8 -> out_channels*8."""
 
-    def __init__(self, in_channels: int, out_channels: int, device=None, dtype=None):
+    def __init__(self, in_channels: int, out_channels: int, device=None, dtype=None, keep_spectra: bool = True):
         super().__init__()
         self.in_channels, self.out_channels = in_channels, out_channels
+        self.keep_spectra = keep_spectra
         self.weight = torch.nn.Parameter(torch.empty(out_channels, in_channels, 8, device=device, dtype=dtype))
         with torch.no_grad():
             self.weight.normal_(0.0, 1.0 / math.sqrt(in_channels * 8))
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
-        return EQLinearP4MFunction.apply(x, self.weight)
+        return EQLinearP4MFunction.apply(x, self.weight, self.keep_spectra)
 
     def extra_repr(self) -> str:
         return "in_channels=%d, out_channels=%d, group=p4m" % (self.in_channels, self.out_channels)

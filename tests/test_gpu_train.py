@@ -218,10 +218,11 @@ def test_train_full_size(key):
     cmp.check()
 
 
-@pytest.mark.parametrize("grads", ["both", "w_only", "x_only"])
+@pytest.mark.parametrize("grads", ["both", "w_only", "x_only", "both_plain"])
 def test_layer_autograd_through_training_entry_points(grads):
     """EQLinearFunction: with a weight gradient the forward keeps the workspace and the
-    backward runs the training entry points (with only one gradient, the plain ones)."""
+    backward runs the training entry points (with only one gradient, or keep_spectra=False,
+    the plain ones)."""
     from group_circulant_linear_p4_amd.layer import eqlinear
     T, N, Cp, Dp = 4, 333, 256, 520
     wl = W.Workload("t", "test", T, N, Cp, Dp, "f16", ("fwd", "bwd_x", "bwd_w"), seed=91)
@@ -229,7 +230,7 @@ def test_layer_autograd_through_training_entry_points(grads):
     x = torch.from_numpy(x_h).to(DEV).reshape(3, 111, Cp * T).requires_grad_(grads != "w_only")
     w = torch.from_numpy(w_h).to(DEV).requires_grad_(grads != "x_only")
     print("case layer %s" % grads, flush=True)
-    y = eqlinear(x, w)
+    y = eqlinear(x, w, keep_spectra=grads != "both_plain")
     y.backward(torch.from_numpy(dy_h).to(DEV).reshape(3, 111, Dp * T))
     torch.cuda.synchronize()
     assert rel_err(y.detach().cpu().numpy().reshape(N, -1), oracle.fwd(x_h, w_h)) <= TOL["f16"]
