@@ -294,8 +294,8 @@ int eqlinear_bwd_w(const void* x, const void* dy, void* dw, void* workspace, siz
  * Contract: eqlinear_bwd_w_train's workspace must hold what eqlinear_fwd_train (for
  * this x) and eqlinear_bwd_x_train (for this dy) wrote there, for the same N, Cp, Dp,
  * T and dtype, ordered before it on the stream, with nothing else writing that memory
- * in between; the library cannot check this.  Each call's own result is complete when
- * it returns (y, dx) or completes on the stream (dw).  The spectra cover every row and
+ * in between; the library cannot check this.  Like every entry point these only enqueue
+ * work on the stream: outputs are complete when that work is.  The spectra cover every row and
  * every channel of the layer; padding units past the channel count may hold stale
  * values and only reach gradient entries that are discarded.
  */
