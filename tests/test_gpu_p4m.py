@@ -4,8 +4,8 @@ The library runs p4m as the C_4 layer on 2C' x 2D' channels with a tied weight (
 include/eqlinear.h). Checked here through the C ABI and the torch layer:
 - the tied weight, bit for bit, against the oracle's group law;
 - y, dx and dw of EQLinearP4MFunction against oracle.p4m_oracle (relative Frobenius error
-  <= 1e-5 for fp32, <= 3e-3 for fp16), on shapes whose C_4 view spans several tiles with
-  ragged tails;
+  <= 1e-5 for fp32, <= 3e-3 for fp16), through the training entry points and through the
+  plain passes, on shapes whose C_4 view spans several tiles with ragged tails;
 - equivariance of the GPU outputs under right translation by r and by s.
 """
 import numpy as np
@@ -58,15 +58,18 @@ def test_p4m_expanded_weight_follows_the_group_law(dtype):
 CASES = [(300, 5, 7), (1000, 48, 40), (2049, 17, 130), (4100, 96, 64)]
 
 
+@pytest.mark.parametrize("keep", [True, False], ids=["train", "plain"])
 @pytest.mark.parametrize("dtype", ["f16", "f32"])
 @pytest.mark.parametrize("shape", CASES, ids=lambda s: "N%d_C%d_D%d" % s)
-def test_p4m_layer_matches_oracle(dtype, shape):
+def test_p4m_layer_matches_oracle(dtype, shape, keep):
+    """keep: the training entry points (the weight gradient reads the spectra the forward
+    and the input gradient left in the workspace); otherwise the plain passes."""
     N, Cp, Dp = shape
-    print("case p4m layer %s N=%d C'=%d D'=%d" % (dtype, N, Cp, Dp), flush=True)
+    print("case p4m layer %s N=%d C'=%d D'=%d keep_spectra=%s" % (dtype, N, Cp, Dp, keep), flush=True)
     x, w, dy = inputs(N, Cp, Dp, dtype, 10 + N)
     xt = torch.from_numpy(x).to(DEV).requires_grad_(True)
     wt = torch.from_numpy(w).to(DEV).requires_grad_(True)
-    y = EQLinearP4MFunction.apply(xt, wt)
+    y = EQLinearP4MFunction.apply(xt, wt, keep)
     y.backward(torch.from_numpy(dy).to(DEV))
     torch.cuda.synchronize()
     tol = TOL[dtype]
