@@ -76,9 +76,12 @@ def parse():
 
 def bwdw_fused_path(N, Cp, Dp, T, elt) -> bool:
     """Whether the library's weight gradient takes its fused path for this shape (the
-    rule include/eqlinear.h documents for eqlinear_bwd_w)."""
+    rule include/eqlinear.h documents for eqlinear_bwd_w, with its EQL_BWDW_PATH override)."""
     if N == 0 or T not in (1, 2, 4) or (Dp * T * elt) % 16 or N * Dp * T * elt >= 2**32:
         return False
+    forced = os.environ.get("EQL_BWDW_PATH")
+    if forced in ("fused", "separate"):
+        return forced == "fused"
     planes = {1: 1, 2: 2, 4: 6}[T]
     return 2.0 * planes * N * Dp * Cp / (elt * T * N * (Cp + Dp)) < 400.0
 
